@@ -1,0 +1,160 @@
+/*
+ * ls_replay.h -- C ABI of liblsreplay: branch-replay attention and the clipped-GRPO
+ * token objective for long-context GRPO, on AMD Instinct MI355X (gfx950).
+ *
+ * Method: LongStraw branch replay, as summarised in the LongStraw study notes
+ * (dimensionstp.github.io, "LongStraw" summary). A long prompt's per-layer state
+ * (here: one attention layer's K/V) is captured once and kept resident (§2-1 step 1,
+ * §3-2 (1)-(2)); the G responses of a group are then replayed one at a time against it,
+ * each response's backward adding its prompt-side gradient into resident accumulators
+ * (§2-1 step 4, §3-2 (4)), with a single finalisation after the last response (§2-1
+ * step 5, §3-2 (7)). The per-token objective is the clipped GRPO policy loss (§1-1,
+ * L_policy equation).
+ *
+ * Conventions for every entry point:
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call only
+ *    enqueues work on that stream and returns; it never synchronises.
+ *  - Pointers marked "device" are caller-owned device allocations; pointers marked "host"
+ *    are read during the call only. The library allocates nothing and keeps no state.
+ *  - bf16 is IEEE bfloat16 stored as 16-bit words; fp32 is IEEE binary32.
+ *  - All argument checks run on the host before any HIP call; a failed check returns an
+ *    error code and touches no memory. A HIP launch/runtime error returns LS_ERR_HIP.
+ *    Nothing throws or aborts across the ABI. NaN/Inf in data propagate and are not checked.
+ *  - Results are bitwise reproducible run to run for the same inputs and arguments:
+ *    no floating-point atomics are used on any output.
+ */
+#ifndef LS_REPLAY_H
+#define LS_REPLAY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LS_OK = 0,
+  LS_ERR_INVALID_ARG = -1, /* a pointer, size, stride or value is invalid                 */
+  LS_ERR_UNSUPPORTED = -2, /* valid, but this build has no kernel for it (e.g. head dim)  */
+  LS_ERR_WORKSPACE = -3,   /* workspace missing or smaller than ls_*_workspace_bytes      */
+  LS_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed                   */
+} ls_status;
+
+/* Shape of one attention layer in replay.
+ *  P        prompt length (>= 0; 0 gives plain causal attention over the response).
+ *  Hq, Hkv  query / key-value heads, Hq % Hkv == 0; query head h reads kv head h / (Hq/Hkv).
+ *  Dqk, Dv  head dims; supported pairs: (64,64), (128,128). Other pairs: LS_ERR_UNSUPPORTED.
+ *  ldk, ldv elements between consecutive tokens of K and of V, for prompt and suffix alike;
+ *           element (token j, kv head k, dim d) sits at K[j*ldk + k*Dqk + d] and
+ *           V[j*ldv + k*Dv + d]. ldk >= Hkv*Dqk, ldv >= Hkv*Dv, both multiples of 8.
+ *           Latent KV (Hkv == 1, V = first Dv dims of K) passes V = K and ldv = ldk.
+ *  softmax_scale  finite and > 0 (the usual choice is 1/sqrt(Dqk)).
+ */
+typedef struct ls_attn_desc {
+  int32_t P;
+  int32_t Hq, Hkv;
+  int32_t Dqk, Dv;
+  int64_t ldk, ldv;
+  float softmax_scale;
+} ls_attn_desc;
+
+#define LS_MAX_RESPONSES_PER_CALL 64
+
+/* Workspace size in bytes for ls_replay_attn_fwd (which = 0) or ls_replay_attn_bwd
+ * (which = 1, exact prompt-gradient mode; which = 2, response-only mode) with these
+ * arguments. cu_seqlens: host, n_resp + 1 packed-row offsets (see ls_replay_attn_fwd).
+ * Writes the size to *bytes. Errors: LS_ERR_INVALID_ARG / LS_ERR_UNSUPPORTED as the
+ * matching call would return. */
+int ls_replay_attn_workspace_bytes(const ls_attn_desc* desc, int32_t n_resp, const int32_t* cu_seqlens,
+                                   int32_t which, size_t* bytes);
+
+/* Replay attention forward (LongStraw study notes §2-1 step 4, §3-2 (2) and (4)).
+ * n_resp (1..LS_MAX_RESPONSES_PER_CALL) responses are packed along the token axis:
+ * response i owns rows cu_seqlens[i] .. cu_seqlens[i+1]-1 (host array, cu_seqlens[0] = 0,
+ * non-decreasing; empty responses are allowed). T = cu_seqlens[n_resp].
+ * For response i, row t (0-based within the response) and query head h, with k = h/(Hq/Hkv):
+ * the query attends to all P prompt keys Kp[:,k] and to the response's own keys Ks[s,k]
+ * for s <= t, with softmax over scores softmax_scale * <q, key>.
+ *  Kp, Vp  device bf16 [P, Hkv, *] with strides ldk/ldv; READ ONLY (the library never writes
+ *          prompt state, so it can be reused for every response of the group, §3-2 (3)).
+ *          May be NULL when P == 0.
+ *  Q       device bf16 [T, Hq, Dqk] contiguous.
+ *  Ks, Vs  device bf16 [T, Hkv, *] with strides ldk/ldv (latent KV: Vs = Ks).
+ *  O       device bf16 [T, Hq, Dv] contiguous, overwritten.
+ *  lse     device fp32 [Hq, T], overwritten: natural-log sum of exp of the visible scores.
+ *  workspace  device, >= ls_replay_attn_workspace_bytes(which = 0), 256-byte aligned; may be
+ *          NULL when that size is 0.
+ * All device pointers 16-byte aligned. T == 0 returns LS_OK and launches nothing. */
+int ls_replay_attn_fwd(void* stream, const ls_attn_desc* desc,
+                       const void* Kp, const void* Vp,
+                       int32_t n_resp, const int32_t* cu_seqlens,
+                       const void* Q, const void* Ks, const void* Vs,
+                       void* O, float* lse,
+                       void* workspace, size_t workspace_bytes);
+
+/* Replay attention backward (same section; the prompt-side term is the dl/dz_P part of the
+ * gradient decomposition of §2-2). Arguments as in ls_replay_attn_fwd, plus:
+ *  O, lse  the forward's outputs for these inputs.
+ *  dO      device bf16 [T, Hq, Dv] contiguous.
+ *  dQ      device bf16 [T, Hq, Dqk] contiguous, overwritten.
+ *  dKs     device bf16 [T, Hkv, Dqk] contiguous, overwritten.
+ *  dVs     device bf16 [T, Hkv, Dv] contiguous, overwritten (latent KV: returned separately
+ *          from dKs; the latent gradient is dKs plus dVs padded to Dqk, formed by the caller).
+ *  dKp_accum, dVp_accum  device fp32 [P, Hkv, Dqk] / [P, Hkv, Dv] contiguous. Both non-NULL:
+ *          exact prompt-gradient mode, the prompt-side gradient of these responses is ADDED in
+ *          place (never zeroed by the library: the caller zeroes them at the start of a group
+ *          and reads them after the last response). Both NULL: response-only closure (stop-
+ *          gradient prompt boundary, §2-2), accumulators not touched. Exactly one NULL is
+ *          LS_ERR_INVALID_ARG. Two calls that add into the same accumulators must be ordered
+ *          (same stream or caller events).
+ *  workspace  >= ls_replay_attn_workspace_bytes(which = 1 exact, 2 response-only). */
+int ls_replay_attn_bwd(void* stream, const ls_attn_desc* desc,
+                       const void* Kp, const void* Vp,
+                       int32_t n_resp, const int32_t* cu_seqlens,
+                       const void* Q, const void* Ks, const void* Vs,
+                       const void* O, const float* lse, const void* dO,
+                       void* dQ, void* dKs, void* dVs,
+                       float* dKp_accum, float* dVp_accum,
+                       void* workspace, size_t workspace_bytes);
+
+/* Workspace bytes for ls_grpo_token_loss over T rows of vocabulary V (written to *bytes). */
+int ls_grpo_workspace_bytes(int64_t T, int32_t V, size_t* bytes);
+
+/* Clipped-GRPO token objective and its gradient (LongStraw study notes §1-1, L_policy):
+ *   L = -(1/G) sum_i (1/R_i) sum_t min(rho A_i, clip(rho, 1-eps, 1+eps) A_i),
+ *   rho = exp(logp - old_logp), logp = log_softmax(logits row)[target],
+ *   A_i = (r_i - mean(r)) / (std(r) + 1e-6)  (population std over the G rewards; the
+ *   pages say only that the advantage is built from the group rewards).
+ * This call handles responses first .. first+count-1, whose rows are packed in `logits`.
+ *  V         vocabulary size, 1..196608 (larger: LS_ERR_UNSUPPORTED).
+ *  G, R, rewards  group size and host arrays [G] of all response lengths (each >= 1) and
+ *            rewards (finite); A and 1/(G R_i) are formed on the host in float64.
+ *  eps       clip range, 0 < eps < 1.
+ *  logits    device bf16 [T, V], T = R[first] + ... + R[first+count-1].
+ *  targets   device int32 [T], sampled token ids. An id outside [0, V) is not read from
+ *            memory: that row's logp, loss term and dlogits become NaN.
+ *  old_logp  device fp32 [T].
+ *  dlogits   device bf16 [T, V], overwritten with dL/dlogits (may not alias logits).
+ *  loss_accum  device fp32 scalar; this call ADDS its share of L (ordered, deterministic).
+ *  logp_out  device fp32 [T] or NULL; clipped_out device uint8 [T] or NULL (1 where the
+ *            clipped branch is strictly smaller, so the token's gradient is zero).
+ *  workspace >= ls_grpo_workspace_bytes(T, V), 16-byte aligned.
+ * logits/dlogits rows are read/written with 16-byte accesses when V % 8 == 0 and both are
+ * 16-byte aligned, else element-wise. */
+int ls_grpo_token_loss(void* stream, int32_t V, int32_t G,
+                       const int32_t* R, const float* rewards,
+                       float eps, int32_t first, int32_t count,
+                       const void* logits, const int32_t* targets, const float* old_logp,
+                       void* dlogits, float* loss_accum,
+                       float* logp_out, uint8_t* clipped_out,
+                       void* workspace, size_t workspace_bytes);
+
+/* Static string naming a status code. */
+const char* ls_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LS_REPLAY_H */

@@ -1,0 +1,247 @@
+// Host side of liblsreplay: argument validation (pure C++, before any HIP call),
+// workspace sizing, advantage computation and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/ls_replay.h"
+#include "kernels.h"
+
+namespace {
+
+using lsr::kMaxResp;
+constexpr int32_t kMaxVocab = 196608;  // largest row the loss kernel holds in registers
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_desc(const ls_attn_desc* d) {
+  if (!d) return LS_ERR_INVALID_ARG;
+  if (d->P < 0 || d->Hq < 1 || d->Hkv < 1 || (d->Hq % d->Hkv) != 0) return LS_ERR_INVALID_ARG;
+  if (d->Dqk < 1 || d->Dv < 1 || d->Dv > d->Dqk) return LS_ERR_INVALID_ARG;
+  if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.0f)) return LS_ERR_INVALID_ARG;
+  if (d->ldk < (int64_t)d->Hkv * d->Dqk || d->ldv < (int64_t)d->Hkv * d->Dv) return LS_ERR_INVALID_ARG;
+  if ((d->ldk % 8) != 0 || (d->ldv % 8) != 0) return LS_ERR_INVALID_ARG;
+  const bool ok_shape = (d->Dqk == 64 && d->Dv == 64) || (d->Dqk == 128 && d->Dv == 128);
+  if (!ok_shape) return LS_ERR_UNSUPPORTED;
+  return LS_OK;
+}
+
+int check_cu(int32_t n_resp, const int32_t* cu) {
+  if (n_resp < 1 || !cu) return LS_ERR_INVALID_ARG;
+  if (n_resp > LS_MAX_RESPONSES_PER_CALL) return LS_ERR_UNSUPPORTED;
+  if (cu[0] != 0) return LS_ERR_INVALID_ARG;
+  for (int i = 0; i < n_resp; ++i)
+    if (cu[i + 1] < cu[i]) return LS_ERR_INVALID_ARG;
+  return LS_OK;
+}
+
+int plan_for(const ls_attn_desc* d, int32_t n_resp, const int32_t* cu, int which, lsr::AttnPlan* pl) {
+  int st = check_desc(d);
+  if (st != LS_OK) return st;
+  st = check_cu(n_resp, cu);
+  if (st != LS_OK) return st;
+  // sizes must fit the kernels' 32-bit row arithmetic
+  const int64_t T = cu[n_resp];
+  const int64_t g = d->Hq / d->Hkv;
+  if (T * d->Hq > INT32_MAX || T * g > INT32_MAX / 2 || (int64_t)d->P + T > INT32_MAX / 2) return LS_ERR_UNSUPPORTED;
+  if (!lsr::plan_attn(which, d->P, d->Hq, d->Hkv, d->Dqk, d->Dv, n_resp, cu, pl)) return LS_ERR_UNSUPPORTED;
+  return LS_OK;
+}
+
+void fill_geom(lsr::AttnGeom* g, const ls_attn_desc* d, const void* Kp, const void* Vp, int32_t n_resp,
+               const int32_t* cu, const void* Q, const void* Ks, const void* Vs) {
+  g->Kp = static_cast<const uint16_t*>(Kp);
+  g->Vp = static_cast<const uint16_t*>(Vp);
+  g->Q = static_cast<const uint16_t*>(Q);
+  g->Ks = static_cast<const uint16_t*>(Ks);
+  g->Vs = static_cast<const uint16_t*>(Vs);
+  g->ldk = d->ldk;
+  g->ldv = d->ldv;
+  g->P = d->P;
+  g->Hq = d->Hq;
+  g->Hkv = d->Hkv;
+  g->g = d->Hq / d->Hkv;
+  g->T = cu[n_resp];
+  g->scale = d->softmax_scale;
+  g->scale_log2 = d->softmax_scale * 1.4426950408889634f;
+  g->n_resp = n_resp;
+  for (int i = 0; i <= kMaxResp; ++i) g->tok0[i] = cu[i <= n_resp ? i : n_resp];
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ls_status_string(int status) {
+  switch (status) {
+    case LS_OK: return "LS_OK";
+    case LS_ERR_INVALID_ARG: return "LS_ERR_INVALID_ARG";
+    case LS_ERR_UNSUPPORTED: return "LS_ERR_UNSUPPORTED";
+    case LS_ERR_WORKSPACE: return "LS_ERR_WORKSPACE";
+    case LS_ERR_HIP: return "LS_ERR_HIP";
+    default: return "LS_UNKNOWN_STATUS";
+  }
+}
+
+int ls_replay_attn_workspace_bytes(const ls_attn_desc* desc, int32_t n_resp, const int32_t* cu_seqlens,
+                                   int32_t which, size_t* bytes) {
+  if (!bytes || which < 0 || which > 2) return LS_ERR_INVALID_ARG;
+  lsr::AttnPlan pl;
+  const int st = plan_for(desc, n_resp, cu_seqlens, which, &pl);
+  if (st != LS_OK) return st;
+  *bytes = pl.ws_bytes;
+  return LS_OK;
+}
+
+int ls_replay_attn_fwd(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
+                       const int32_t* cu_seqlens, const void* Q, const void* Ks, const void* Vs, void* O, float* lse,
+                       void* workspace, size_t workspace_bytes) {
+  lsr::AttnPlan pl;
+  int st = plan_for(desc, n_resp, cu_seqlens, 0, &pl);
+  if (st != LS_OK) return st;
+  const int64_t T = cu_seqlens[n_resp];
+  if (desc->P > 0 && (!Kp || !Vp || !aligned(Kp, 16) || !aligned(Vp, 16))) return LS_ERR_INVALID_ARG;
+  if (T == 0) return LS_OK;
+  const void* dev[] = {Q, Ks, Vs, O, lse};
+  for (const void* p : dev)
+    if (!p || !aligned(p, 16)) return LS_ERR_INVALID_ARG;
+  if (pl.ws_bytes > 0 && (!workspace || !aligned(workspace, 256))) return LS_ERR_WORKSPACE;
+  if (workspace_bytes < pl.ws_bytes) return LS_ERR_WORKSPACE;
+
+  lsr::FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  fill_geom(&a.geo, desc, Kp, Vp, n_resp, cu_seqlens, Q, Ks, Vs);
+  a.O = static_cast<uint16_t*>(O);
+  a.lse = lse;
+  char* ws = static_cast<char*>(workspace);
+  a.o_part = pl.splits > 1 ? reinterpret_cast<float*>(ws + pl.off_a) : nullptr;
+  a.lse_part = pl.splits > 1 ? reinterpret_cast<float*>(ws + pl.off_b) : nullptr;
+  a.splits = pl.splits;
+  a.ptiles = pl.ptiles;
+  a.ptiles_per_split = pl.ptiles_per_split;
+  a.qtiles = pl.qtiles;
+  for (int i = 0; i <= kMaxResp; ++i) a.tile0[i] = pl.tile0[i];
+  const hipError_t e = lsr::launch_attn_fwd(a, desc->Dqk, desc->Dv, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LS_OK : LS_ERR_HIP;
+}
+
+int ls_replay_attn_bwd(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
+                       const int32_t* cu_seqlens, const void* Q, const void* Ks, const void* Vs, const void* O,
+                       const float* lse, const void* dO, void* dQ, void* dKs, void* dVs, float* dKp_accum,
+                       float* dVp_accum, void* workspace, size_t workspace_bytes) {
+  if ((dKp_accum == nullptr) != (dVp_accum == nullptr)) return LS_ERR_INVALID_ARG;
+  const bool exact = dKp_accum != nullptr;
+  lsr::AttnPlan pl;
+  int st = plan_for(desc, n_resp, cu_seqlens, exact ? 1 : 2, &pl);
+  if (st != LS_OK) return st;
+  const int64_t T = cu_seqlens[n_resp];
+  if (desc->P > 0 && (!Kp || !Vp || !aligned(Kp, 16) || !aligned(Vp, 16))) return LS_ERR_INVALID_ARG;
+  if (exact && desc->P > 0 && (!aligned(dKp_accum, 16) || !aligned(dVp_accum, 16))) return LS_ERR_INVALID_ARG;
+  if (T == 0) return LS_OK;
+  const void* dev[] = {Q, Ks, Vs, O, lse, dO, dQ, dKs, dVs};
+  for (const void* p : dev)
+    if (!p || !aligned(p, 16)) return LS_ERR_INVALID_ARG;
+  if (pl.ws_bytes > 0 && (!workspace || !aligned(workspace, 256))) return LS_ERR_WORKSPACE;
+  if (workspace_bytes < pl.ws_bytes) return LS_ERR_WORKSPACE;
+
+  lsr::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  fill_geom(&a.geo, desc, Kp, Vp, n_resp, cu_seqlens, Q, Ks, Vs);
+  a.O = static_cast<const uint16_t*>(O);
+  a.lse = lse;
+  a.dO = static_cast<const uint16_t*>(dO);
+  a.dQ = static_cast<uint16_t*>(dQ);
+  a.dKs = static_cast<uint16_t*>(dKs);
+  a.dVs = static_cast<uint16_t*>(dVs);
+  a.dKp = exact && desc->P > 0 ? dKp_accum : nullptr;
+  a.dVp = exact && desc->P > 0 ? dVp_accum : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.delta = reinterpret_cast<float*>(ws + pl.off_a);
+  a.dq_part = pl.splits > 1 ? reinterpret_cast<float*>(ws + pl.off_b) : nullptr;
+  a.splits = pl.splits;
+  a.ptiles = pl.ptiles;
+  a.ptiles_per_split = pl.ptiles_per_split;
+  a.qtiles = pl.qtiles;
+  for (int i = 0; i <= kMaxResp; ++i) a.tile0[i] = pl.tile0[i];
+  a.ktiles_prompt = (a.dKp != nullptr) ? pl.ktiles_prompt : 0;
+  for (int i = 0; i <= kMaxResp; ++i) a.ktile0[i] = pl.ktile0[i];
+  const hipError_t e = lsr::launch_attn_bwd(a, desc->Dqk, desc->Dv, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LS_OK : LS_ERR_HIP;
+}
+
+int ls_grpo_workspace_bytes(int64_t T, int32_t V, size_t* bytes) {
+  if (!bytes || T < 0 || V < 1) return LS_ERR_INVALID_ARG;
+  *bytes = lsr::grpo_workspace_bytes(T);
+  return LS_OK;
+}
+
+int ls_grpo_token_loss(void* stream, int32_t V, int32_t G, const int32_t* R, const float* rewards, float eps,
+                       int32_t first, int32_t count, const void* logits, const int32_t* targets,
+                       const float* old_logp, void* dlogits, float* loss_accum, float* logp_out,
+                       uint8_t* clipped_out, void* workspace, size_t workspace_bytes) {
+  if (V < 1 || G < 1 || !R || !rewards) return LS_ERR_INVALID_ARG;
+  if (V > kMaxVocab) return LS_ERR_UNSUPPORTED;
+  if (!std::isfinite(eps) || !(eps > 0.0f) || !(eps < 1.0f)) return LS_ERR_INVALID_ARG;
+  if (first < 0 || count < 1 || (int64_t)first + count > G) return LS_ERR_INVALID_ARG;
+  for (int i = 0; i < G; ++i)
+    if (R[i] < 1 || !std::isfinite(rewards[i])) return LS_ERR_INVALID_ARG;
+  int64_t T = 0;
+  for (int i = first; i < first + count; ++i) T += R[i];
+  if (T > INT32_MAX) return LS_ERR_UNSUPPORTED;
+  if (!logits || !targets || !old_logp || !dlogits || !loss_accum) return LS_ERR_INVALID_ARG;
+  if (!aligned(logits, 2) || !aligned(dlogits, 2) || !aligned(targets, 4) || !aligned(old_logp, 4) ||
+      !aligned(loss_accum, 4) || (logp_out && !aligned(logp_out, 4)))
+    return LS_ERR_INVALID_ARG;
+  const char* lb = static_cast<const char*>(logits);
+  const char* db = static_cast<const char*>(dlogits);
+  const int64_t nbytes = T * (int64_t)V * 2;
+  if (lb < db + nbytes && db < lb + nbytes) return LS_ERR_INVALID_ARG;  // dlogits may not alias logits
+  const size_t need = lsr::grpo_workspace_bytes(T);
+  if (!workspace || !aligned(workspace, 16)) return LS_ERR_WORKSPACE;
+  if (workspace_bytes < need) return LS_ERR_WORKSPACE;
+
+  // group advantage in float64 on the host: A_i = (r_i - mean) / (std_pop + 1e-6)
+  double mean = 0.0;
+  for (int i = 0; i < G; ++i) mean += rewards[i];
+  mean /= G;
+  double var = 0.0;
+  for (int i = 0; i < G; ++i) var += (rewards[i] - mean) * (rewards[i] - mean);
+  const double sd = std::sqrt(var / G);
+
+  const bool vec = (V % 8) == 0 && aligned(logits, 16) && aligned(dlogits, 16);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // responses are launched in batches of at most kMaxResp
+  int64_t row0 = 0;
+  for (int b0 = first; b0 < first + count; b0 += kMaxResp) {
+    const int nb = (first + count - b0) < kMaxResp ? (first + count - b0) : kMaxResp;
+    lsr::GrpoArgs a;
+    std::memset(&a, 0, sizeof(a));
+    int64_t rows = 0;
+    for (int k = 0; k < nb; ++k) {
+      const int i = b0 + k;
+      rows += R[i];
+      a.row_end[k] = (int32_t)rows;
+      a.A[k] = (float)((rewards[i] - mean) / (sd + 1e-6));
+      a.w[k] = (float)(1.0 / ((double)G * (double)R[i]));
+    }
+    a.n = nb;
+    a.T = rows;
+    a.V = V;
+    a.eps = eps;
+    a.logits = static_cast<const uint16_t*>(logits) + row0 * V;
+    a.dlogits = static_cast<uint16_t*>(dlogits) + row0 * V;
+    a.targets = targets + row0;
+    a.old_logp = old_logp + row0;
+    a.row_loss = static_cast<float*>(workspace) + row0;
+    a.logp_out = logp_out ? logp_out + row0 : nullptr;
+    a.clipped_out = clipped_out ? clipped_out + row0 : nullptr;
+    a.loss_accum = loss_accum;
+    if (lsr::launch_grpo(a, vec, st) != hipSuccess) return LS_ERR_HIP;
+    row0 += rows;
+  }
+  return LS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Work decomposition of replay attention (host side, pure C++).
+//
+// Query side (forward and dQ kernels): the rows of one kv head are GQA-packed (all g query
+// heads of a token are consecutive rows) and cut into tiles of kQTile rows per response.
+// Key side: the P prompt keys are cut into tiles of kKTile keys and distributed over S
+// splits; the response's own (causal) keys are handled by the last split. Split partials
+// are merged by log-sum-exp (forward) or summed (dQ), which is the same algebra as merging
+// attention partials of prompt pages held by different owners (LongStraw study notes,
+// §3-2 (2): cross-rank log-sum-exp and output merge). S is chosen to fill the chip.
+//
+// dK/dV kernel: one workgroup owns kDKTile keys of one kv head, for every prompt key tile
+// (exact prompt-gradient mode only) and every response's suffix key tile.
+#include <algorithm>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace lsr {
+
+namespace {
+constexpr int kQTile = 128;   // packed query rows per forward / dQ workgroup
+constexpr int kKTile = 64;    // keys per forward / dQ tile
+constexpr int kDKTile = 128;  // keys per dK/dV workgroup
+constexpr int kTargetBlocks = 2048;
+constexpr int kMinTilesPerSplit = 8;
+constexpr int kMaxSplits = 64;
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, const int32_t* cu, AttnPlan* pl) {
+  const bool ok = (Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128);
+  if (!ok) return false;
+  std::memset(pl, 0, sizeof(*pl));
+  const int g = Hq / Hkv;
+  const long long T = cu[n_resp];
+  int qt = 0, kt = 0;
+  for (int i = 0; i < n_resp; ++i) {
+    pl->tile0[i] = qt;
+    pl->ktile0[i] = kt;
+    const long long R = cu[i + 1] - cu[i];
+    qt += (int)((R * g + kQTile - 1) / kQTile);
+    kt += (int)((R + kDKTile - 1) / kDKTile);
+  }
+  for (int i = n_resp; i <= kMaxResp; ++i) {
+    pl->tile0[i] = qt;
+    pl->ktile0[i] = kt;
+  }
+  pl->qtiles = qt;
+  pl->ptiles = (P + kKTile - 1) / kKTile;
+  pl->ktiles_prompt = which == 1 ? (P + kDKTile - 1) / kDKTile : 0;
+
+  int S = 1;
+  const long long w0 = (long long)qt * Hkv;
+  if (pl->ptiles > 0 && w0 > 0) {
+    S = (int)std::min<long long>(kMaxSplits, (kTargetBlocks + w0 - 1) / w0);
+    S = std::max(1, std::min(S, pl->ptiles / kMinTilesPerSplit));
+  }
+  int pps = pl->ptiles > 0 ? (pl->ptiles + S - 1) / S : 0;
+  if (pps > 0) S = (pl->ptiles + pps - 1) / pps;  // no empty splits
+  pl->splits = S;
+  pl->ptiles_per_split = pps;
+
+  size_t off = 0;
+  if (which == 0) {
+    if (S > 1) {
+      pl->off_a = off;
+      off = align256(off + (size_t)S * T * Hq * Dv * 4);
+      pl->off_b = off;
+      off = align256(off + (size_t)S * Hq * T * 4);
+    }
+  } else {
+    pl->off_a = off;  // delta [Hq, T]
+    off = align256(off + (size_t)Hq * T * 4);
+    if (S > 1) {
+      pl->off_b = off;
+      off = align256(off + (size_t)S * T * Hq * Dqk * 4);
+    }
+  }
+  pl->ws_bytes = off;
+  return true;
+}
+
+}  // namespace lsr

@@ -1,0 +1,99 @@
+// Device helpers shared by the gfx950 kernels of liblsreplay.
+//
+// MFMA operand layouts used throughout (v_mfma_f32_32x32x16_bf16, wave64):
+//   A[m][k] (32x16): lane l holds A[l%32][8*(l/32) + 0..7]   (8 bf16, one 16-byte LDS read
+//                    when a row's k values are contiguous)
+//   B[k][n] (16x32): lane l holds B[8*(l/32) + 0..7][l%32]
+//   C[m][n] (32x32): lane l, register r holds C[8*(r/4) + 4*(l/32) + r%4][l%32]
+// So a C tile keeps one n index per lane. The kernels put the softmax row (query) on n
+// whenever per-row statistics are needed, so row max/sum/rescale stay lane-local.
+//
+// A C tile's 16 registers, converted to bf16 in order, form the B operand of the next
+// MFMA whose k index runs over C's m index permuted as
+//   k position (g = l/32, j) <-> m = 16*h + 4*g + j        (j = 0..3)
+//                                 m = 16*h + 8 + 4*g + j-4  (j = 4..7)
+// for register half h (registers 8h..8h+7). The matching A operand is fetched with the
+// same permutation via ds_read_b64_tr_b16 (two 4-element transposed reads).
+//
+// ds_read_b64_tr_b16 (gfx950): within each 16-lane group, lane j passes the address of
+// element (k0 + j/4, n0 + 4*(j%4)) of a row-major [k][n] LDS tile and receives the four
+// values (k0 + e, n0 + j), e = 0..3 -- a transposed 4x16 block.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lsr {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LSR_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Buffer resource word 3 for the gfx9 family (raw buffer, 32-bit data format) and the
+// cache-policy bit that marks streaming (non-temporal) accesses.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kSlc = 2;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
+
+// Round-to-nearest-even pack (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8 consecutive registers of a C tile (r0..r0+7) -> bf16 B/A operand.
+__device__ __forceinline__ bf16x8 c_regs_to_bf16x8(const f32x16& c, int r0) {
+  bf16x8 v;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (__bf16)c[r0 + j];
+  return v;
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t* lds_elem_ptr) {
+  return *reinterpret_cast<const LSR_LDS bf16x8*>(reinterpret_cast<uintptr_t>(lds_elem_ptr));
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* lds_elem_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<LSR_LDS s16x4*>(reinterpret_cast<uintptr_t>(lds_elem_ptr)));
+}
+
+__device__ __forceinline__ bf16x8 join_tr(const s16x4& a, const s16x4& b) {
+  typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+  s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+}  // namespace lsr

@@ -1,0 +1,206 @@
+// Fused clipped-GRPO token objective (LongStraw study notes, §1-1, L_policy equation).
+//
+// One workgroup per token row. The bf16 logits row is read from HBM exactly once into
+// VGPRs (16-byte loads, consecutive threads on consecutive 16-byte chunks); the row max
+// and the sum of exponentials are wave reductions combined through LDS; the dlogits row is
+// then produced from the same registers and written once. HBM traffic per token is the
+// algorithmic minimum: 2V bytes in, 2V bytes out, plus target, old log-prob, log-prob.
+//
+// Per row t of response i (A = A_i, w = 1/(G R_i)):
+//   lse = max + log(sum exp(x - max)),  logp = x_y - lse,  rho = exp(logp - old)
+//   term = min(rho A, clip(rho, 1-eps, 1+eps) A);  row_loss = -w term
+//   clipped = clip(rho) A < rho A  (then the gradient is zero)
+//   dlogits = c (softmax(x) - onehot(y)),  c = clipped ? 0 : w A rho
+// The loss is summed by a second single-workgroup kernel in a fixed order (deterministic).
+#include "common.h"
+#include "kernels.h"
+
+namespace lsr {
+
+namespace {
+
+__device__ __forceinline__ void row_coefs(const GrpoArgs& a, int64_t row, float* A, float* w) {
+  int i = 0;
+  while (i + 1 < a.n && row >= a.row_end[i]) ++i;
+  *A = a.A[i];
+  *w = a.w[i];
+}
+
+template <int NT>
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+  constexpr int NW = NT / 64;
+  v = is_max ? wave_max(v) : wave_sum(v);
+  const int wv = threadIdx.x / 64;
+  __syncthreads();  // red[] may still be read from a previous reduction
+  if ((threadIdx.x & 63) == 0) red[wv] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) r = is_max ? fmaxf(r, red[k]) : r + red[k];
+  return r;
+}
+
+// Scalar part shared by both row kernels: everything that depends on (x_y, lse) only.
+// Returns the dlogits coefficient c. A target outside [0, V) or NaN data make the row NaN.
+__device__ __forceinline__ float row_scalar(const GrpoArgs& a, int64_t row, float xy, bool y_ok, float lse) {
+  float A, w;
+  row_coefs(a, row, &A, &w);
+  const float logp = y_ok ? xy - lse : __builtin_nanf("");
+  const float rho = expf(logp - a.old_logp[row]);
+  const bool nan = !(rho == rho);
+  const float unclipped = rho * A;
+  const float clipped_v = fminf(fmaxf(rho, 1.0f - a.eps), 1.0f + a.eps) * A;
+  const bool clipped = !nan && (clipped_v < unclipped);
+  const float term = nan ? rho : fminf(unclipped, clipped_v);
+  if (threadIdx.x == 0) {
+    a.row_loss[row] = -w * term;
+    if (a.logp_out) a.logp_out[row] = logp;
+    if (a.clipped_out) a.clipped_out[row] = clipped ? 1 : 0;
+  }
+  return clipped ? 0.0f : w * A * rho;
+}
+
+// Vector path: V % 8 == 0, 16-byte aligned rows; NCH 16-byte chunks per thread in registers.
+// Rows are read through a buffer resource (one VGPR offset per thread, the chunk column in
+// the SGPR offset) so no per-chunk 64-bit addresses stay live; chunks past the row end are
+// masked to -inf after the load and never stored.
+template <int NT, int NCH>
+__global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
+  __shared__ float red[NT / 64];
+  __shared__ float xy_s;
+  const int64_t row = blockIdx.x;
+  const int nch = a.V >> 3;
+  const int y = a.targets[row];
+  const bool y_ok = (y >= 0) && (y < a.V);
+  const __amdgpu_buffer_rsrc_t src =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.logits + row * (int64_t)a.V), 0, a.V * 2, kBufferWord3);
+  const int voff = threadIdx.x * 16;
+
+  u32x4 v[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(src, voff, j * NT * 16, kSlc);
+#pragma unroll
+  for (int j = 0; j < NCH; ++j)
+    if ((int)threadIdx.x + j * NT >= nch) v[j] = u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+  if (threadIdx.x == 0) xy_s = y_ok ? bf16_to_f32(a.logits[row * (int64_t)a.V + y]) : 0.0f;
+
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    m = fmaxf(m, fmaxf(fmaxf(bf16_lo(v[j].x), bf16_hi(v[j].x)), fmaxf(bf16_lo(v[j].y), bf16_hi(v[j].y))));
+    m = fmaxf(m, fmaxf(fmaxf(bf16_lo(v[j].z), bf16_hi(v[j].z)), fmaxf(bf16_lo(v[j].w), bf16_hi(v[j].w))));
+  }
+  m = block_reduce<NT>(m, red, true);
+  // keep only the packed row live across the passes (re-derive floats on use, no spills)
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) asm volatile("" : "+v"(v[j]));
+  const float mb = m * kLog2e;
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s += fast_exp2(__builtin_fmaf(bf16_lo(v[j][q]), kLog2e, -mb));
+      s += fast_exp2(__builtin_fmaf(bf16_hi(v[j][q]), kLog2e, -mb));
+    }
+  }
+  s = block_reduce<NT>(s, red, false);
+  const float lse = m + fast_log2(s) * kLn2;
+  const float c = row_scalar(a, row, xy_s, y_ok, lse);
+  const float lb = lse * kLog2e;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) asm volatile("" : "+v"(v[j]));
+
+  // Stores are global (FLAT) stores: the compiler protects their data registers from the
+  // next VALU write, which it does not do for buffer stores with an SGPR offset.
+  char* dst = reinterpret_cast<char*>(a.dlogits + row * (int64_t)a.V);
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int cj = (int)threadIdx.x + j * NT;
+    const int e0 = cj * 8;
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = e0 + 2 * q;
+      float p0 = fast_exp2(__builtin_fmaf(bf16_lo(v[j][q]), kLog2e, -lb));
+      float p1 = fast_exp2(__builtin_fmaf(bf16_hi(v[j][q]), kLog2e, -lb));
+      p0 -= (e == y) ? 1.0f : 0.0f;
+      p1 -= (e + 1 == y) ? 1.0f : 0.0f;
+      o[q] = pack_bf16x2(c * p0, c * p1);
+    }
+    if (cj < nch) __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst + voff + j * NT * 16));
+  }
+}
+
+// Element-wise path for any V / alignment: three passes over the row (L2-resident).
+__global__ __launch_bounds__(256) void grpo_rows_scalar(GrpoArgs a) {
+  constexpr int NT = 256;
+  __shared__ float red[NT / 64];
+  const int64_t row = blockIdx.x;
+  const uint16_t* x = a.logits + row * (int64_t)a.V;
+  const int y = a.targets[row];
+  const bool y_ok = (y >= 0) && (y < a.V);
+  float m = -INFINITY;
+  for (int e = threadIdx.x; e < a.V; e += NT) m = fmaxf(m, bf16_to_f32(x[e]));
+  m = block_reduce<NT>(m, red, true);
+  float s = 0.0f;
+  for (int e = threadIdx.x; e < a.V; e += NT) s += fast_exp2((bf16_to_f32(x[e]) - m) * kLog2e);
+  s = block_reduce<NT>(s, red, false);
+  const float lse = m + fast_log2(s) * kLn2;
+  const float xy = y_ok ? bf16_to_f32(x[y]) : 0.0f;
+  const float c = row_scalar(a, row, xy, y_ok, lse);
+  uint16_t* d = a.dlogits + row * (int64_t)a.V;
+  for (int e = threadIdx.x; e < a.V; e += NT) {
+    float p = fast_exp2((bf16_to_f32(x[e]) - lse) * kLog2e) - ((e == y) ? 1.0f : 0.0f);
+    d[e] = (uint16_t)(pack_bf16x2(c * p, 0.0f) & 0xffffu);
+  }
+}
+
+// Fixed-order sum of the per-row losses, added to *loss_accum.
+__global__ __launch_bounds__(256) void grpo_sum(const float* row_loss, int64_t T, float* loss_accum) {
+  __shared__ double part[256];
+  double acc = 0.0;
+  for (int64_t r = threadIdx.x; r < T; r += 256) acc += (double)row_loss[r];
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) part[threadIdx.x] += part[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss_accum = (float)((double)*loss_accum + part[0]);
+}
+
+template <int NT, int NCH>
+hipError_t go_vec(const GrpoArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((grpo_rows_vec<NT, NCH>), dim3((unsigned)a.T), dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t grpo_workspace_bytes(int64_t T) { return (size_t)((T * 4 + 255) / 256 * 256); }
+
+hipError_t launch_grpo(const GrpoArgs& a, bool vec, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (vec) {
+    const int nch = a.V / 8;
+    if (nch <= 256) e = go_vec<256, 1>(a, st);
+    else if (nch <= 512) e = go_vec<256, 2>(a, st);
+    else if (nch <= 1024) e = go_vec<256, 4>(a, st);
+    else if (nch <= 2048) e = go_vec<256, 8>(a, st);
+    else if (nch <= 4096) e = go_vec<256, 16>(a, st);
+    else if (nch <= 1024 * 8) e = go_vec<1024, 8>(a, st);
+    else if (nch <= 1024 * 12) e = go_vec<1024, 12>(a, st);
+    else if (nch <= 1024 * 16) e = go_vec<1024, 16>(a, st);
+    else if (nch <= 1024 * 19) e = go_vec<1024, 19>(a, st);
+    else e = go_vec<1024, 24>(a, st);  // V <= 196608 (checked by the host API)
+  } else {
+    hipLaunchKernelGGL(grpo_rows_scalar, dim3((unsigned)a.T), dim3(256), 0, st, a);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(grpo_sum, dim3(1), dim3(256), 0, st, (const float*)a.row_loss, a.T, a.loss_accum);
+  return hipGetLastError();
+}
+
+}  // namespace lsr

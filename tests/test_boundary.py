@@ -1,0 +1,138 @@
+"""The C ABI without a GPU: the library loads, exports every function include/ls_replay.h
+declares, and rejects invalid arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from prefix_shared_branch_amd import lsreplay as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BAD = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def declared_functions():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ls_\w+)\s*\(", src, flags=re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert names == set(L.EXPORTED), names
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for c, s in ((0, "LS_OK"), (-1, "LS_ERR_INVALID_ARG"), (-2, "LS_ERR_UNSUPPORTED"), (-3, "LS_ERR_WORKSPACE"),
+                 (-4, "LS_ERR_HIP"), (5, "LS_UNKNOWN_STATUS")):
+        assert L.ls_status_string(c) == s
+
+
+def desc(**kw):
+    d = L.AttnDesc()
+    d.P, d.Hq, d.Hkv, d.Dqk, d.Dv, d.ldk, d.ldv, d.softmax_scale = 1024, 8, 2, 64, 64, 128, 128, 0.125
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def ws_bytes(d, cu, which=0):
+    cu = np.asarray(cu, dtype=np.int32)
+    out = ctypes.c_size_t(0)
+    rc = L.lib().ls_replay_attn_workspace_bytes(ctypes.byref(d), len(cu) - 1,
+                                                cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), which,
+                                                ctypes.byref(out))
+    return rc, out.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=7), L.LS_ERR_INVALID_ARG),            # Hq % Hkv != 0
+    (dict(P=-1), L.LS_ERR_INVALID_ARG),
+    (dict(Hkv=0), L.LS_ERR_INVALID_ARG),
+    (dict(Dqk=96, Dv=96, ldk=192, ldv=192), L.LS_ERR_UNSUPPORTED),
+    (dict(Dv=128), L.LS_ERR_INVALID_ARG),           # Dv > Dqk
+    (dict(ldk=120), L.LS_ERR_INVALID_ARG),          # ldk < Hkv * Dqk
+    (dict(ldk=132), L.LS_ERR_INVALID_ARG),          # not a multiple of 8
+    (dict(softmax_scale=float("nan")), L.LS_ERR_INVALID_ARG),
+    (dict(softmax_scale=0.0), L.LS_ERR_INVALID_ARG),
+])
+def test_desc_validation(kw, code):
+    assert ws_bytes(desc(**kw), [0, 100])[0] == code
+
+
+def test_seqlens_validation():
+    d = desc()
+    assert ws_bytes(d, [1, 100])[0] == L.LS_ERR_INVALID_ARG         # cu[0] != 0
+    assert ws_bytes(d, [0, 100, 50])[0] == L.LS_ERR_INVALID_ARG     # decreasing
+    assert ws_bytes(d, list(range(0, 66)))[0] == L.LS_ERR_UNSUPPORTED  # 65 responses
+    assert ws_bytes(d, [0, 0, 10])[0] == L.LS_OK                    # empty response allowed
+    assert ws_bytes(d, [0, 100], which=3)[0] == L.LS_ERR_INVALID_ARG
+    rc, n = ws_bytes(desc(P=0), [0, 10], which=1)
+    assert rc == L.LS_OK and n > 0                                   # delta buffer
+
+
+def _fwd(d, cu, Kp=BAD, Vp=BAD, Q=BAD, Ks=BAD, Vs=BAD, O=BAD, lse=BAD, ws=BAD, nbytes=1 << 40):
+    cu = np.asarray(cu, dtype=np.int32)
+    return L.lib().ls_replay_attn_fwd(None, ctypes.byref(d), Kp, Vp, len(cu) - 1,
+                                      cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), Q, Ks, Vs, O, lse, ws,
+                                      nbytes)
+
+
+def _bwd(d, cu, dKp=BAD, dVp=BAD, ws=BAD, nbytes=1 << 40, Q=BAD):
+    cu = np.asarray(cu, dtype=np.int32)
+    return L.lib().ls_replay_attn_bwd(None, ctypes.byref(d), BAD, BAD, len(cu) - 1,
+                                      cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), Q, BAD, BAD, BAD, BAD,
+                                      BAD, BAD, BAD, BAD, dKp, dVp, ws, nbytes)
+
+
+def test_fwd_bwd_pointer_and_workspace_validation():
+    d = desc()
+    assert _fwd(d, [0, 10], Q=None) == L.LS_ERR_INVALID_ARG
+    assert _fwd(d, [0, 10], Q=ctypes.c_void_p(0x1008)) == L.LS_ERR_INVALID_ARG   # misaligned
+    assert _fwd(d, [0, 10], Kp=None) == L.LS_ERR_INVALID_ARG                     # P > 0 needs prompt K
+    assert _fwd(d, [0, 0]) == L.LS_OK                                            # nothing to do
+    rc, need = ws_bytes(desc(P=1 << 20), [0, 64], 0)
+    assert rc == L.LS_OK and need > 0
+    assert _fwd(desc(P=1 << 20), [0, 64], nbytes=need - 1) == L.LS_ERR_WORKSPACE
+    assert _fwd(desc(P=1 << 20), [0, 64], ws=None, nbytes=need) == L.LS_ERR_WORKSPACE
+    assert _bwd(d, [0, 10], dKp=None) == L.LS_ERR_INVALID_ARG                    # exactly one accumulator
+    assert _bwd(d, [0, 10], dVp=None) == L.LS_ERR_INVALID_ARG
+    assert _bwd(d, [0, 10], dKp=None, dVp=None, Q=None) == L.LS_ERR_INVALID_ARG
+    assert _bwd(d, [0, 10], nbytes=0) == L.LS_ERR_WORKSPACE
+
+
+def _loss(V=4096, G=2, R=(3, 4), rewards=(0.0, 1.0), eps=0.2, first=0, count=2, logits=BAD, dl=ctypes.c_void_p(0x90000),
+          ws=BAD, nbytes=1 << 30, targets=BAD):
+    Ra = np.asarray(R, dtype=np.int32)
+    ra = np.asarray(rewards, dtype=np.float32)
+    return L.lib().ls_grpo_token_loss(None, V, G, Ra.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                      ra.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), eps, first, count, logits,
+                                      targets, BAD, dl, BAD, None, None, ws, nbytes)
+
+
+def test_loss_validation():
+    assert _loss(V=0) == L.LS_ERR_INVALID_ARG
+    assert _loss(V=200000) == L.LS_ERR_UNSUPPORTED
+    assert _loss(eps=0.0) == L.LS_ERR_INVALID_ARG
+    assert _loss(eps=1.0) == L.LS_ERR_INVALID_ARG
+    assert _loss(eps=float("nan")) == L.LS_ERR_INVALID_ARG
+    assert _loss(R=(0, 4)) == L.LS_ERR_INVALID_ARG                  # R_i <= 0
+    assert _loss(rewards=(0.0, float("inf"))) == L.LS_ERR_INVALID_ARG
+    assert _loss(first=1, count=2) == L.LS_ERR_INVALID_ARG          # beyond G
+    assert _loss(count=0) == L.LS_ERR_INVALID_ARG
+    assert _loss(targets=None) == L.LS_ERR_INVALID_ARG
+    assert _loss(dl=BAD) == L.LS_ERR_INVALID_ARG                    # dlogits aliases logits
+    assert _loss(ws=None) == L.LS_ERR_WORKSPACE
+    assert _loss(nbytes=4) == L.LS_ERR_WORKSPACE
+    out = ctypes.c_size_t(0)
+    assert L.lib().ls_grpo_workspace_bytes(1000, 4096, ctypes.byref(out)) == L.LS_OK and out.value >= 4000
+    assert L.lib().ls_grpo_workspace_bytes(-1, 4096, ctypes.byref(out)) == L.LS_ERR_INVALID_ARG

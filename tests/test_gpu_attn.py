@@ -1,0 +1,187 @@
+"""GPU parity of ls_replay_attn_fwd / ls_replay_attn_bwd against the fp64 oracle.
+
+Replay semantics (LongStraw study notes §2-1 step 4, §3-2 (2)/(4)): response queries attend to
+the resident prompt K/V and, causally, to their own K/V; serial replay adds each response's
+prompt-side gradient into fp32 accumulators owned by the prompt pages. Every case runs the
+kernels through the C ABI on seeded bf16 inputs and compares with the oracle element by element.
+"""
+import numpy as np
+import pytest
+
+from oracle import attn
+from prefix_shared_branch_amd import inputs
+from tests.helpers import check_bf16_out, check_fp32_accum, dev_bf16, host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+class Case:
+    """Seeded inputs of one config with explicit response lengths (packed)."""
+
+    def __init__(self, cfg, lengths):
+        import torch
+        self.cfg = cfg
+        self.lengths = np.asarray(lengths, dtype=np.int32)
+        self.cu = inputs.cu_seqlens(self.lengths)
+        T = int(self.cu[-1])
+        kp = inputs.prompt_k(cfg)
+        vp = inputs.prompt_v(cfg) if not cfg.mla else None
+        q, ks, do = inputs.suffix_q(cfg, 0, T), inputs.suffix_k(cfg, 0, T), inputs.suffix_do(cfg, 0, T)
+        vs = inputs.suffix_v(cfg, 0, T) if not cfg.mla else None
+        self.h = dict(Kp=inputs.bf16_bits_to_f64(kp), Q=inputs.bf16_bits_to_f64(q), Ks=inputs.bf16_bits_to_f64(ks),
+                      dO=inputs.bf16_bits_to_f64(do))
+        self.kp, self.q, self.ks, self.do = dev_bf16(kp), dev_bf16(q), dev_bf16(ks), dev_bf16(do)
+        if cfg.mla:
+            self.vp, self.vs = self.kp[:, :, :cfg.Dv], self.ks[:, :, :cfg.Dv]
+            self.h["Vp"], self.h["Vs"] = self.h["Kp"][:, :, :cfg.Dv], self.h["Ks"][:, :, :cfg.Dv]
+        else:
+            self.vp, self.vs = dev_bf16(vp), dev_bf16(vs)
+            self.h["Vp"], self.h["Vs"] = inputs.bf16_bits_to_f64(vp), inputs.bf16_bits_to_f64(vs)
+        self.torch = torch
+
+    def fwd(self, cu=None, sl=slice(None)):
+        from prefix_shared_branch_amd import lsreplay as L
+        cu = self.cu if cu is None else cu
+        return L.ls_replay_attn_fwd(self.q[sl], self.ks[sl], self.vs[sl], self.kp, self.vp, cu, self.cfg.scale)
+
+    def bwd(self, o, lse, dkp=None, dvp=None, cu=None, sl=slice(None)):
+        from prefix_shared_branch_amd import lsreplay as L
+        cu = self.cu if cu is None else cu
+        return L.ls_replay_attn_bwd(self.q[sl], self.ks[sl], self.vs[sl], self.kp, self.vp, cu, o, lse, self.do[sl],
+                                    dkp, dvp, self.cfg.scale)
+
+    def accums(self):
+        t = self.torch
+        P, Hkv = self.cfg.P, self.cfg.Hkv
+        return (t.zeros(P, Hkv, self.cfg.Dqk, dtype=t.float32, device="cuda"),
+                t.zeros(P, Hkv, self.cfg.Dv, dtype=t.float32, device="cuda"))
+
+    def oracle(self, accumulate=True):
+        h = self.h
+        O, LSE = attn.replay_attn_fwd(h["Kp"], h["Vp"], h["Q"], h["Ks"], h["Vs"], self.cu, self.cfg.scale)
+        dKp = np.zeros_like(h["Kp"]) if accumulate else None
+        dVp = np.zeros(h["Vp"].shape) if accumulate else None
+        dQ, dKs, dVs = attn.replay_attn_bwd(h["Kp"], h["Vp"], h["Q"], h["Ks"], h["Vs"], h["dO"], self.cu,
+                                            self.cfg.scale, dKp, dVp)
+        return dict(O=O, LSE=LSE, dQ=dQ, dKs=dKs, dVs=dVs, dKp=dKp, dVp=dVp)
+
+
+def _check_all(got, ref, literal_abs=True):
+    check_bf16_out(host_f64(got["O"]), ref["O"], "O", literal_abs=literal_abs)
+    lse = host_f64(got["LSE"])
+    assert np.max(np.abs(lse - ref["LSE"])) <= 1e-4, np.max(np.abs(lse - ref["LSE"]))
+    check_bf16_out(host_f64(got["dQ"]), ref["dQ"], "dQ", literal_abs=literal_abs)
+    check_bf16_out(host_f64(got["dKs"]), ref["dKs"], "dKs", literal_abs=literal_abs)
+    check_bf16_out(host_f64(got["dVs"]), ref["dVs"], "dVs", literal_abs=literal_abs)
+    if ref.get("dKp") is not None and ref["dKp"].size:
+        check_fp32_accum(host_f64(got["dKp"]), ref["dKp"], "dKp")
+        check_fp32_accum(host_f64(got["dVp"]), ref["dVp"], "dVp")
+
+
+def _serial(case):
+    """Serial replay: one call per response, prompt gradients accumulated in place."""
+    t = case.torch
+    dkp, dvp = case.accums()
+    outs = {k: [] for k in ("O", "LSE", "dQ", "dKs", "dVs")}
+    for i in range(len(case.lengths)):
+        r0, r1 = int(case.cu[i]), int(case.cu[i + 1])
+        cu1 = [0, r1 - r0]
+        o, lse = case.fwd(cu1, slice(r0, r1))
+        dq, dks, dvs = case.bwd(o, lse, dkp, dvp, cu1, slice(r0, r1))
+        for k, v in zip(("O", "LSE", "dQ", "dKs", "dVs"), (o, lse, dq, dks, dvs)):
+            outs[k].append(v)
+    t.cuda.synchronize()
+    got = {k: t.cat(v, dim=1 if k == "LSE" else 0) for k, v in outs.items()}
+    got["dKp"], got["dVp"] = dkp, dvp
+    return got
+
+
+def test_tiny_full_group_serial_replay():
+    case = Case(inputs.CONFIGS["tiny"], inputs.response_lengths(inputs.CONFIGS["tiny"]))
+    _check_all(_serial(case), case.oracle())
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_ragged_multi_response_call(D):
+    cfg = inputs.replace(inputs.CONFIGS["tiny"], Hq=6, Hkv=2, Dqk=D, Dv=D, P=1000, seed=31)
+    case = Case(cfg, [1, 37, 130])
+    t = case.torch
+    dkp, dvp = case.accums()
+    o, lse = case.fwd()
+    dq, dks, dvs = case.bwd(o, lse, dkp, dvp)
+    t.cuda.synchronize()
+    _check_all(dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp), case.oracle())
+
+
+def test_no_prompt_is_plain_causal():
+    cfg = inputs.replace(inputs.CONFIGS["tiny"], P=0, seed=32)
+    case = Case(cfg, [70, 5])
+    o, lse = case.fwd()
+    dq, dks, dvs = case.bwd(o, lse)
+    case.torch.cuda.synchronize()
+    # no prompt: gradients of order 1-4, so only the scale-aware bounds apply
+    _check_all(dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs), case.oracle(accumulate=False), literal_abs=False)
+
+
+def test_split_k_merge_path():
+    """Few query tiles and a long prompt: the planner picks many splits (LSE merge, dQ partial sums)."""
+    cfg = inputs.replace(inputs.CONFIGS["tiny"], Hq=8, Hkv=2, Dqk=128, Dv=128, P=20000 + 37, seed=33)
+    case = Case(cfg, [50])
+    from prefix_shared_branch_amd import lsreplay as L
+    desc = L.make_desc(case.q, case.kp, case.vp, case.ks, case.vs, cfg.scale)
+    assert L.ls_replay_attn_workspace_bytes(desc, case.cu, 0) > 0      # split partials in use
+    t = case.torch
+    dkp, dvp = case.accums()
+    o, lse = case.fwd()
+    dq, dks, dvs = case.bwd(o, lse, dkp, dvp)
+    t.cuda.synchronize()
+    _check_all(dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp), case.oracle())
+
+
+def test_serial_equals_batched_call_and_modes():
+    """One call over the whole group == G serial calls (accumulators to 1e-6 rel); response-only
+    mode leaves accumulators untouched and gives bitwise the same dQ/dKs/dVs; K/V never written."""
+    cfg = inputs.replace(inputs.CONFIGS["tiny"], seed=34)
+    case = Case(cfg, [64, 100, 77, 128])
+    t = case.torch
+    kp0, vp0 = case.kp.clone(), case.vp.clone()
+    ser = _serial(case)
+    dkp, dvp = case.accums()
+    o, lse = case.fwd()
+    dq, dks, dvs = case.bwd(o, lse, dkp, dvp)
+    snap_k, snap_v = dkp.clone(), dvp.clone()
+    dq2, dks2, dvs2 = case.bwd(o, lse)                       # response-only closure
+    t.cuda.synchronize()
+    for a, b in ((dkp, ser["dKp"]), (dvp, ser["dVp"])):
+        rel = (a - b).norm().item() / b.norm().item()
+        assert rel <= 1e-6, rel
+    assert t.equal(o, ser["O"]) and t.equal(lse, ser["LSE"])
+    assert t.equal(dq, dq2) and t.equal(dks, dks2) and t.equal(dvs, dvs2)
+    assert t.equal(dkp, snap_k) and t.equal(dvp, snap_v)
+    assert t.equal(case.kp, kp0) and t.equal(case.vp, vp0)
+
+
+def test_bitwise_determinism():
+    cfg = inputs.replace(inputs.CONFIGS["tiny"], P=5000, seed=35)
+    case = Case(cfg, [90, 33])
+    t = case.torch
+    res = []
+    for _ in range(2):
+        dkp, dvp = case.accums()
+        o, lse = case.fwd()
+        dq, dks, dvs = case.bwd(o, lse, dkp, dvp)
+        res.append((o, lse, dq, dks, dvs, dkp, dvp))
+    t.cuda.synchronize()
+    for a, b in zip(*res):
+        assert t.equal(a, b)
+
+
+def test_mid_shape_short_response():
+    """Mid config (Hq 32 / Hkv 8, D 128, P 32768) with its first 256 response rows: an exact sub-problem."""
+    case = Case(inputs.CONFIGS["mid"], [256])
+    t = case.torch
+    dkp, dvp = case.accums()
+    o, lse = case.fwd()
+    dq, dks, dvs = case.bwd(o, lse, dkp, dvp)
+    t.cuda.synchronize()
+    _check_all(dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp), case.oracle())
