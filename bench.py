@@ -1,0 +1,298 @@
+"""Benchmark of the branch-replay hot path on one MI355X.
+
+One step = one GRPO group of the named workload, replayed serially as the LongStraw study
+notes prescribe (§2-1 step 4, §3-2 (4)): zero the resident prompt-gradient accumulators,
+then for each of the G responses run replay attention forward, the fused clipped-GRPO token
+loss over that response's logits, and replay attention backward (which adds the response's
+prompt-side gradient in place). Inputs are seeded synthetic tensors already resident in HBM
+when the timed region starts.
+
+Prints one JSON line (rank 0). `value` = replayed response tokens per second of whole steps.
+Also reported: the dominant kernel against its roofline, per-call times, algorithmic and
+executed TFLOP/s, the loss kernel's GB/s, and the CPU oracle timed on a bounded sample.
+
+usage: python bench.py [--steps K] [--warmup W] [--workload million] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from prefix_shared_branch_amd import inputs  # noqa: E402
+
+METRIC = "replayed response tokens/s (fwd+bwd) at prompt P; % bf16 MFMA peak; loss GB/s"
+PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="million", choices=["tiny", "mid", "long", "million"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = automatic)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def to_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class Workload:
+    """Resident inputs and reusable outputs/workspaces of one group."""
+
+    def __init__(self, cfg):
+        import torch
+        from prefix_shared_branch_amd import lsreplay as L
+        self.cfg = cfg
+        self.R = inputs.response_lengths(cfg)
+        self.G = int(cfg.G)
+        self.cu = inputs.cu_seqlens(self.R)
+        self.rewards = inputs.rewards(cfg)
+        T = int(self.cu[-1])
+        t0 = time.time()
+        self.kp = to_dev(inputs.prompt_k(cfg))
+        self.vp = to_dev(inputs.prompt_v(cfg))
+        log(f"prompt K/V resident ({2 * self.kp.numel() * 2 / 2**30:.2f} GiB) in {time.time() - t0:.1f}s")
+        self.q = to_dev(inputs.suffix_q(cfg, 0, T))
+        self.ks = to_dev(inputs.suffix_k(cfg, 0, T))
+        self.vs = to_dev(inputs.suffix_v(cfg, 0, T))
+        self.do = to_dev(inputs.suffix_do(cfg, 0, T))
+        self.logits, self.targets, self.old = [], [], []
+        t0 = time.time()
+        for i in range(self.G):
+            lg = to_dev(inputs.logits(cfg, i, 0, int(self.R[i])))
+            y = torch.from_numpy(inputs.targets(cfg, i, int(self.R[i]))).cuda()
+            # old-policy log-probs = current log-probs + N(0, sigma^2) noise (input synthesis only)
+            lp = torch.empty(int(self.R[i]), dtype=torch.float32, device="cuda")
+            for r0 in range(0, int(self.R[i]), 512):
+                blk = lg[r0:r0 + 512].float()
+                lp[r0:r0 + 512] = torch.log_softmax(blk, dim=1).gather(1, y[r0:r0 + 512, None].long())[:, 0]
+                del blk
+            noise = torch.from_numpy(inputs.old_logp_noise(cfg, i, int(self.R[i]))).cuda()
+            self.logits.append(lg)
+            self.targets.append(y)
+            self.old.append(lp + noise)
+        log(f"logits of {self.G} responses resident in {time.time() - t0:.1f}s")
+        Rmax = int(self.R.max())
+        dev = "cuda"
+        self.dkp = torch.zeros(cfg.P, cfg.Hkv, cfg.Dqk, dtype=torch.float32, device=dev)
+        self.dvp = torch.zeros(cfg.P, cfg.Hkv, cfg.Dv, dtype=torch.float32, device=dev)
+        self.o = torch.empty(Rmax, cfg.Hq, cfg.Dv, dtype=torch.bfloat16, device=dev)
+        self.dq = torch.empty(Rmax, cfg.Hq, cfg.Dqk, dtype=torch.bfloat16, device=dev)
+        self.dks = torch.empty(Rmax, cfg.Hkv, cfg.Dqk, dtype=torch.bfloat16, device=dev)
+        self.dvs = torch.empty(Rmax, cfg.Hkv, cfg.Dv, dtype=torch.bfloat16, device=dev)
+        self.dlogits = torch.empty(Rmax, cfg.V, dtype=torch.bfloat16, device=dev)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
+        desc = L.make_desc(self.q, self.kp, self.vp, self.ks, self.vs, cfg.scale)
+        wf = max(L.ls_replay_attn_workspace_bytes(desc, [0, int(r)], 0) for r in self.R)
+        wb = max(L.ls_replay_attn_workspace_bytes(desc, [0, int(r)], 1) for r in self.R)
+        wl = L.ls_grpo_workspace_bytes(Rmax, cfg.V)
+        self.ws = torch.empty(max(wf, wb, wl, 256), dtype=torch.uint8, device=dev)
+        self.lse = [torch.empty(cfg.Hq, int(r), dtype=torch.float32, device=dev) for r in self.R]
+
+    def response(self, i, times=None, exact=True):
+        import torch
+        from prefix_shared_branch_amd import lsreplay as L
+        cfg = self.cfg
+        r0, r1 = int(self.cu[i]), int(self.cu[i + 1])
+        R = r1 - r0
+        sl = slice(r0, r1)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if times is not None else None
+        if ev:
+            ev[0].record()
+        o, lse = L.ls_replay_attn_fwd(self.q[sl], self.ks[sl], self.vs[sl], self.kp, self.vp, [0, R], cfg.scale,
+                                      out=self.o[:R], lse=self.lse[i], workspace=self.ws)
+        if ev:
+            ev[1].record()
+        L.ls_grpo_token_loss(self.logits[i], self.targets[i], self.old[i], self.R, self.rewards, cfg.eps, i, 1,
+                             self.loss, dlogits=self.dlogits[:R], workspace=self.ws)
+        if ev:
+            ev[2].record()
+        L.ls_replay_attn_bwd(self.q[sl], self.ks[sl], self.vs[sl], self.kp, self.vp, [0, R], o, lse, self.do[sl],
+                             self.dkp if exact else None, self.dvp if exact else None, cfg.scale,
+                             dq=self.dq[:R], dks=self.dks[:R], dvs=self.dvs[:R], workspace=self.ws)
+        if ev:
+            ev[3].record()
+            times.append(ev)
+
+    def step(self, times=None):
+        self.dkp.zero_()
+        self.dvp.zero_()
+        self.loss.zero_()
+        for i in range(self.G):
+            self.response(i, times)
+
+
+def flops(cfg, R):
+    """Algorithmic and executed MFMA flops of one response (per visible pair and query head)."""
+    pairs = R * cfg.P + R * (R + 1) // 2
+    d, dv = cfg.Dqk, cfg.Dv
+    prompt_pairs = R * cfg.P
+    alg = 6 * (d + dv) * pairs * cfg.Hq
+    executed = (2 * (d + dv) * pairs             # forward: S, PV
+                + (2 * d + 2 * dv) * pairs       # dK/dV kernel: S, dP recomputed
+                + 2 * (2 * dv + 2 * d) * prompt_pairs + (2 * dv + 2 * d) * (pairs - prompt_pairs)  # dV, dK (hi/lo on prompt)
+                + (4 * d + 2 * dv) * pairs) * cfg.Hq   # dQ kernel: S, dP, dQ
+    return alg, executed, pairs
+
+
+def cpu_baseline(cfg, rows):
+    """Time the fp64 oracle on a bounded sample: the first `rows` rows of response 0 against the full
+    prompt (an exact sub-problem), for the query heads of kv head 0, forward + backward with
+    prompt-gradient accumulation; scaled to all kv heads (heads are independent). Plus the loss on
+    256 rows of the vocabulary."""
+    from oracle import attn, grpo
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    f64 = inputs.bf16_bits_to_f64
+    g = cfg.Hq // cfg.Hkv
+    Kp = f64(inputs.prompt_k(cfg)[:, :1, :])
+    Vp = f64(inputs.prompt_v(cfg)[:, :1, :])
+    Q = f64(inputs.suffix_q(cfg, 0, rows)[:, :g, :])
+    Ks = f64(inputs.suffix_k(cfg, 0, rows)[:, :1, :])
+    Vs = f64(inputs.suffix_v(cfg, 0, rows)[:, :1, :])
+    dO = f64(inputs.suffix_do(cfg, 0, rows)[:, :g, :])
+    dKp, dVp = np.zeros_like(Kp), np.zeros_like(Vp)
+    t0 = time.time()
+    attn.replay_attn_fwd(Kp, Vp, Q, Ks, Vs, [0, rows], cfg.scale)
+    attn.replay_attn_bwd(Kp, Vp, Q, Ks, Vs, dO, [0, rows], cfg.scale, dKp, dVp)
+    t_attn = time.time() - t0
+    del Kp, Vp, dKp, dVp
+    R = inputs.response_lengths(cfg)
+    n = min(256, int(R[0]))
+    x = f64(inputs.logits(cfg, 0, 0, n))
+    y = inputs.targets(cfg, 0, n)
+    old = grpo.token_logp(x, y) + inputs.old_logp_noise(cfg, 0, n)
+    t0 = time.time()
+    grpo.grpo_token_loss(x, y, old, np.concatenate([[n], R[1:]]), inputs.rewards(cfg), cfg.G, cfg.eps, 0, 1)
+    t_loss = time.time() - t0
+    loss_bytes = n * (4 * cfg.V + 12)
+    return {"value": rows / (t_attn * cfg.Hkv), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, first {rows} rows of response 0 against the full prompt P={cfg.P} "
+                      f"(exact sub-problem), the {g} query heads of kv head 0, forward + backward with prompt-"
+                      f"gradient accumulation: {t_attn:.1f}s, scaled by Hkv={cfg.Hkv}; loss on {n} rows of "
+                      f"V={cfg.V}: {loss_bytes / t_loss / 1e9:.3f} GB/s",
+            "loss_GBps": loss_bytes / t_loss / 1e9}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (the prompt-axis sharding "
+              "design is documented, not built). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from prefix_shared_branch_amd import lsreplay as L
+    L.lib()   # fail loudly if the HIP library is missing
+    cfg = inputs.CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    wl = Workload(cfg)
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    times = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        wl.step(times)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.1f} ms/step (host wall {wall:.1f}s)")
+
+    t_fwd = sum(ev[0].elapsed_time(ev[1]) for ev in times) / args.steps
+    t_loss = sum(ev[1].elapsed_time(ev[2]) for ev in times) / args.steps
+    t_bwd = sum(ev[2].elapsed_time(ev[3]) for ev in times) / args.steps
+    tokens = int(wl.R.sum())
+    alg = exe = 0
+    for r in wl.R:
+        a, e, _ = flops(cfg, int(r))
+        alg += a
+        exe += e
+    loss_bytes = tokens * (4 * cfg.V + 12)
+
+    # dominant kernel: the dK/dV prompt kernel, timed as (exact - response-only) backward per response
+    import statistics
+    dk_ms = []
+    for i in range(min(4, wl.G)):
+        tt = {}
+        for exact in (True, False, True, False):
+            ev = []
+            wl.response(i, ev, exact=exact)
+            torch.cuda.synchronize()
+            tt.setdefault(exact, []).append(ev[0][2].elapsed_time(ev[0][3]))
+        dk_ms.append(min(tt[True]) - min(tt[False]))
+    dkdv_ms = statistics.median(dk_ms)
+    R0 = int(wl.R[0])
+    dkdv_alg = 2 * (cfg.Dqk + cfg.Dv) * R0 * cfg.P * cfg.Hq     # dV and dK products over prompt pairs
+    roof_ach = dkdv_alg / (dkdv_ms * 1e-3) / 1e12
+    fwd_alg = 2 * (cfg.Dqk + cfg.Dv) * flops(cfg, R0)[2] * cfg.Hq
+
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "P": cfg.P, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Dqk": cfg.Dqk, "Dv": cfg.Dv,
+                   "G": cfg.G, "R": [int(r) for r in wl.R] if len(set(wl.R.tolist())) > 1 else int(wl.R[0]),
+                   "vocab": cfg.V, "eps": cfg.eps, "gradient_semantics": "exact-prompt-grad"},
+        "roofline": {"bound": "mfma", "achieved": roof_ach, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                     "frac": roof_ach / (PEAK_BF16 / 1e12), "traffic": None,
+                     "kernel": "replay_bwd_dkdv (prompt keys)", "avg_ms": dkdv_ms},
+        "detail": {
+            "attn_tokens_per_s": tokens / ((t_fwd + t_bwd) * 1e-3),
+            "attn_alg_TFLOPs": alg / ((t_fwd + t_bwd) * 1e-3) / 1e12,
+            "attn_alg_frac_peak": alg / ((t_fwd + t_bwd) * 1e-3) / PEAK_BF16,
+            "attn_exec_TFLOPs": exe / ((t_fwd + t_bwd) * 1e-3) / 1e12,
+            "fwd_ms_per_group": t_fwd, "bwd_ms_per_group": t_bwd, "loss_ms_per_group": t_loss,
+            "fwd_alg_TFLOPs": fwd_alg * wl.G / (t_fwd * 1e-3) / 1e12,
+            "loss_GBps": loss_bytes / (t_loss * 1e-3) / 1e9,
+            "loss_frac_hbm": loss_bytes / (t_loss * 1e-3) / PEAK_HBM,
+            "peak_mem_GiB": torch.cuda.max_memory_allocated() / 2**30,
+            "pages_context": "2.1M token positions on eight H20 GPUs (whole model, end to end; not comparable)",
+        },
+    }
+    if not args.no_cpu_baseline:
+        rows = args.cpu_rows or (256 if cfg.P <= 65536 else 32)
+        del wl
+        torch.cuda.empty_cache()
+        log(f"cpu baseline: oracle on {rows} rows")
+        out["cpu_baseline"] = cpu_baseline(cfg, rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
