@@ -19,6 +19,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", o
 # the packed-fp32 feature stays off: every v_pk_*_f32 is left out of the kernels
 HIP_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-ffp-contract=fast"]
+# Per-source extras. Forward: MFMA accumulators in VGPRs -- the softmax rescale touches them with
+# VALU ops, which cannot address AGPRs, and the default AGPR form copies them back and forth.
+SOURCE_FLAGS = {"replay_attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):
@@ -36,7 +39,8 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     jobs = []
     for s in HIP_SOURCES:
         obj = os.path.join(BUILD, s + ".o")
-        jobs.append([HIPCC, *COMMON, *HIP_FLAGS, *extra, "-c", os.path.join(CSRC, s), "-o", obj])
+        jobs.append([HIPCC, *COMMON, *HIP_FLAGS, *SOURCE_FLAGS.get(s, []), *extra, "-c", os.path.join(CSRC, s),
+                     "-o", obj])
     for s in CXX_SOURCES:
         obj = os.path.join(BUILD, s + ".o")
         jobs.append([HIPCC, *COMMON, *extra, "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-x", "c++", "-c", os.path.join(CSRC, s), "-o", obj])
@@ -52,8 +56,8 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     asm_jobs = []
     for s in HIP_SOURCES:
         asm = os.path.join(BUILD, s + ".s")
-        asm_jobs.append([HIPCC, *COMMON, *HIP_FLAGS, *extra, "-S", "--cuda-device-only", os.path.join(CSRC, s),
-                         "-o", asm])
+        asm_jobs.append([HIPCC, *COMMON, *HIP_FLAGS, *SOURCE_FLAGS.get(s, []), *extra, "-S", "--cuda-device-only",
+                         os.path.join(CSRC, s), "-o", asm])
     with ThreadPoolExecutor(max_workers=min(8, len(asm_jobs))) as ex:
         list(ex.map(_run, asm_jobs))
     for j in asm_jobs:

@@ -18,7 +18,8 @@
 namespace lsr {
 
 namespace {
-constexpr int kQTile = 128;   // packed query rows per forward / dQ workgroup
+constexpr int kQTileFwd = 128;  // packed query rows per forward workgroup (32 per wave)
+constexpr int kQTileDq = 128;   // packed query rows per dQ workgroup
 constexpr int kKTile = 64;    // keys per forward / dQ tile
 constexpr int kDKTile = 128;  // keys per dK/dV workgroup
 constexpr int kTargetBlocks = 2048;
@@ -34,6 +35,7 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
   std::memset(pl, 0, sizeof(*pl));
   const int g = Hq / Hkv;
   const long long T = cu[n_resp];
+  const int kQTile = which == 0 ? kQTileFwd : kQTileDq;
   int qt = 0, kt = 0;
   for (int i = 0; i < n_resp; ++i) {
     pl->tile0[i] = qt;

@@ -81,6 +81,70 @@ __device__ __forceinline__ bf16x8 join_tr(const s16x4& a, const s16x4& b) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// ---- LDS tiles without padding: logical 16-byte chunk c of row r is stored at chunk c ^ swz(r).
+// Conflict-free on gfx950 both for 16-byte row reads (8 lanes on 8 consecutive rows, same chunk)
+// and for ds_read_b64_tr_b16 (4 consecutive rows x 64 contiguous bytes per 32 lanes).
+template <int CH>  // 16-byte chunks per row (power of two)
+__device__ __forceinline__ int swz(int r) {
+  const int f = ((r & 3) << 2) ^ ((r >> 2) & 3) ^ (r & 2);
+  return f & (CH - 1);
+}
+
+// ---- Padded LDS tiles of 64 rows: row r starts at byte 16 * PCH * r (PCH >= CH chunks of 16 B).
+// PCH = CH + 1 makes 16-byte row-wise reads conflict-free (8 lanes on 8 rows hit 8 distinct
+// 16-byte bank groups); PCH = CH + 4 makes ds_read_b64_tr_b16 conflict-free (4 rows x 64 B).
+// Every fragment offset is then a per-lane base plus a compile-time immediate.
+// A 64-row tile is exactly PCH 1 KB direct-load instructions; lanes that fall on a pad chunk
+// reload the row's last real chunk (never read). Rows past nvalid reload row nvalid - 1.
+template <int CH, int PCH>
+__device__ __forceinline__ void dma_tile64(const uint16_t* base, int64_t ld, int nvalid, char* lds, int wv, int lane);
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane i's bytes land at
+// lds_wave_base + 16 i. lds_wave_base must be wave-uniform.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+template <int CH, int PCH>
+__device__ __forceinline__ void dma_tile64(const uint16_t* base, int64_t ld, int nvalid, char* lds, int wv, int lane) {
+  static_assert(PCH >= CH, "pitch");
+  // opaque lane id: the per-lane row/chunk arithmetic is recomputed for every tile (a few ALU ops)
+  // instead of being hoisted out of the tile loop, where it would pin registers for the whole kernel
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+#pragma unroll
+  for (int k = 0; k < (PCH + 3) / 4; ++k) {
+    const int ins = wv + 4 * k;  // wave-uniform
+    if (ins < PCH) {
+      const int q = ins * 64 + ln;
+      int row = q / PCH;
+      int c = q - row * PCH;
+      c = c < CH ? c : CH - 1;
+      row = row < nvalid ? row : nvalid - 1;
+      lds_dma16(base + (int64_t)row * ld + c * 8, lds + ins * 1024);
+    }
+  }
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave still outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ bf16x8 lds_b128_at(const char* base, int byte_off) {
+  return *reinterpret_cast<const LSR_LDS bf16x8*>(reinterpret_cast<uintptr_t>(base + byte_off));
+}
+
+__device__ __forceinline__ s16x4 lds_tr_at(const char* base, int byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<LSR_LDS s16x4*>(reinterpret_cast<uintptr_t>(base + byte_off)));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

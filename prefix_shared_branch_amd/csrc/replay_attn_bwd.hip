@@ -16,6 +16,8 @@
 //                  Suffix tiles: causal, bf16 dKs/dVs stores.
 // replay_bwd_dq    query-tile owner with split-K over the prompt (like the forward);
 //                  recomputes S and dP per key tile; partials summed in fixed order.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -329,23 +331,31 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
 // ------------------------------------------------------------------ dQ (query owner, split-K)
 template <int D, int DV>
 struct DqCfg {
-  static constexpr int BM = 128;
-  static constexpr int BN = 64;
-  static constexpr int NT = 256;
-  static constexpr int KP = D + 8;
-  static constexpr int VPT = DV + 8;
+  static constexpr int BM = 128;              // packed query rows per workgroup (32 per wave)
+  static constexpr int BN = 64;               // keys per tile
+  static constexpr int KCH = D / 8;           // 16-byte chunks per row
+  static constexpr int VCH = DV / 8;
+  static constexpr int KP = KCH + 1;          // padded pitches in chunks (row-wise reads conflict-free)
+  static constexpr int VP = VCH + 1;
+  static constexpr int KROW = KP * 16;        // LDS bytes per row
+  static constexpr int VROW = VP * 16;
+  static constexpr int KBYTES = BN * KROW;
+  static constexpr int VBYTES = BN * VROW;
   static constexpr int KS = D / 16;
   static constexpr int VS = DV / 16;
   static constexpr int DB = D / 32;
-  static constexpr int KCH = BN * D / 8 / NT;
-  static constexpr int VCH = BN * DV / 8 / NT;
 };
 
+// Two workgroups per CU (68 KB of LDS each, <= 256 registers per wave) so that the two waves on a
+// SIMD hide each other's LDS and softmax latency. K and V tiles stream global -> LDS by DMA into
+// padded rows; K is read both row-wise (S^T = K Q^T) and transposed (dQ^T = K^T dS^T).
 template <int D, int DV>
-__global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void replay_bwd_dq(BwdArgs a) {
   using C = DqCfg<D, DV>;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][C::BN * C::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][C::BN * C::VPT];
+  __shared__ __attribute__((aligned(1024))) char sK0[C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[C::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[C::VBYTES];
 
   const AttnGeom& G = a.geo;
   const int W = a.qtiles * G.Hkv * a.splits;
@@ -367,7 +377,8 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int hl = lane >> 5;
-  const int mrow = m0 + wv * 32 + (lane & 31);
+  const int l32 = lane & 31;
+  const int mrow = m0 + wv * 32 + l32;
   const bool rvalid = mrow < M;
   const int trow = rvalid ? mrow / g : 0;
   const int hq = kvh * g + (rvalid ? mrow - trow * g : 0);
@@ -385,6 +396,13 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
   const float lrow = rvalid ? a.lse[(int64_t)hq * G.T + tok] * kLog2e : INFINITY;
   const float drow = rvalid ? a.delta[(int64_t)hq * G.T + tok] : 0.0f;
 
+  // lane-constant LDS byte offsets; row-wise reads of K and V share one table (same row length)
+  // per-lane LDS bases; every fragment adds a compile-time immediate
+  const int rbk = l32 * C::KROW + hl * 16;   // row-wise reads of K (key l32, 8 dims at 16ks + 8hl)
+  const int rbv = l32 * C::VROW + hl * 16;   // row-wise reads of V
+  // transposed reads of K: row 4hl + jj/4 (+ 8 sec + 16 hs + 32 kb), column 16 (lane/16 % 2) + 4 (jj % 4) (+ 32 b)
+  const int tbk = (4 * hl + ((lane & 15) >> 2)) * C::KROW + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+
   const int pt0 = sp * a.ptiles_per_split;
   const int np = max(0, min(a.ptiles, pt0 + a.ptiles_per_split) - pt0);
   const int t_lo = m0 / g;
@@ -392,7 +410,6 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
   const int ns = (sp == a.splits - 1) ? (t_hi / C::BN + 1) : 0;
   const int nit = np + ns;
 
-  u32x4 kreg[C::KCH], vreg[C::VCH];
   auto tile_info = [&](int it, const uint16_t*& kb, const uint16_t*& vb, int& key0, int& nvalid, bool& sfx) {
     if (it < np) {
       key0 = (pt0 + it) * C::BN;
@@ -408,92 +425,109 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
       sfx = true;
     }
   };
-  auto load_tile = [&](int it) {
+  auto issue_tile = [&](int it, char* kdst, char* vdst) {
     const uint16_t *kb, *vb;
     int key0, nvalid;
     bool sfx;
     tile_info(it, kb, vb, key0, nvalid, sfx);
-#pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      const int c = threadIdx.x + u * C::NT;
-      const int row = c / (D / 8), col = c % (D / 8);
-      kreg[u] = row < nvalid ? *reinterpret_cast<const u32x4*>(kb + (int64_t)row * G.ldk + col * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < C::VCH; ++u) {
-      const int c = threadIdx.x + u * C::NT;
-      const int row = c / (DV / 8), col = c % (DV / 8);
-      vreg[u] = row < nvalid ? *reinterpret_cast<const u32x4*>(vb + (int64_t)row * G.ldv + col * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      const int c = threadIdx.x + u * C::NT;
-      *reinterpret_cast<u32x4*>(&sK[buf][(c / (D / 8)) * C::KP + (c % (D / 8)) * 8]) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < C::VCH; ++u) {
-      const int c = threadIdx.x + u * C::NT;
-      *reinterpret_cast<u32x4*>(&sV[buf][(c / (DV / 8)) * C::VPT + (c % (DV / 8)) * 8]) = vreg[u];
-    }
+    dma_tile64<C::KCH, C::KP>(kb, G.ldk, nvalid, kdst, wv, lane);
+    dma_tile64<C::VCH, C::VP>(vb, G.ldv, nvalid, vdst, wv, lane);
   };
 
   f32x16 dq[C::DB];
 #pragma unroll
   for (int b = 0; b < C::DB; ++b) dq[b] = f32x16{};
   const float c2 = G.scale_log2;
-  const int jj = lane & 15;
-  const int n0l = 16 * ((lane >> 4) & 1) + 4 * (jj & 3);
 
-  if (nit > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < nit; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < nit) load_tile(it + 1);
-    const uint16_t *kbp, *vbp;
-    int key0, nvalid;
-    bool sfx;
-    tile_info(it, kbp, vbp, key0, nvalid, sfx);
-    const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
-    const bool need_mask = causal || nvalid < C::BN;
+  // MASK is a compile-time flag: only ragged prompt tiles and the response's diagonal tiles take
+  // the masked body; everywhere else the softmax has no per-element conditions at all
+  auto compute_body = [&](auto mask_tag, const char* kbuf, const char* vbuf, int key0, int nvalid, bool causal) {
+    constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // Fragments stream in groups of four: each group's LDS reads are in flight while the
+      // previous group's MFMAs run, so at most two groups (32 registers) are live at once.
       // S^T[key][row] = K Q^T, dP^T = V dO^T: lane holds row (lane & 31), keys 8(r/4) + 4hl + r%4
+      constexpr int NG = C::KS / 2;  // fragments per group; equals the number of 32-wide dQ blocks
+      static_assert(C::KS == C::VS && NG == C::DB, "grouping assumes Dqk == Dv");
+      const char* kr = kbuf + kb * 32 * C::KROW;
+      const char* vr = vbuf + kb * 32 * C::VROW;
+      bf16x8 g0[NG], g1[NG];
+#pragma unroll
+      for (int i = 0; i < NG; ++i) g0[i] = lds_b128_at(kr + i * 32, rbk);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NG; ++i) g1[i] = lds_b128_at(kr + (NG + i) * 32, rbk);
       f32x16 s = f32x16{}, dp = f32x16{};
-      const uint16_t* kr = &sK[buf][(kb * 32 + (lane & 31)) * C::KP + hl * 8];
-      const uint16_t* vr = &sV[buf][(kb * 32 + (lane & 31)) * C::VPT + hl * 8];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) s = mfma32(lds_read_b128(kr + ks * 16), qf[ks], s);
+      for (int i = 0; i < NG; ++i) s = mfma32(g0[i], qf[i], s);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < C::VS; ++ks) dp = mfma32(lds_read_b128(vr + ks * 16), of[ks], dp);
+      for (int i = 0; i < NG; ++i) g0[i] = lds_b128_at(vr + i * 32, rbv);
+#pragma unroll
+      for (int i = 0; i < NG; ++i) s = mfma32(g1[i], qf[NG + i], s);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NG; ++i) g1[i] = lds_b128_at(vr + (NG + i) * 32, rbv);
+#pragma unroll
+      for (int i = 0; i < NG; ++i) dp = mfma32(g0[i], of[i], dp);
+      __builtin_amdgcn_sched_barrier(0);
+      // transposed K fragments (first half of the keys) in flight while dS is formed
+      auto tr_frags = [&](int hs, bf16x8* tf) {
+        const char* kt = kbuf + (kb * 32 + 16 * hs) * C::KROW;
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b)
+          tf[b] = join_tr(lds_tr_at(kt + b * 64, tbk), lds_tr_at(kt + 8 * C::KROW + b * 64, tbk));
+      };
+      tr_frags(0, g0);
+#pragma unroll
+      for (int i = 0; i < NG; ++i) dp = mfma32(g1[i], of[NG + i], dp);
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
         float pv = fast_exp2(__builtin_fmaf(s[r], c2, -lrow));
-        if (need_mask && (key >= nvalid || (causal && key0 + key > trow))) pv = 0.0f;
+        if constexpr (MASK) pv = (key >= nvalid || (causal && key0 + key > trow)) ? 0.0f : pv;
         ds[r] = pv * (dp[r] - drow);
       }
-      // dQ^T[d][row] += K^T dS^T
+      // dQ^T[d][row] += K^T dS^T (second half's fragments load under the first half's MFMAs)
+      tr_frags(1, g1);
+      {
+        const bf16x8 db = c_regs_to_bf16x8(ds, 0);
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        const bf16x8 db = c_regs_to_bf16x8(ds, 8 * hs);
-        const uint16_t* ktr = &sK[buf][(kb * 32 + 16 * hs + 4 * hl + (jj >> 2)) * C::KP + n0l];
-#pragma unroll
-        for (int b = 0; b < C::DB; ++b) {
-          const bf16x8 at = join_tr(lds_read_tr(ktr + b * 32), lds_read_tr(ktr + b * 32 + 8 * C::KP));
-          dq[b] = mfma32(at, db, dq[b]);
-        }
+        for (int b = 0; b < C::DB; ++b) dq[b] = mfma32(g0[b], db, dq[b]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const bf16x8 db = c_regs_to_bf16x8(ds, 8);
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b) dq[b] = mfma32(g1[b], db, dq[b]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (it + 1 < nit) store_tile(buf ^ 1);
+  };
+  auto compute = [&](int it, const char* kbuf, const char* vbuf) {
+    const uint16_t *kbp, *vbp;
+    int key0, nvalid;
+    bool sfx;
+    tile_info(it, kbp, vbp, key0, nvalid, sfx);
+    const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
+    if (causal || nvalid < C::BN) compute_body(std::true_type{}, kbuf, vbuf, key0, nvalid, causal);
+    else compute_body(std::false_type{}, kbuf, vbuf, key0, nvalid, causal);
+  };
+
+  if (nit > 0) issue_tile(0, sK0, sV0);
+  for (int it = 0; it < nit; it += 2) {
+    wait_vmem();
     __syncthreads();
+    if (it + 1 < nit) issue_tile(it + 1, sK1, sV1);
+    compute(it, sK0, sV0);
+    if (it + 1 >= nit) break;
+    wait_vmem();
+    __syncthreads();
+    if (it + 2 < nit) issue_tile(it + 2, sK0, sV0);
+    compute(it + 1, sK1, sV1);
   }
 
   if (!rvalid) return;

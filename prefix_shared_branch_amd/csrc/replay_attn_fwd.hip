@@ -2,12 +2,14 @@
 // the queries of one response attend to all prompt keys and, causally, to the response's
 // own keys.
 //
-// replay_fwd: one workgroup = 4 waves = 128 GQA-packed query rows of one kv head, over the
-// prompt key tiles of one split (plus, in the last split, the response's causal key tiles).
-// Per 64-key tile:  K, V tiles are staged global -> VGPR -> LDS (double-buffered, padded
-// rows); each wave computes S^T = K Q^T (MFMA 32x32x16 bf16, Q fragments held in VGPRs,
-// K read from LDS), an online softmax whose row statistics are lane-local (one query row
-// per lane), and O^T += V^T P^T with V^T fetched by LDS transpose reads.
+// replay_fwd: one workgroup = 4 waves x 64 = 256 GQA-packed query rows of one kv head, over
+// the prompt key tiles of one split (plus, in the last split, the response's causal key
+// tiles). 64-key K and V tiles stream global -> LDS by direct DMA (double-buffered, XOR-
+// swizzled rows without padding). Per 32-key block each wave computes S^T = K Q^T for its two
+// 32-row blocks (MFMA 32x32x16 bf16, Q fragments held in VGPRs, every K fragment read from LDS
+// feeds two MFMAs), an online softmax whose row statistics are lane-local (one query row per
+// lane; the O rescale is skipped when no row maximum moved), and O^T += V^T P^T with V^T
+// fetched by LDS transpose reads, again shared by both row blocks.
 // Workgroup ids are mapped so that each XCD owns a contiguous run of (kv head, split)
 // streams: concurrently resident query tiles sweep the same prompt K/V tiles, which are
 // then fetched from HBM once per XCD and served to its CUs from L2.
@@ -21,28 +23,36 @@ namespace lsr {
 
 namespace {
 
+// Query rows per wave: 32 * RB. RB = 1 keeps two waves per SIMD resident (latency of one wave's
+// softmax and LDS reads hidden behind the other's MFMAs); RB = 2 shares each LDS fragment between
+// two MFMAs but leaves one wave per SIMD.
+constexpr int kFwdRowBlocks = 1;
+
 template <int D, int DV>
 struct FwdCfg {
-  static constexpr int BM = 128;         // packed query rows per workgroup
-  static constexpr int BN = 64;          // keys per tile
-  static constexpr int NT = 256;
-  static constexpr int KP = D + 8;       // LDS row pitch (elements) of the K tile
-  static constexpr int VPT = DV + 8;     // LDS row pitch of the V tile
-  static constexpr int KS = D / 16;      // MFMA k-steps over the head dim
-  static constexpr int NB = DV / 32;     // 32-wide blocks of the value dim
-  static constexpr int KCH = BN * D / 8 / NT;
-  static constexpr int VCH = BN * DV / 8 / NT;
+  static constexpr int RB = kFwdRowBlocks;
+  static constexpr int BM = 128 * RB;         // packed query rows per workgroup
+  static constexpr int BN = 64;               // keys per tile
+  static constexpr int KCH = D / 8;           // 16-byte chunks per K row
+  static constexpr int VCH = DV / 8;
+  static constexpr int KROW = D * 2;          // bytes per K row in LDS
+  static constexpr int VROW = DV * 2;
+  static constexpr int KBYTES = BN * KROW;
+  static constexpr int VBYTES = BN * VROW;
+  static constexpr int KINS = KBYTES / 1024 / 4;  // 1 KB direct-load instructions per wave per K tile
+  static constexpr int VINS = VBYTES / 1024 / 4;
+  static constexpr int KS = D / 16;           // MFMA k-steps over the head dim
+  static constexpr int NB = DV / 32;          // 32-wide blocks of the value dim
 };
 
-__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
 template <int D, int DV>
-__global__ __launch_bounds__(256, 2) void replay_fwd(FwdArgs a) {
+__global__ __launch_bounds__(256, kFwdRowBlocks == 1 ? 2 : 1) void replay_fwd(FwdArgs a) {
   using C = FwdCfg<D, DV>;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][C::BN * C::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][C::BN * C::VPT];
+  // two pipeline stages (64 KB at D = 128, so two workgroups fit in a CU's LDS)
+  __shared__ __attribute__((aligned(1024))) char sK0[C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[C::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[C::VBYTES];
 
   const AttnGeom& G = a.geo;
   const int W = a.qtiles * G.Hkv * a.splits;
@@ -64,18 +74,45 @@ __global__ __launch_bounds__(256, 2) void replay_fwd(FwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int hl = lane >> 5;
-  const int mrow = m0 + wv * 32 + (lane & 31);
-  const bool rvalid = mrow < M;
-  const int trow = rvalid ? mrow / g : 0;
-  const int hq = kvh * g + (rvalid ? mrow - trow * g : 0);
+  const int l32 = lane & 31;
 
-  bf16x8 qf[C::KS];
-  {
-    const uint16_t* qrow = G.Q + ((int64_t)(tokb + trow) * G.Hq + hq) * D + hl * 8;
+  // two 32-row blocks per wave; one query row per lane in each
+  bool rvalid[C::RB];
+  int trow[C::RB], hq[C::RB];
+  bf16x8 qf[C::RB][C::KS];
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb) {
+    const int mrow = m0 + wv * 32 * C::RB + rb * 32 + l32;
+    rvalid[rb] = mrow < M;
+    trow[rb] = rvalid[rb] ? mrow / g : 0;
+    hq[rb] = kvh * g + (rvalid[rb] ? mrow - trow[rb] * g : 0);
+    const uint16_t* qrow = G.Q + ((int64_t)(tokb + trow[rb]) * G.Hq + hq[rb]) * D + hl * 8;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      if (rvalid) qf[ks] = ld_bf16x8(qrow + ks * 16);
-      else qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      if (rvalid[rb]) qf[rb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + ks * 16));
+      else qf[rb][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      // with one wave per SIMD, Q fragments (only ever MFMA operands) live in AGPRs, leaving
+      // VGPRs for the accumulators and prefetched LDS fragments; at two waves per SIMD the
+      // register file is split evenly and they stay in VGPRs
+      if constexpr (C::RB == 2) asm volatile("" : "+a"(qf[rb][ks]));
+    }
+  }
+
+  // lane-constant LDS byte offsets (the tile base and the 32-key block offset are added as immediates)
+  int koff[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = l32 * C::KROW + (((2 * ks + hl) ^ swz<C::KCH>(l32)) << 4);
+  int voff[2][C::NB];
+  {
+    const int jj = lane & 15;
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int row = 4 * hl + (jj >> 2) + 8 * sec;  // row within the 16-row group (mod 16)
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) {
+        const int chunk = nb * 4 + 2 * ((lane >> 4) & 1) + ((jj & 3) >> 1);
+        voff[sec][nb] = row * C::VROW + ((chunk ^ swz<C::VCH>(row)) << 4) + (jj & 1) * 8;
+      }
     }
   }
 
@@ -87,7 +124,6 @@ __global__ __launch_bounds__(256, 2) void replay_fwd(FwdArgs a) {
   const int ns = (sp == a.splits - 1) ? (t_hi / C::BN + 1) : 0;
   const int nit = np + ns;
 
-  u32x4 kreg[C::KCH], vreg[C::VCH];
   auto tile_info = [&](int it, const uint16_t*& kb, const uint16_t*& vb, int& key0, int& nvalid, bool& sfx) {
     if (it < np) {
       key0 = (pt0 + it) * C::BN;
@@ -103,149 +139,178 @@ __global__ __launch_bounds__(256, 2) void replay_fwd(FwdArgs a) {
       sfx = true;
     }
   };
-  auto load_tile = [&](int it) {
+  // global -> LDS: each 1 KB instruction fills 1024 / (row bytes) consecutive rows; rows past the
+  // valid keys re-read the last valid row (finite data, masked out of the softmax)
+  auto issue_tile = [&](int it, char* kdst, char* vdst) {
     const uint16_t *kb, *vb;
     int key0, nvalid;
     bool sfx;
     tile_info(it, kb, vb, key0, nvalid, sfx);
 #pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      const int c = threadIdx.x + u * C::NT;
-      const int row = c / (D / 8), col = c % (D / 8);
-      kreg[u] = row < nvalid ? *reinterpret_cast<const u32x4*>(kb + (int64_t)row * G.ldk + col * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < C::KINS; ++u) {
+      const int ins = wv * C::KINS + u;
+      const int row = ins * (64 / C::KCH) + lane / C::KCH;
+      const int c = (lane % C::KCH) ^ swz<C::KCH>(row);
+      lds_dma16(kb + (int64_t)min(row, nvalid - 1) * G.ldk + c * 8, kdst + ins * 1024);
     }
 #pragma unroll
-    for (int u = 0; u < C::VCH; ++u) {
-      const int c = threadIdx.x + u * C::NT;
-      const int row = c / (DV / 8), col = c % (DV / 8);
-      vreg[u] = row < nvalid ? *reinterpret_cast<const u32x4*>(vb + (int64_t)row * G.ldv + col * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      const int c = threadIdx.x + u * C::NT;
-      const int row = c / (D / 8), col = c % (D / 8);
-      *reinterpret_cast<u32x4*>(&sK[buf][row * C::KP + col * 8]) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < C::VCH; ++u) {
-      const int c = threadIdx.x + u * C::NT;
-      const int row = c / (DV / 8), col = c % (DV / 8);
-      *reinterpret_cast<u32x4*>(&sV[buf][row * C::VPT + col * 8]) = vreg[u];
+    for (int u = 0; u < C::VINS; ++u) {
+      const int ins = wv * C::VINS + u;
+      const int row = ins * (64 / C::VCH) + lane / C::VCH;
+      const int c = (lane % C::VCH) ^ swz<C::VCH>(row);
+      lds_dma16(vb + (int64_t)min(row, nvalid - 1) * G.ldv + c * 8, vdst + ins * 1024);
     }
   };
 
-  f32x16 o[C::NB];
+  f32x16 o[C::RB][C::NB];
+  float m_run[C::RB], l_run[C::RB];
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) o[nb] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  for (int rb = 0; rb < C::RB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) o[rb][nb] = f32x16{};
+  }
   const float c2 = G.scale_log2;
 
-  if (nit > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < nit; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < nit) load_tile(it + 1);
+  // only ragged prompt tiles and the response's diagonal tiles take the (wave-uniform) mask branch
+  auto compute = [&](int it, const char* kbuf, const char* vbuf) {
     const uint16_t *kbp, *vbp;
     int key0, nvalid;
     bool sfx;
     tile_info(it, kbp, vbp, key0, nvalid, sfx);
     const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
-    const bool need_mask = causal || nvalid < C::BN;
+    const bool masked = causal || nvalid < C::BN;
 
-    f32x16 st[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      st[kb] = f32x16{};
-      const uint16_t* kr = &sK[buf][(kb * 32 + (lane & 31)) * C::KP + hl * 8];
+      f32x16 st[C::RB];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) st[kb] = mfma32(lds_read_b128(kr + ks * 16), qf[ks], st[kb]);
-    }
-    if (need_mask) {
+      for (int rb = 0; rb < C::RB; ++rb) st[rb] = f32x16{};
+      bf16x8 vf[2][C::NB];
+      if constexpr (C::RB == 2) {
+        // one wave per SIMD: issue all K fragments of this 32-key block at once, then the
+        // S^T = K Q^T MFMAs, then all V^T fragments (transposed LDS reads) so they are in flight
+        // while the softmax runs
+        bf16x8 kf[C::KS];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int ks = 0; ks < C::KS; ++ks) kf[ks] = lds_b128_at(kbuf, kb * 32 * C::KROW + koff[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+          for (int rb = 0; rb < C::RB; ++rb) st[rb] = mfma32(kf[ks], qf[rb][ks], st[rb]);
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const int rowbase = (kb * 32 + 16 * hs) * C::VROW;
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+            vf[hs][nb] = join_tr(lds_tr_at(vbuf, rowbase + voff[0][nb]), lds_tr_at(vbuf, rowbase + voff[1][nb]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // two waves per SIMD hide each other's latencies: plain per-fragment order
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) st[0] = mfma32(lds_b128_at(kbuf, kb * 32 * C::KROW + koff[ks]), qf[0][ks], st[0]);
+      }
+      if (masked) {
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const bool bad = key >= nvalid || (causal && key0 + key > trow[rb]);
+            st[rb][r] = bad ? -INFINITY : st[rb][r];
+          }
+      }
+      // stage 4: online softmax, one row per lane (the other half-wave holds the row's other keys)
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[rb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run[rb], mx);
+        const float ms = (m_new == -INFINITY ? 0.0f : m_new) * c2;
+        const float alpha = fast_exp2(m_run[rb] * c2 - ms);
+        m_run[rb] = m_new;
+        if (__any(alpha != 1.0f)) {
+          l_run[rb] *= alpha;
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb) o[rb][nb] *= alpha;
+        }
+        float ls = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const bool bad = key >= nvalid || (causal && key0 + key > trow);
-          if (bad) st[kb][r] = -INFINITY;
+          const float p = fast_exp2(__builtin_fmaf(st[rb][r], c2, -ms));
+          st[rb][r] = p;
+          ls += p;
         }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float ms = (m_new == -INFINITY ? 0.0f : m_new) * c2;
-    const float alpha = fast_exp2(m_run * c2 - ms);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) o[nb] *= alpha;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(__builtin_fmaf(st[kb][r], c2, -ms));
-        st[kb][r] = p;
-        l_run += p;
+        l_run[rb] += ls;
       }
-    // O^T += V^T P^T
-    const int jj = lane & 15;
-    const int n0l = 16 * ((lane >> 4) & 1) + 4 * (jj & 3);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      // stage 5: O^T += V^T P^T; each V^T fragment feeds two MFMAs
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
-        const bf16x8 pb = c_regs_to_bf16x8(st[kb], 8 * hs);
-        const int k0 = kb * 32 + 16 * hs + 4 * hl + (jj >> 2);
-        const uint16_t* vr = &sV[buf][k0 * C::VPT + n0l];
+        bf16x8 pb[C::RB];
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) pb[rb] = c_regs_to_bf16x8(st[rb], 8 * hs);
+        const int rowbase = (kb * 32 + 16 * hs) * C::VROW;
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
-          const s16x4 t0 = lds_read_tr(vr + nb * 32);
-          const s16x4 t1 = lds_read_tr(vr + nb * 32 + 8 * C::VPT);
-          o[nb] = mfma32(join_tr(t0, t1), pb, o[nb]);
+          const bf16x8 va = C::RB == 2 ? vf[hs][nb]
+                                       : join_tr(lds_tr_at(vbuf, rowbase + voff[0][nb]), lds_tr_at(vbuf, rowbase + voff[1][nb]));
+#pragma unroll
+          for (int rb = 0; rb < C::RB; ++rb) o[rb][nb] = mfma32(va, pb[rb], o[rb][nb]);
         }
       }
-    if (it + 1 < nit) store_tile(buf ^ 1);
+    }
+  };
+
+  // tile it+1 streams into the other stage while tile it is computed; the barrier after the
+  // wait makes every wave's part of tile it visible and retires all reads of the stage refilled next
+  if (nit > 0) issue_tile(0, sK0, sV0);
+  for (int it = 0; it < nit; it += 2) {
+    wait_vmem();
     __syncthreads();
+    if (it + 1 < nit) issue_tile(it + 1, sK1, sV1);
+    compute(it, sK0, sV0);
+    if (it + 1 >= nit) break;
+    wait_vmem();
+    __syncthreads();
+    if (it + 2 < nit) issue_tile(it + 2, sK0, sV0);
+    compute(it + 1, sK1, sV1);
   }
 
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (!rvalid) return;
-  const int64_t tok = tokb + trow;
-  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-  const float lse = l_run > 0.0f ? m_run * G.scale + fast_log2(l_run) * kLn2 : -INFINITY;
-  if (a.splits == 1) {
-    uint16_t* orow = a.O + (tok * G.Hq + hq) * DV + 4 * hl;
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
+  for (int rb = 0; rb < C::RB; ++rb) {
+    const float l = l_run[rb] + __shfl_xor(l_run[rb], 32, 64);
+    if (!rvalid[rb]) continue;
+    const int64_t tok = tokb + trow[rb];
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float lse = l > 0.0f ? m_run[rb] * G.scale + fast_log2(l) * kLn2 : -INFINITY;
+    if (a.splits == 1) {
+      uint16_t* orow = a.O + (tok * G.Hq + hq[rb]) * DV + 4 * hl;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x2 v = {pack_bf16x2(o[nb][4 * q] * inv, o[nb][4 * q + 1] * inv),
-                         pack_bf16x2(o[nb][4 * q + 2] * inv, o[nb][4 * q + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + nb * 32 + 8 * q) = v;
-      }
-    if (hl == 0) a.lse[(int64_t)hq * G.T + tok] = lse;
-  } else {
-    float* orow = a.o_part + (((int64_t)sp * G.T + tok) * G.Hq + hq) * DV + 4 * hl;
+      for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
+        for (int q = 0; q < 4; ++q) {
+          const u32x2 v = {pack_bf16x2(o[rb][nb][4 * q] * inv, o[rb][nb][4 * q + 1] * inv),
+                           pack_bf16x2(o[rb][nb][4 * q + 2] * inv, o[rb][nb][4 * q + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + nb * 32 + 8 * q) = v;
+        }
+      if (hl == 0) a.lse[(int64_t)hq[rb] * G.T + tok] = lse;
+    } else {
+      float* orow = a.o_part + (((int64_t)sp * G.T + tok) * G.Hq + hq[rb]) * DV + 4 * hl;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = {o[nb][4 * q] * inv, o[nb][4 * q + 1] * inv, o[nb][4 * q + 2] * inv,
-                         o[nb][4 * q + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + nb * 32 + 8 * q) = v;
-      }
-    if (hl == 0) a.lse_part[((int64_t)sp * G.Hq + hq) * G.T + tok] = lse;
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {o[rb][nb][4 * q] * inv, o[rb][nb][4 * q + 1] * inv, o[rb][nb][4 * q + 2] * inv,
+                           o[rb][nb][4 * q + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + nb * 32 + 8 * q) = v;
+        }
+      if (hl == 0) a.lse_part[((int64_t)sp * G.Hq + hq[rb]) * G.T + tok] = lse;
+    }
   }
 }
 

@@ -23,16 +23,58 @@ def _regs(spec: str) -> set[int]:
     return {int(m.group(1))} if m else set()
 
 
-def _instructions(lines):
+def _parse(lines):
+    """Instructions as (line number, text) plus a map from label to the index of the next instruction."""
+    insts, labels = [], {}
     for n, raw in enumerate(lines):
         s = raw.split(";")[0].strip()
-        if not s or s.startswith(".") or s.endswith(":"):
+        if not s or s.startswith("."):
+            if s.startswith(".LBB") and s.endswith(":"):
+                labels[s[:-1]] = len(insts)
             continue
-        yield n, s
+        if s.endswith(":"):
+            labels[s[:-1]] = len(insts)
+            continue
+        insts.append((n, s))
+    return insts, labels
+
+
+def _hazard_after(insts, labels, k, data, waits, seen):
+    """Follow every control path from instruction k on until _WAIT_STATES wait states have passed."""
+    while k < len(insts) and waits < _WAIT_STATES:
+        if (k, waits) in seen:
+            return None
+        seen.add((k, waits))
+        n2, s2 = insts[k]
+        op = s2.split()[0]
+        if op == "s_endpgm":
+            return None
+        if op == "s_nop":
+            waits += int(s2.split()[1], 0) + 1
+            k += 1
+            continue
+        if op.startswith("s_branch") or op.startswith("s_cbranch"):
+            target = s2.split()[1]
+            if target in labels:
+                hit = _hazard_after(insts, labels, labels[target], data, waits + 1, seen)
+                if hit:
+                    return hit
+            if op.startswith("s_branch"):
+                return None
+            waits += 1
+            k += 1
+            continue
+        if op.startswith("v_") and not op.startswith(("v_cmp", "v_readlane", "v_readfirstlane")):
+            dst = s2.split(None, 1)[1].split(",")[0]
+            if _regs(dst) & data:
+                return f"'{s2}' (line {n2 + 1}) after {waits} wait state(s)"
+        waits += 1
+        k += 1
+    return None
 
 
 def scan(asm_text: str) -> list[str]:
-    insts = list(_instructions(asm_text.splitlines()))
+    insts, labels = _parse(asm_text.splitlines())
     problems = []
     for k, (n, s) in enumerate(insts):
         m = _STORE.match(s)
@@ -40,18 +82,7 @@ def scan(asm_text: str) -> list[str]:
             continue
         ops = [o.strip() for o in m.group(2).split(",")]
         data = _regs(ops[0] if m.group(1).startswith("buffer") else ops[1])
-        waits = 0
-        for n2, s2 in insts[k + 1:]:
-            if waits >= _WAIT_STATES:
-                break
-            op = s2.split()[0]
-            if op == "s_nop":
-                waits += int(s2.split()[1], 0) + 1
-                continue
-            if op.startswith("v_") and not op.startswith(("v_cmp", "v_readlane", "v_readfirstlane")):
-                dst = s2.split(None, 1)[1].split(",")[0]
-                if _regs(dst) & data:
-                    problems.append(f"line {n + 1}: '{s}' then '{s2}' after {waits} wait state(s)")
-                    break
-            waits += 1
+        hit = _hazard_after(insts, labels, k + 1, data, 0, set())
+        if hit:
+            problems.append(f"line {n + 1}: '{s}' then {hit}")
     return problems
