@@ -15,7 +15,9 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call only
  *    enqueues work on that stream and returns; it never synchronises.
  *  - Pointers marked "device" are caller-owned device allocations; pointers marked "host"
- *    are read during the call only. The library allocates nothing and keeps no state.
+ *    are read during the call only. The computing entry points allocate no device memory and
+ *    keep no state (the optional kernel timer at the end of this header keeps host-side
+ *    events while armed).
  *  - bf16 is IEEE bfloat16 stored as 16-bit words; fp32 is IEEE binary32.
  *  - All argument checks run on the host before any HIP call; a failed check returns an
  *    error code and touches no memory. A HIP launch/runtime error returns LS_ERR_HIP.
@@ -152,6 +154,26 @@ int ls_grpo_token_loss(void* stream, int32_t V, int32_t G,
 
 /* Static string naming a status code. */
 const char* ls_status_string(int status);
+
+/* Kernel timer -- instrumentation for benchmarks, not part of the replay computation.
+ * ls_kernel_timer_start arms the timer for one kernel and clears earlier records; from then on
+ * every launch of that kernel by the entry points above is bracketed by two HIP events recorded
+ * on the caller's stream (the events are created by the library on first use and kept for reuse).
+ * ls_kernel_timer_stop disarms it, waits for the recorded events and writes the summed device
+ * time in milliseconds and the number of launches. At most 65536 launches are recorded per
+ * arming (more: stop returns LS_ERR_HIP). Errors: an unknown kernel id, NULL outputs or stop
+ * without start give LS_ERR_INVALID_ARG; a failed event call gives LS_ERR_HIP. The timer is
+ * process-wide and guarded by a mutex; timing calls on several streams at once is allowed but
+ * sums their overlapping durations. */
+typedef enum {
+  LS_KERNEL_ATTN_FWD = 0,     /* replay attention forward main kernel (split partials)      */
+  LS_KERNEL_DKDV_PROMPT = 1,  /* backward dK/dV over the prompt keys (exact mode only)       */
+  LS_KERNEL_DQ = 2,           /* backward dQ (split over the prompt keys)                    */
+  LS_KERNEL_GRPO_ROWS = 3     /* per-row pass of the GRPO token loss                         */
+} ls_kernel_id;
+
+int ls_kernel_timer_start(int32_t kernel);
+int ls_kernel_timer_stop(float* total_ms, int32_t* launches);
 
 #ifdef __cplusplus
 }

@@ -182,6 +182,7 @@ size_t grpo_workspace_bytes(int64_t T) { return (size_t)((T * 4 + 255) / 256 * 2
 
 hipError_t launch_grpo(const GrpoArgs& a, bool vec, hipStream_t st) {
   hipError_t e = hipSuccess;
+  timer_mark(LS_KERNEL_GRPO_ROWS, st, false);
   if (vec) {
     const int nch = a.V / 8;
     if (nch <= 256) e = go_vec<256, 1>(a, st);
@@ -198,6 +199,7 @@ hipError_t launch_grpo(const GrpoArgs& a, bool vec, hipStream_t st) {
     hipLaunchKernelGGL(grpo_rows_scalar, dim3((unsigned)a.T), dim3(256), 0, st, a);
     e = hipGetLastError();
   }
+  timer_mark(LS_KERNEL_GRPO_ROWS, st, true);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(grpo_sum, dim3(1), dim3(256), 0, st, (const float*)a.row_loss, a.T, a.loss_accum);
   return hipGetLastError();

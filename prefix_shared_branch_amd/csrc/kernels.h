@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/ls_replay.h"
+
 namespace lsr {
 
 constexpr int kMaxResp = 64;
@@ -95,5 +97,9 @@ struct AttnPlan {
 bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, const int32_t* cu, AttnPlan* plan);
 hipError_t launch_attn_fwd(FwdArgs& a, int Dqk, int Dv, hipStream_t st);
 hipError_t launch_attn_bwd(BwdArgs& a, int Dqk, int Dv, hipStream_t st);
+
+// Kernel timer hooks (timer.cpp): bracket a launch; no-ops unless the timer is armed for `kernel`
+// (an ls_kernel_id value).
+void timer_mark(int kernel, hipStream_t st, bool end);
 
 }  // namespace lsr

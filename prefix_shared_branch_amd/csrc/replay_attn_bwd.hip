@@ -579,7 +579,9 @@ hipError_t bwd_go(BwdArgs& a, hipStream_t st) {
   }
   if (a.ktiles_prompt > 0) {
     const long long W = (long long)a.ktiles_prompt * G.Hkv;
+    timer_mark(LS_KERNEL_DKDV_PROMPT, st, false);
     hipLaunchKernelGGL((replay_bwd_dkdv<D, DV, true>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(256), 0, st, a);
+    timer_mark(LS_KERNEL_DKDV_PROMPT, st, true);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {
@@ -592,7 +594,9 @@ hipError_t bwd_go(BwdArgs& a, hipStream_t st) {
   {
     const long long W = (long long)a.qtiles * G.Hkv * a.splits;
     if (W > 0) {
+      timer_mark(LS_KERNEL_DQ, st, false);
       hipLaunchKernelGGL((replay_bwd_dq<D, DV>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(256), 0, st, a);
+      timer_mark(LS_KERNEL_DQ, st, true);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }

@@ -346,7 +346,9 @@ hipError_t fwd_go(FwdArgs& a, hipStream_t st) {
   const long long W = (long long)a.qtiles * a.geo.Hkv * a.splits;
   if (W == 0) return hipSuccess;
   const long long per_xcd = (W + 7) / 8;
+  timer_mark(LS_KERNEL_ATTN_FWD, st, false);
   hipLaunchKernelGGL((replay_fwd<D, DV>), dim3((unsigned)(per_xcd * 8)), dim3(256), 0, st, a);
+  timer_mark(LS_KERNEL_ATTN_FWD, st, true);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const long long total = (long long)a.geo.T * a.geo.Hq * (DV / 4);

@@ -18,7 +18,9 @@ LIB_PATH = os.path.join(_HERE, "liblsreplay.so")
 LS_OK, LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP = 0, -1, -2, -3, -4
 LS_MAX_RESPONSES_PER_CALL = 64
 EXPORTED = ("ls_replay_attn_workspace_bytes", "ls_replay_attn_fwd", "ls_replay_attn_bwd",
-            "ls_grpo_workspace_bytes", "ls_grpo_token_loss", "ls_status_string")
+            "ls_grpo_workspace_bytes", "ls_grpo_token_loss", "ls_status_string", "ls_kernel_timer_start",
+            "ls_kernel_timer_stop")
+LS_KERNEL_ATTN_FWD, LS_KERNEL_DKDV_PROMPT, LS_KERNEL_DQ, LS_KERNEL_GRPO_ROWS = 0, 1, 2, 3
 
 
 class LsError(RuntimeError):
@@ -61,6 +63,10 @@ def lib():
         L.ls_grpo_workspace_bytes.argtypes = [i64, i32, ctypes.POINTER(sz)]
         L.ls_grpo_token_loss.restype = ctypes.c_int
         L.ls_grpo_token_loss.argtypes = [vp, i32, i32, pi32, pf32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz]
+        L.ls_kernel_timer_start.restype = ctypes.c_int
+        L.ls_kernel_timer_start.argtypes = [i32]
+        L.ls_kernel_timer_stop.restype = ctypes.c_int
+        L.ls_kernel_timer_stop.argtypes = [pf32, pi32]
         _lib = L
     return _lib
 
@@ -222,3 +228,16 @@ def ls_grpo_token_loss(logits, targets, old_logp, R, rewards, eps, first, count,
         _stream(), V, len(Ra), Rp, rp, float(eps), int(first), int(count), _ptr(logits), _ptr(targets),
         _ptr(old_logp), _ptr(dlogits), _ptr(loss_accum), _ptr(logp_out), _ptr(clipped_out), _ptr(ws), ws.numel()))
     return dlogits
+
+
+def ls_kernel_timer_start(kernel: int) -> None:
+    """Arm the library's kernel timer for one kernel (an LS_KERNEL_* id)."""
+    _check("ls_kernel_timer_start", lib().ls_kernel_timer_start(int(kernel)))
+
+
+def ls_kernel_timer_stop():
+    """Disarm the kernel timer; returns (summed device milliseconds, launches)."""
+    ms = ctypes.c_float(0.0)
+    n = ctypes.c_int32(0)
+    _check("ls_kernel_timer_stop", lib().ls_kernel_timer_stop(ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)

@@ -136,3 +136,18 @@ def test_loss_validation():
     out = ctypes.c_size_t(0)
     assert L.lib().ls_grpo_workspace_bytes(1000, 4096, ctypes.byref(out)) == L.LS_OK and out.value >= 4000
     assert L.lib().ls_grpo_workspace_bytes(-1, 4096, ctypes.byref(out)) == L.LS_ERR_INVALID_ARG
+
+
+def test_kernel_timer_validation():
+    lib = L.lib()
+    ms, n = ctypes.c_float(1.0), ctypes.c_int32(7)
+    # stop without start: invalid, outputs cleared, no HIP call made
+    assert lib.ls_kernel_timer_stop(ctypes.byref(ms), ctypes.byref(n)) == L.LS_ERR_INVALID_ARG
+    assert ms.value == 0.0 and n.value == 0
+    for bad in (-1, 4, 100):
+        assert lib.ls_kernel_timer_start(bad) == L.LS_ERR_INVALID_ARG
+    assert lib.ls_kernel_timer_stop(None, None) == L.LS_ERR_INVALID_ARG
+    # armed, nothing launched: zero launches and zero time, without touching the device
+    assert lib.ls_kernel_timer_start(L.LS_KERNEL_DQ) == L.LS_OK
+    assert lib.ls_kernel_timer_stop(ctypes.byref(ms), ctypes.byref(n)) == L.LS_OK
+    assert ms.value == 0.0 and n.value == 0

@@ -185,3 +185,23 @@ def test_mid_shape_short_response():
     dq, dks, dvs = case.bwd(o, lse, dkp, dvp)
     t.cuda.synchronize()
     _check_all(dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp), case.oracle())
+
+
+def test_kernel_timer_counts_launches():
+    """The instrumentation timer brackets each launch of the armed kernel and nothing else."""
+    from prefix_shared_branch_amd import lsreplay as L
+    case = Case(inputs.CONFIGS["tiny"], [70, 90])
+    t = case.torch
+    dkp, dvp = case.accums()
+    L.ls_kernel_timer_start(L.LS_KERNEL_DKDV_PROMPT)
+    o, lse = case.fwd()
+    case.bwd(o, lse, dkp, dvp)      # exact mode: one prompt dK/dV launch
+    case.bwd(o, lse)                # response-only: no prompt dK/dV launch
+    case.bwd(o, lse, dkp, dvp)
+    ms, n = L.ls_kernel_timer_stop()
+    t.cuda.synchronize()
+    assert n == 2 and ms > 0.0, (ms, n)
+    L.ls_kernel_timer_start(L.LS_KERNEL_ATTN_FWD)
+    case.fwd()
+    ms, n = L.ls_kernel_timer_stop()
+    assert n == 1 and ms > 0.0, (ms, n)
