@@ -232,10 +232,16 @@ def copy_calibration():
     n = 1 << 30
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    for _ in range(4):
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    e0.record()
+    for _ in range(3):
         dst.copy_(src)
+    e1.record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 4}), flush=True)
+    gbps = 3 * 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 4, "copy_GBps": gbps}), flush=True)
 
 
 def main():
