@@ -123,6 +123,11 @@ int ls_replay_attn_fwd(void* stream, const ls_attn_desc* desc, const void* Kp, c
   a.ptiles_per_split = pl.ptiles_per_split;
   a.qtiles = pl.qtiles;
   for (int i = 0; i <= kMaxResp; ++i) a.tile0[i] = pl.tile0[i];
+  a.VTp = reinterpret_cast<const uint16_t*>(ws + pl.off_c);
+  a.VTs = reinterpret_cast<const uint16_t*>(ws + pl.off_d);
+  a.ppad = pl.ppad;
+  a.tpad = pl.tpad;
+  for (int i = 0; i <= kMaxResp; ++i) a.spos[i] = pl.spos[i];
   const hipError_t e = lsr::launch_attn_fwd(a, desc->Dqk, desc->Dv, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LS_OK : LS_ERR_HIP;
 }

@@ -18,7 +18,7 @@
 namespace lsr {
 
 namespace {
-constexpr int kQTileFwd = 128;  // packed query rows per forward workgroup (32 per wave)
+constexpr int kQTileFwd = 256;  // packed query rows per forward workgroup (64 per wave)
 constexpr int kQTileDq = 128;   // packed query rows per dQ workgroup
 constexpr int kKTile = 64;    // keys per forward / dQ tile
 constexpr int kDKTile = 128;  // keys per dK/dV workgroup
@@ -36,18 +36,23 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
   const int g = Hq / Hkv;
   const long long T = cu[n_resp];
   const int kQTile = which == 0 ? kQTileFwd : kQTileDq;
-  int qt = 0, kt = 0;
+  int qt = 0, kt = 0, sp = 0;
   for (int i = 0; i < n_resp; ++i) {
     pl->tile0[i] = qt;
     pl->ktile0[i] = kt;
+    pl->spos[i] = sp;
     const long long R = cu[i + 1] - cu[i];
     qt += (int)((R * g + kQTile - 1) / kQTile);
     kt += (int)((R + kDKTile - 1) / kDKTile);
+    sp += (int)((R + kKTile - 1) / kKTile * kKTile);
   }
   for (int i = n_resp; i <= kMaxResp; ++i) {
     pl->tile0[i] = qt;
     pl->ktile0[i] = kt;
+    pl->spos[i] = sp;
   }
+  pl->ppad = (int64_t)(P + kKTile - 1) / kKTile * kKTile;
+  pl->tpad = sp;
   pl->qtiles = qt;
   pl->ptiles = (P + kKTile - 1) / kKTile;
   pl->ktiles_prompt = which == 1 ? (P + kDKTile - 1) / kDKTile : 0;
@@ -71,6 +76,11 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
       pl->off_b = off;
       off = align256(off + (size_t)S * Hq * T * 4);
     }
+    // dimension-major packed V of the prompt and of the responses
+    pl->off_c = off;
+    off = align256(off + (size_t)Hkv * Dv * pl->ppad * 2);
+    pl->off_d = off;
+    off = align256(off + (size_t)Hkv * Dv * pl->tpad * 2);
   } else {
     pl->off_a = off;  // delta [Hq, T]
     off = align256(off + (size_t)Hq * T * 4);

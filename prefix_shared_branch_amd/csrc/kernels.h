@@ -50,12 +50,31 @@ struct AttnGeom {
   int32_t tok0[kMaxResp + 1];   // cu_seqlens
 };
 
+// Dimension-major repacking of key-major K or V rows (pack.hip): see launch_pack_keys_t.
+struct PackArgs {
+  const uint16_t* src;   // [rows, ld] bf16; head h, dim d of row r at src[r * ld + h * dim + d]
+  int64_t ld;
+  int32_t dim, heads;    // dim a multiple of 64
+  int32_t nseg;          // 1 .. kMaxResp segments
+  int64_t row0[kMaxResp];  // first source row of each segment
+  int32_t n[kMaxResp];     // keys of each segment
+  int64_t col0[kMaxResp];  // first output slot of each segment (multiple of 64, increasing)
+  uint16_t* out;         // [heads * dim, out_ld] bf16
+  int64_t out_ld;        // slots per output row (multiple of 64)
+  int64_t cols;          // slots written per row (= out_ld)
+};
+hipError_t launch_pack_keys_t(const PackArgs& a, hipStream_t st);
+
 struct FwdArgs {
   AttnGeom geo;
   uint16_t* O;          // bf16 [T, Hq, Dv]
   float* lse;           // [Hq, T]
   float* o_part;        // [S, T, Hq, Dv] fp32 (S > 1)
   float* lse_part;      // [S, Hq, T] (S > 1)
+  const uint16_t* VTp;  // packed prompt V: [Hkv * Dv, ppad] (pack.hip layout)
+  const uint16_t* VTs;  // packed response V: [Hkv * Dv, tpad], response i from slot spos[i]
+  int64_t ppad, tpad;
+  int32_t spos[kMaxResp + 1];
   int32_t splits;       // S
   int32_t ptiles;       // prompt key tiles
   int32_t ptiles_per_split;
@@ -89,8 +108,10 @@ struct AttnPlan {
   int tile0[kMaxResp + 1];
   int ktiles_prompt;
   int ktile0[kMaxResp + 1];
+  int64_t ppad, tpad;           // packed prompt / response key slots (multiples of 64)
+  int spos[kMaxResp + 1];       // first packed slot of each response
   size_t ws_bytes;
-  size_t off_a, off_b, off_c;   // workspace sub-buffer offsets
+  size_t off_a, off_b, off_c, off_d;   // workspace sub-buffer offsets
 };
 
 // which: 0 fwd, 1 bwd exact, 2 bwd response-only. Returns false if (Dqk, Dv) has no kernel.

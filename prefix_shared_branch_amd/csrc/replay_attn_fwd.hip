@@ -2,17 +2,19 @@
 // the queries of one response attend to all prompt keys and, causally, to the response's
 // own keys.
 //
-// replay_fwd: one workgroup = 4 waves x 64 = 256 GQA-packed query rows of one kv head, over
-// the prompt key tiles of one split (plus, in the last split, the response's causal key
-// tiles). 64-key K and V tiles stream global -> LDS by direct DMA (double-buffered, XOR-
-// swizzled rows without padding). Per 32-key block each wave computes S^T = K Q^T for its two
-// 32-row blocks (MFMA 32x32x16 bf16, Q fragments held in VGPRs, every K fragment read from LDS
-// feeds two MFMAs), an online softmax whose row statistics are lane-local (one query row per
-// lane; the O rescale is skipped when no row maximum moved), and O^T += V^T P^T with V^T
-// fetched by LDS transpose reads, again shared by both row blocks.
-// Workgroup ids are mapped so that each XCD owns a contiguous run of (kv head, split)
-// streams: concurrently resident query tiles sweep the same prompt K/V tiles, which are
-// then fetched from HBM once per XCD and served to its CUs from L2.
+// replay_fwd: one workgroup = 4 waves x 64 = 256 GQA-packed query rows of one kv head (one wave
+// per SIMD), over the prompt key tiles of one split (plus, in the last split, the response's
+// causal key tiles). Per 64-key tile, K (key-major) and V (dimension-major, packed by pack.hip)
+// stream global -> LDS by direct DMA into a three-stage ring of XOR-swizzled tiles. Per 32-key
+// block each wave computes S^T = K Q^T for its two 32-row blocks (MFMA 32x32x16 bf16; Q fragments
+// stay in registers; every K fragment read from LDS feeds two MFMAs), an online softmax whose row
+// statistics are lane-local (one query row per lane), and O^T += V^T P^T where P^T comes straight
+// from the score accumulators and every V^T fragment is one 16-byte LDS read feeding two MFMAs.
+// The softmax stabiliser is only moved when a row maximum exceeds it by more than 2^8 (in exp2
+// units), so the O rescale is rare; probabilities stay <= 256, far inside fp32/bf16 range.
+// Workgroup ids are mapped so that each XCD owns a contiguous run of (kv head, split) streams:
+// concurrently resident query tiles sweep the same prompt K/V tiles, which are then fetched from
+// HBM once per XCD and served to its CUs from L2.
 //
 // replay_fwd_merge: log-sum-exp merge of the split partials,
 //   lse = log sum_s exp(lse_s),  O = sum_s exp(lse_s - lse) O_s.
@@ -23,36 +25,43 @@ namespace lsr {
 
 namespace {
 
-// Query rows per wave: 32 * RB. RB = 1 keeps two waves per SIMD resident (latency of one wave's
-// softmax and LDS reads hidden behind the other's MFMAs); RB = 2 shares each LDS fragment between
-// two MFMAs but leaves one wave per SIMD.
-constexpr int kFwdRowBlocks = 1;
-
 template <int D, int DV>
 struct FwdCfg {
-  static constexpr int RB = kFwdRowBlocks;
-  static constexpr int BM = 128 * RB;         // packed query rows per workgroup
+  static constexpr int RB = 2;                // 32-row blocks per wave
+  static constexpr int BM = 4 * 32 * RB;      // packed query rows per workgroup
   static constexpr int BN = 64;               // keys per tile
   static constexpr int KCH = D / 8;           // 16-byte chunks per K row
-  static constexpr int VCH = DV / 8;
   static constexpr int KROW = D * 2;          // bytes per K row in LDS
-  static constexpr int VROW = DV * 2;
+  static constexpr int VTROW = BN * 2;        // bytes per packed V^T row (one dim, 64 keys)
   static constexpr int KBYTES = BN * KROW;
-  static constexpr int VBYTES = BN * VROW;
-  static constexpr int KINS = KBYTES / 1024 / 4;  // 1 KB direct-load instructions per wave per K tile
+  static constexpr int VBYTES = DV * VTROW;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int NSTAGE = 3;
+  static constexpr int KINS = KBYTES / 1024 / 4;  // 1 KB direct loads per wave per tile
   static constexpr int VINS = VBYTES / 1024 / 4;
   static constexpr int KS = D / 16;           // MFMA k-steps over the head dim
   static constexpr int NB = DV / 32;          // 32-wide blocks of the value dim
+  static constexpr float kStale = 8.0f;       // stabiliser slack (exp2 units)
 };
 
+__device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
+
+// max / sum of a value over lanes l and l ^ 32. The swap of two copies of v leaves, in each lane,
+// the lane's own value in one result and its partner's in the other; combining the two results
+// with a commutative operation gives both lanes the same bits.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D, int DV>
-__global__ __launch_bounds__(256, kFwdRowBlocks == 1 ? 2 : 1) void replay_fwd(FwdArgs a) {
+__global__ __launch_bounds__(256, 1) void replay_fwd(FwdArgs a) {
   using C = FwdCfg<D, DV>;
-  // two pipeline stages (64 KB at D = 128, so two workgroups fit in a CU's LDS)
-  __shared__ __attribute__((aligned(1024))) char sK0[C::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sK1[C::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV0[C::VBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV1[C::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE];
 
   const AttnGeom& G = a.geo;
   const int W = a.qtiles * G.Hkv * a.splits;
@@ -76,7 +85,7 @@ __global__ __launch_bounds__(256, kFwdRowBlocks == 1 ? 2 : 1) void replay_fwd(Fw
   const int hl = lane >> 5;
   const int l32 = lane & 31;
 
-  // two 32-row blocks per wave; one query row per lane in each
+  // query rows: block rb of wave wv holds packed rows m0 + 64 wv + 32 rb + (lane % 32)
   bool rvalid[C::RB];
   int trow[C::RB], hq[C::RB];
   bf16x8 qf[C::RB][C::KS];
@@ -91,30 +100,20 @@ __global__ __launch_bounds__(256, kFwdRowBlocks == 1 ? 2 : 1) void replay_fwd(Fw
     for (int ks = 0; ks < C::KS; ++ks) {
       if (rvalid[rb]) qf[rb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + ks * 16));
       else qf[rb][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      // with one wave per SIMD, Q fragments (only ever MFMA operands) live in AGPRs, leaving
-      // VGPRs for the accumulators and prefetched LDS fragments; at two waves per SIMD the
-      // register file is split evenly and they stay in VGPRs
-      if constexpr (C::RB == 2) asm volatile("" : "+a"(qf[rb][ks]));
+      // Q fragments are only ever MFMA operands: keep them in AGPRs
+      asm volatile("" : "+a"(qf[rb][ks]));
     }
   }
 
-  // lane-constant LDS byte offsets (the tile base and the 32-key block offset are added as immediates)
+  // lane-constant LDS byte offsets within a stage (block and tile offsets are immediates)
   int koff[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) koff[ks] = l32 * C::KROW + (((2 * ks + hl) ^ swz<C::KCH>(l32)) << 4);
-  int voff[2][C::NB];
-  {
-    const int jj = lane & 15;
+  int voff[2][2];  // [32-key block][16-key half]: packed slots 32 kb + 16 h + 8 hl .. +7 of dim row l32
 #pragma unroll
-    for (int sec = 0; sec < 2; ++sec) {
-      const int row = 4 * hl + (jj >> 2) + 8 * sec;  // row within the 16-row group (mod 16)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const int chunk = nb * 4 + 2 * ((lane >> 4) & 1) + ((jj & 3) >> 1);
-        voff[sec][nb] = row * C::VROW + ((chunk ^ swz<C::VCH>(row)) << 4) + (jj & 1) * 8;
-      }
-    }
-  }
+    for (int h = 0; h < 2; ++h) voff[kb][h] = C::KBYTES + l32 * C::VTROW + (((4 * kb + 2 * h + hl) ^ swz<8>(l32)) << 4);
 
   // key range: prompt tiles of this split, then (last split) the response's causal tiles
   const int pt0 = sp * a.ptiles_per_split;
@@ -124,170 +123,170 @@ __global__ __launch_bounds__(256, kFwdRowBlocks == 1 ? 2 : 1) void replay_fwd(Fw
   const int ns = (sp == a.splits - 1) ? (t_hi / C::BN + 1) : 0;
   const int nit = np + ns;
 
-  auto tile_info = [&](int it, const uint16_t*& kb, const uint16_t*& vb, int& key0, int& nvalid, bool& sfx) {
+  // global -> LDS for tile `it` into stage buffer `buf`
+  auto issue_tile = [&](int it, char* buf) {
+    const uint16_t* kb;
+    const uint16_t* vb;
+    int nvalid;
     if (it < np) {
-      key0 = (pt0 + it) * C::BN;
+      const int key0 = (pt0 + it) * C::BN;
       nvalid = min(C::BN, G.P - key0);
       kb = G.Kp + (int64_t)key0 * G.ldk + kvh * D;
-      vb = G.Vp + (int64_t)key0 * G.ldv + kvh * DV;
-      sfx = false;
+      vb = a.VTp + (int64_t)kvh * DV * a.ppad + key0;
     } else {
-      key0 = (it - np) * C::BN;
+      const int key0 = (it - np) * C::BN;
       nvalid = min(C::BN, R - key0);
       kb = G.Ks + (int64_t)(tokb + key0) * G.ldk + kvh * D;
-      vb = G.Vs + (int64_t)(tokb + key0) * G.ldv + kvh * DV;
-      sfx = true;
+      vb = a.VTs + (int64_t)kvh * DV * a.tpad + a.spos[ri] + key0;
     }
-  };
-  // global -> LDS: each 1 KB instruction fills 1024 / (row bytes) consecutive rows; rows past the
-  // valid keys re-read the last valid row (finite data, masked out of the softmax)
-  auto issue_tile = [&](int it, char* kdst, char* vdst) {
-    const uint16_t *kb, *vb;
-    int key0, nvalid;
-    bool sfx;
-    tile_info(it, kb, vb, key0, nvalid, sfx);
+    const int64_t vld = it < np ? a.ppad : a.tpad;
+    // an opaque copy of the lane id: the per-lane row/chunk arithmetic below is redone for every
+    // tile (a few VALU ops) instead of being hoisted out of the tile loop into pinned registers
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    // K: each 1 KB instruction fills 1024 / KROW rows; rows past the valid keys re-read the last
+    // valid row (finite data, masked out of the softmax)
 #pragma unroll
     for (int u = 0; u < C::KINS; ++u) {
       const int ins = wv * C::KINS + u;
-      const int row = ins * (64 / C::KCH) + lane / C::KCH;
-      const int c = (lane % C::KCH) ^ swz<C::KCH>(row);
-      lds_dma16(kb + (int64_t)min(row, nvalid - 1) * G.ldk + c * 8, kdst + ins * 1024);
+      const int row = ins * (64 / C::KCH) + ln / C::KCH;
+      const int c = (ln % C::KCH) ^ swz<C::KCH>(row);
+      lds_dma16(kb + (int64_t)min(row, nvalid - 1) * G.ldk + c * 8, buf + ins * 1024);
     }
+    // V^T: 8 dim rows of 128 bytes per instruction; slots past the keys hold zeros
 #pragma unroll
     for (int u = 0; u < C::VINS; ++u) {
       const int ins = wv * C::VINS + u;
-      const int row = ins * (64 / C::VCH) + lane / C::VCH;
-      const int c = (lane % C::VCH) ^ swz<C::VCH>(row);
-      lds_dma16(vb + (int64_t)min(row, nvalid - 1) * G.ldv + c * 8, vdst + ins * 1024);
+      const int row = ins * 8 + (ln >> 3);
+      const int c = (ln & 7) ^ swz<8>(row);
+      lds_dma16(vb + (int64_t)row * vld + c * 8, buf + C::KBYTES + ins * 1024);
     }
   };
 
   f32x16 o[C::RB][C::NB];
-  float m_run[C::RB], l_run[C::RB];
+  float mu[C::RB], l_run[C::RB];   // stabiliser (score * scale * log2 e) and row sum of this lane's keys
 #pragma unroll
   for (int rb = 0; rb < C::RB; ++rb) {
-    m_run[rb] = -INFINITY;
+    mu[rb] = -INFINITY;
     l_run[rb] = 0.0f;
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) o[rb][nb] = f32x16{};
   }
   const float c2 = G.scale_log2;
 
-  // only ragged prompt tiles and the response's diagonal tiles take the (wave-uniform) mask branch
-  auto compute = [&](int it, const char* kbuf, const char* vbuf) {
-    const uint16_t *kbp, *vbp;
+  auto compute = [&](int it, const char* buf) {
     int key0, nvalid;
     bool sfx;
-    tile_info(it, kbp, vbp, key0, nvalid, sfx);
+    if (it < np) {
+      key0 = (pt0 + it) * C::BN;
+      nvalid = min(C::BN, G.P - key0);
+      sfx = false;
+    } else {
+      key0 = (it - np) * C::BN;
+      nvalid = min(C::BN, R - key0);
+      sfx = true;
+    }
     const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
     const bool masked = causal || nvalid < C::BN;
-
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // S^T = K Q^T for both row blocks; each K fragment feeds two MFMAs
       f32x16 st[C::RB];
 #pragma unroll
       for (int rb = 0; rb < C::RB; ++rb) st[rb] = f32x16{};
-      bf16x8 vf[2][C::NB];
-      if constexpr (C::RB == 2) {
-        // one wave per SIMD: issue all K fragments of this 32-key block at once, then the
-        // S^T = K Q^T MFMAs, then all V^T fragments (transposed LDS reads) so they are in flight
-        // while the softmax runs
-        bf16x8 kf[C::KS];
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) kf[ks] = lds_b128_at(kbuf, kb * 32 * C::KROW + koff[ks]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8 kf = lds_b128_at(buf, kb * 32 * C::KROW + koff[ks]);
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
+        for (int rb = 0; rb < C::RB; ++rb) st[rb] = mfma32(kf, qf[rb][ks], st[rb]);
+      }
+      if (__builtin_expect(masked, 0)) {
+        asm volatile("");  // keeps this a real (wave-uniform) branch instead of per-element selects
+        // register r holds tile key kb*32 + 8(r/4) + 4hl + r%4; it is visible iff that key is below
+        // nvalid and (causal tiles) key0 + key <= the row's token
 #pragma unroll
-          for (int rb = 0; rb < C::RB; ++rb) st[rb] = mfma32(kf[ks], qf[rb][ks], st[rb]);
+        for (int rb = 0; rb < C::RB; ++rb) {
+          const int lim = min(nvalid, causal ? trow[rb] - key0 + 1 : nvalid) - kb * 32 - 4 * hl;
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          const int rowbase = (kb * 32 + 16 * hs) * C::VROW;
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb)
-            vf[hs][nb] = join_tr(lds_tr_at(vbuf, rowbase + voff[0][nb]), lds_tr_at(vbuf, rowbase + voff[1][nb]));
+          for (int r = 0; r < 16; ++r) st[rb][r] = (8 * (r >> 2) + (r & 3)) < lim ? st[rb][r] : -INFINITY;
         }
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        // two waves per SIMD hide each other's latencies: plain per-fragment order
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) st[0] = mfma32(lds_b128_at(kbuf, kb * 32 * C::KROW + koff[ks]), qf[0][ks], st[0]);
       }
-      if (masked) {
-#pragma unroll
-        for (int rb = 0; rb < C::RB; ++rb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            const bool bad = key >= nvalid || (causal && key0 + key > trow[rb]);
-            st[rb][r] = bad ? -INFINITY : st[rb][r];
-          }
-      }
-      // stage 4: online softmax, one row per lane (the other half-wave holds the row's other keys)
+      // online softmax, one query row per lane (the other half-wave holds the row's other keys)
+      bf16x8 pb[C::RB][2];
 #pragma unroll
       for (int rb = 0; rb < C::RB; ++rb) {
-        float mx = -INFINITY;
+        float mx = max3f(st[rb][0], st[rb][1], st[rb][2]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[rb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run[rb], mx);
-        const float ms = (m_new == -INFINITY ? 0.0f : m_new) * c2;
-        const float alpha = fast_exp2(m_run[rb] * c2 - ms);
-        m_run[rb] = m_new;
-        if (__any(alpha != 1.0f)) {
+        for (int r = 3; r < 15; r += 2) mx = max3f(mx, st[rb][r], st[rb][r + 1]);
+        mx = __builtin_fmaxf(mx, st[rb][15]);
+        mx = pair_max(mx) * c2;
+        const bool move = mx > mu[rb] + C::kStale;
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(move) != 0, 0)) {
+          asm volatile("");  // rare: a real branch, never speculated into unconditional multiplies
+          const float mnew = move ? mx : mu[rb];
+          const float alpha = move ? fast_exp2(mu[rb] - mnew) : 1.0f;   // 0 on a row's first visible keys
+          mu[rb] = mnew;
           l_run[rb] *= alpha;
 #pragma unroll
           for (int nb = 0; nb < C::NB; ++nb) o[rb][nb] *= alpha;
         }
-        float ls = 0.0f;
+        const float msub = mu[rb] == -INFINITY ? 0.0f : mu[rb];
+        // probabilities; the row sum is taken in fp32 (the LSE must hold to ~1e-5 even over a few keys)
+        float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(st[rb][r], c2, -ms));
-          st[rb][r] = p;
-          ls += p;
+        for (int r = 0; r < 16; r += 2) {
+          st[rb][r] = fast_exp2(__builtin_fmaf(st[rb][r], c2, -msub));
+          st[rb][r + 1] = fast_exp2(__builtin_fmaf(st[rb][r + 1], c2, -msub));
+          ls0 += st[rb][r];
+          ls1 += st[rb][r + 1];
         }
-        l_run[rb] += ls;
+        l_run[rb] += ls0 + ls1;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) pb[rb][h] = c_regs_to_bf16x8(st[rb], 8 * h);
       }
-      // stage 5: O^T += V^T P^T; each V^T fragment feeds two MFMAs
+      // O^T += V^T P^T; each V^T fragment (one 16-byte read of packed slots) feeds two MFMAs
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        bf16x8 pb[C::RB];
-#pragma unroll
-        for (int rb = 0; rb < C::RB; ++rb) pb[rb] = c_regs_to_bf16x8(st[rb], 8 * hs);
-        const int rowbase = (kb * 32 + 16 * hs) * C::VROW;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
-          const bf16x8 va = C::RB == 2 ? vf[hs][nb]
-                                       : join_tr(lds_tr_at(vbuf, rowbase + voff[0][nb]), lds_tr_at(vbuf, rowbase + voff[1][nb]));
+          const bf16x8 vf = lds_b128_at(buf, nb * 32 * C::VTROW + voff[kb][h]);
 #pragma unroll
-          for (int rb = 0; rb < C::RB; ++rb) o[rb][nb] = mfma32(va, pb[rb], o[rb][nb]);
+          for (int rb = 0; rb < C::RB; ++rb) o[rb][nb] = mfma32(vf, pb[rb][h], o[rb][nb]);
         }
-      }
     }
   };
 
-  // tile it+1 streams into the other stage while tile it is computed; the barrier after the
-  // wait makes every wave's part of tile it visible and retires all reads of the stage refilled next
-  if (nit > 0) issue_tile(0, sK0, sV0);
-  for (int it = 0; it < nit; it += 2) {
-    wait_vmem();
-    __syncthreads();
-    if (it + 1 < nit) issue_tile(it + 1, sK1, sV1);
-    compute(it, sK0, sV0);
-    if (it + 1 >= nit) break;
-    wait_vmem();
-    __syncthreads();
-    if (it + 2 < nit) issue_tile(it + 2, sK0, sV0);
-    compute(it + 1, sK1, sV1);
+  // three-stage ring: tile it+2 streams in while tile it is computed. Before computing tile it,
+  // wait for this wave's loads of tile it (tile it+1's stay in flight), then a barrier makes every
+  // wave's part visible and retires all reads of the stage refilled next (tile it-1's).
+  char* const st0 = smem;
+  char* const st1 = smem + C::STAGE;
+  char* const st2 = smem + 2 * C::STAGE;
+  constexpr int kPerTile = C::KINS + C::VINS;
+  if (nit > 0) issue_tile(0, st0);
+  if (nit > 1) issue_tile(1, st1);
+  for (int it = 0; it < nit; it += 3) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int t = it + j;
+      if (t >= nit) break;
+      char* cur = j == 0 ? st0 : (j == 1 ? st1 : st2);
+      char* nxt = j == 0 ? st2 : (j == 1 ? st0 : st1);
+      if (t + 1 < nit) wait_vmem_le<kPerTile>();
+      else wait_vmem();
+      __syncthreads();
+      if (t + 2 < nit) issue_tile(t + 2, nxt);
+      compute(t, cur);
+    }
   }
 
 #pragma unroll
   for (int rb = 0; rb < C::RB; ++rb) {
-    const float l = l_run[rb] + __shfl_xor(l_run[rb], 32, 64);
+    const float l = pair_sum(l_run[rb]);
     if (!rvalid[rb]) continue;
     const int64_t tok = tokb + trow[rb];
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const float lse = l > 0.0f ? m_run[rb] * G.scale + fast_log2(l) * kLn2 : -INFINITY;
+    const float lse = l > 0.0f ? (mu[rb] + fast_log2(l)) * kLn2 : -INFINITY;
     if (a.splits == 1) {
       uint16_t* orow = a.O + (tok * G.Hq + hq[rb]) * DV + 4 * hl;
 #pragma unroll
@@ -345,6 +344,42 @@ template <int D, int DV>
 hipError_t fwd_go(FwdArgs& a, hipStream_t st) {
   const long long W = (long long)a.qtiles * a.geo.Hkv * a.splits;
   if (W == 0) return hipSuccess;
+  // dimension-major packed V of the prompt and of every response
+  const AttnGeom& G = a.geo;
+  if (G.P > 0) {
+    PackArgs p;
+    p.src = G.Vp;
+    p.ld = G.ldv;
+    p.dim = DV;
+    p.heads = G.Hkv;
+    p.nseg = 1;
+    p.row0[0] = 0;
+    p.n[0] = G.P;
+    p.col0[0] = 0;
+    p.out = const_cast<uint16_t*>(a.VTp);
+    p.out_ld = a.ppad;
+    p.cols = a.ppad;
+    hipError_t e = launch_pack_keys_t(p, st);
+    if (e != hipSuccess) return e;
+  }
+  {
+    PackArgs p;
+    p.src = G.Vs;
+    p.ld = G.ldv;
+    p.dim = DV;
+    p.heads = G.Hkv;
+    p.nseg = G.n_resp;
+    for (int i = 0; i < G.n_resp; ++i) {
+      p.row0[i] = G.tok0[i];
+      p.n[i] = G.tok0[i + 1] - G.tok0[i];
+      p.col0[i] = a.spos[i];
+    }
+    p.out = const_cast<uint16_t*>(a.VTs);
+    p.out_ld = a.tpad;
+    p.cols = a.tpad;
+    hipError_t e = launch_pack_keys_t(p, st);
+    if (e != hipSuccess) return e;
+  }
   const long long per_xcd = (W + 7) / 8;
   timer_mark(LS_KERNEL_ATTN_FWD, st, false);
   hipLaunchKernelGGL((replay_fwd<D, DV>), dim3((unsigned)(per_xcd * 8)), dim3(256), 0, st, a);

@@ -1,0 +1,115 @@
+"""GPU parity at the full prompt lengths of the long and Million-token workloads.
+
+Replay attention at P = 262,144 and P = 1,048,576 (LongStraw study notes §2-1 step 4, §3-2 (2)/(4)).
+
+* **Short responses.** The GPU runs every head of the configuration. The oracle recomputes kv head 0
+  and its query heads in full: O, LSE, dQ, dKs, dVs, and the prompt dK/dV accumulators. Heads are
+  independent, and a response's first rows form an exact sub-problem, since row t sees only suffix
+  keys up to t.
+* **Full response.** Response 0 of the Million workload runs in the launch configuration the
+  benchmark times: one call per 4,096-token response, with exact prompt gradients.
+  * O, LSE and dQ are checked on sampled rows. Each row depends on that row alone.
+  * The value-gradient column sums are checked for every kv head. For each kv head k,
+    Σ_j dV_P[j,k] + Σ_s dVs[s,k] = Σ_t Σ_{h in k} dO[t,h], because each row's softmax weights sum
+    to one. This holds at any size and needs no O(P·R) oracle work.
+"""
+import numpy as np
+import pytest
+
+from oracle import attn
+from prefix_shared_branch_amd import inputs
+from tests.helpers import check_bf16_out, check_fp32_accum, dev_bf16, host_f64
+
+pytestmark = pytest.mark.gpu
+
+f64 = inputs.bf16_bits_to_f64
+
+
+class Prompt:
+    """Full-size prompt K/V of a config: device copies (all heads) and float64 kv-head-0 slices."""
+
+    def __init__(self, cfg):
+        import torch
+        self.cfg = cfg
+        kp, vp = inputs.prompt_k(cfg), inputs.prompt_v(cfg)
+        self.kp, self.vp = dev_bf16(kp), dev_bf16(vp)
+        self.kp0, self.vp0 = f64(kp[:, :1, :]), f64(vp[:, :1, :])
+        del kp, vp
+        self.torch = torch
+
+    def run(self, r, exact=True):
+        """fwd + bwd of the first r rows of response 0 on the GPU (one call each)."""
+        from prefix_shared_branch_amd import lsreplay as L
+        t, cfg = self.torch, self.cfg
+        bits = {n: fn(cfg, 0, r) for n, fn in (("q", inputs.suffix_q), ("ks", inputs.suffix_k),
+                                                ("vs", inputs.suffix_v), ("do", inputs.suffix_do))}
+        d = {n: dev_bf16(b) for n, b in bits.items()}
+        dkp = t.zeros(cfg.P, cfg.Hkv, cfg.Dqk, dtype=t.float32, device="cuda") if exact else None
+        dvp = t.zeros(cfg.P, cfg.Hkv, cfg.Dv, dtype=t.float32, device="cuda") if exact else None
+        o, lse = L.ls_replay_attn_fwd(d["q"], d["ks"], d["vs"], self.kp, self.vp, [0, r], cfg.scale)
+        dq, dks, dvs = L.ls_replay_attn_bwd(d["q"], d["ks"], d["vs"], self.kp, self.vp, [0, r], o, lse, d["do"],
+                                            dkp, dvp, cfg.scale)
+        t.cuda.synchronize()
+        return bits, dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp)
+
+
+def _head0_operands(cfg, bits):
+    g = cfg.Hq // cfg.Hkv
+    return (f64(bits["q"][:, :g, :]), f64(bits["ks"][:, :1, :]), f64(bits["vs"][:, :1, :]),
+            f64(bits["do"][:, :g, :]), g)
+
+
+def _check_short(pr, r):
+    cfg = pr.cfg
+    bits, got = pr.run(r)
+    Q, Ks, Vs, dO, g = _head0_operands(cfg, bits)
+    cu = [0, r]
+    O, LSE = attn.replay_attn_fwd(pr.kp0, pr.vp0, Q, Ks, Vs, cu, cfg.scale)
+    dKp, dVp = np.zeros(pr.kp0.shape), np.zeros(pr.vp0.shape)
+    dQ, dKs, dVs = attn.replay_attn_bwd(pr.kp0, pr.vp0, Q, Ks, Vs, dO, cu, cfg.scale, dKp, dVp)
+    check_bf16_out(host_f64(got["O"][:, :g]), O, "O")
+    lse = host_f64(got["LSE"][:g])
+    assert np.max(np.abs(lse - LSE)) <= 1e-4, np.max(np.abs(lse - LSE))
+    check_bf16_out(host_f64(got["dQ"][:, :g]), dQ, "dQ")
+    check_bf16_out(host_f64(got["dKs"][:, :1]), dKs, "dKs")
+    check_bf16_out(host_f64(got["dVs"][:, :1]), dVs, "dVs")
+    check_fp32_accum(host_f64(got["dKp"][:, :1]), dKp, "dKp")
+    check_fp32_accum(host_f64(got["dVp"][:, :1]), dVp, "dVp")
+
+
+def test_long_prompt_short_response():
+    pr = Prompt(inputs.CONFIGS["long"])
+    _check_short(pr, 40)
+
+
+@pytest.fixture(scope="module")
+def million():
+    return Prompt(inputs.CONFIGS["million"])
+
+
+def test_million_prompt_short_response(million):
+    _check_short(million, 16)
+
+
+def test_million_full_response_sampled_rows_and_column_sums(million):
+    pr, cfg = million, million.cfg
+    r = int(inputs.response_lengths(cfg)[0])
+    bits, got = pr.run(r)
+    Q, Ks, Vs, dO, g = _head0_operands(cfg, bits)
+    rows = np.array([0, 63, 2047, r - 1])
+    O, LSE = attn.replay_attn_fwd(pr.kp0, pr.vp0, Q, Ks, Vs, [0, r], cfg.scale, rows=rows)
+    check_bf16_out(host_f64(got["O"][rows, :g]), O[rows], "O rows")
+    lse = host_f64(got["LSE"][:g])[:, rows]
+    d = lse - LSE[:, rows]
+    assert np.max(np.abs(d)) <= 1e-4, f"LSE rows {rows.tolist()}: signed differences by head\n{d}"
+
+    dQ = attn.replay_attn_bwd_rows(pr.kp0, pr.vp0, Q, Ks, Vs, dO, [0, r], cfg.scale, rows)
+    check_bf16_out(host_f64(got["dQ"][rows, :g]), dQ, "dQ rows")
+
+    # column sums of the value gradient, every kv head (fp32 sums of P + R terms)
+    do_all = f64(bits["do"]).reshape(r, cfg.Hkv, g, cfg.Dv)
+    want = do_all.sum(axis=(0, 2))                                       # [Hkv, Dv]
+    have = (got["dVp"].double().sum(dim=0) + got["dVs"].double().sum(dim=0)).cpu().numpy()
+    for k in range(cfg.Hkv):
+        rel = np.linalg.norm(have[k] - want[k]) / np.linalg.norm(want[k])
+        assert rel <= 1e-3, (k, rel)
