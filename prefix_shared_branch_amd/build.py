@@ -13,15 +13,16 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblsreplay.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-HIP_SOURCES = ["grpo_loss.hip", "replay_attn_fwd.hip", "replay_attn_bwd.hip", "pack.hip"]
+HIP_SOURCES = ["grpo_loss.hip", "replay_attn_fwd.hip", "replay_attn_bwd.hip", "replay_attn_dq.hip", "pack.hip"]
 CXX_SOURCES = ["api.cpp", "attn_plan.cpp", "timer.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 # the packed-fp32 feature stays off: every v_pk_*_f32 is left out of the kernels
 HIP_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-ffp-contract=fast"]
-# Per-source extras. Forward: MFMA accumulators in VGPRs -- the softmax rescale touches them with
-# VALU ops, which cannot address AGPRs, and the default AGPR form copies them back and forth.
-SOURCE_FLAGS = {"replay_attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extras. Forward and dQ: MFMA results in VGPRs -- their score tiles are read by VALU
+# ops, which cannot address AGPRs, and the default AGPR form copies them back and forth.
+SOURCE_FLAGS = {"replay_attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "replay_attn_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):

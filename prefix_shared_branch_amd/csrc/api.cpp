@@ -170,6 +170,11 @@ int ls_replay_attn_bwd(void* stream, const ls_attn_desc* desc, const void* Kp, c
   a.ptiles_per_split = pl.ptiles_per_split;
   a.qtiles = pl.qtiles;
   for (int i = 0; i <= kMaxResp; ++i) a.tile0[i] = pl.tile0[i];
+  a.KTp = reinterpret_cast<const uint16_t*>(ws + pl.off_c);
+  a.KTs = reinterpret_cast<const uint16_t*>(ws + pl.off_d);
+  a.ppad = pl.ppad;
+  a.tpad = pl.tpad;
+  for (int i = 0; i <= kMaxResp; ++i) a.spos[i] = pl.spos[i];
   a.ktiles_prompt = (a.dKp != nullptr) ? pl.ktiles_prompt : 0;
   for (int i = 0; i <= kMaxResp; ++i) a.ktile0[i] = pl.ktile0[i];
   const hipError_t e = lsr::launch_attn_bwd(a, desc->Dqk, desc->Dv, static_cast<hipStream_t>(stream));

@@ -19,7 +19,7 @@ namespace lsr {
 
 namespace {
 constexpr int kQTileFwd = 256;  // packed query rows per forward workgroup (64 per wave)
-constexpr int kQTileDq = 128;   // packed query rows per dQ workgroup
+constexpr int kQTileDq = 256;   // packed query rows per dQ workgroup (64 per wave)
 constexpr int kKTile = 64;    // keys per forward / dQ tile
 constexpr int kDKTile = 128;  // keys per dK/dV workgroup
 constexpr int kTargetBlocks = 2048;
@@ -88,6 +88,11 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
       pl->off_b = off;
       off = align256(off + (size_t)S * T * Hq * Dqk * 4);
     }
+    // dimension-major packed K of the prompt and of the responses (dQ kernel)
+    pl->off_c = off;
+    off = align256(off + (size_t)Hkv * Dqk * pl->ppad * 2);
+    pl->off_d = off;
+    off = align256(off + (size_t)Hkv * Dqk * pl->tpad * 2);
   }
   pl->ws_bytes = off;
   return true;

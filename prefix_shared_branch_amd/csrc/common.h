@@ -66,6 +66,12 @@ __device__ __forceinline__ bf16x8 c_regs_to_bf16x8(const f32x16& c, int r0) {
   return v;
 }
 
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
+
 __device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t* lds_elem_ptr) {
   return *reinterpret_cast<const LSR_LDS bf16x8*>(reinterpret_cast<uintptr_t>(lds_elem_ptr));
 }

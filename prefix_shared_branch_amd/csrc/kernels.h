@@ -94,6 +94,10 @@ struct BwdArgs {
   float* dVp;
   float* delta;         // workspace [Hq, T]: rowsum(dO * O)
   float* dq_part;       // workspace [S, T, Hq, Dqk] fp32 (S > 1)
+  const uint16_t* KTp;  // packed prompt K: [Hkv * Dqk, ppad] (pack.hip layout)
+  const uint16_t* KTs;  // packed response K: [Hkv * Dqk, tpad], response i from slot spos[i]
+  int64_t ppad, tpad;
+  int32_t spos[kMaxResp + 1];
   int32_t splits;
   int32_t ptiles;
   int32_t ptiles_per_split;
@@ -118,6 +122,8 @@ struct AttnPlan {
 bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, const int32_t* cu, AttnPlan* plan);
 hipError_t launch_attn_fwd(FwdArgs& a, int Dqk, int Dv, hipStream_t st);
 hipError_t launch_attn_bwd(BwdArgs& a, int Dqk, int Dv, hipStream_t st);
+// dQ part of the backward (replay_attn_dq.hip): K packing, dQ kernel, split reduction
+hipError_t launch_bwd_dq(BwdArgs& a, int Dqk, int Dv, hipStream_t st);
 
 // Kernel timer hooks (timer.cpp): bracket a launch; no-ops unless the timer is armed for `kernel`
 // (an ls_kernel_id value).

@@ -14,8 +14,7 @@
 //                  exactly one workgroup per call); P and dS enter the MFMAs as a bf16 hi/lo
 //                  pair so the fp32 accumulators keep ~16 significant bits per term.
 //                  Suffix tiles: causal, bf16 dKs/dVs stores.
-// replay_bwd_dq    query-tile owner with split-K over the prompt (like the forward);
-//                  recomputes S and dP per key tile; partials summed in fixed order.
+// dQ (query-tile owner, split-K over the prompt) is in replay_attn_dq.hip.
 #include <type_traits>
 
 #include "common.h"
@@ -24,12 +23,6 @@
 namespace lsr {
 
 namespace {
-
-__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
-__device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
 
 // hi = bf16(x), lo = bf16(x - hi) for 8 consecutive C registers
 __device__ __forceinline__ void split_bf16x8(const f32x16& c, int r0, bf16x8& hi, bf16x8& lo) {
@@ -328,246 +321,6 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ dQ (query owner, split-K)
-template <int D, int DV>
-struct DqCfg {
-  static constexpr int BM = 128;              // packed query rows per workgroup (32 per wave)
-  static constexpr int BN = 64;               // keys per tile
-  static constexpr int KCH = D / 8;           // 16-byte chunks per row
-  static constexpr int VCH = DV / 8;
-  static constexpr int KP = KCH + 1;          // padded pitches in chunks (row-wise reads conflict-free)
-  static constexpr int VP = VCH + 1;
-  static constexpr int KROW = KP * 16;        // LDS bytes per row
-  static constexpr int VROW = VP * 16;
-  static constexpr int KBYTES = BN * KROW;
-  static constexpr int VBYTES = BN * VROW;
-  static constexpr int KS = D / 16;
-  static constexpr int VS = DV / 16;
-  static constexpr int DB = D / 32;
-};
-
-// Two workgroups per CU (68 KB of LDS each, <= 256 registers per wave) so that the two waves on a
-// SIMD hide each other's LDS and softmax latency. K and V tiles stream global -> LDS by DMA into
-// padded rows; K is read both row-wise (S^T = K Q^T) and transposed (dQ^T = K^T dS^T).
-template <int D, int DV>
-__global__ __launch_bounds__(256, 2) void replay_bwd_dq(BwdArgs a) {
-  using C = DqCfg<D, DV>;
-  __shared__ __attribute__((aligned(1024))) char sK0[C::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sK1[C::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV0[C::VBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV1[C::VBYTES];
-
-  const AttnGeom& G = a.geo;
-  const int W = a.qtiles * G.Hkv * a.splits;
-  const int per_xcd = (W + 7) >> 3;
-  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (w >= W) return;
-  const int strm = w / a.qtiles;
-  const int qt = w - strm * a.qtiles;
-  const int kvh = strm / a.splits;
-  const int sp = strm - kvh * a.splits;
-  int ri = 0;
-  while (qt >= a.tile0[ri + 1]) ++ri;
-  const int tokb = G.tok0[ri];
-  const int R = G.tok0[ri + 1] - tokb;
-  const int g = G.g;
-  const int M = R * g;
-  const int m0 = (qt - a.tile0[ri]) * C::BM;
-
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int hl = lane >> 5;
-  const int l32 = lane & 31;
-  const int mrow = m0 + wv * 32 + l32;
-  const bool rvalid = mrow < M;
-  const int trow = rvalid ? mrow / g : 0;
-  const int hq = kvh * g + (rvalid ? mrow - trow * g : 0);
-  const int64_t tok = tokb + trow;
-
-  bf16x8 qf[C::KS], of[C::VS];
-  {
-    const uint16_t* qrow = G.Q + (tok * G.Hq + hq) * D + hl * 8;
-    const uint16_t* orow = a.dO + (tok * G.Hq + hq) * DV + hl * 8;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = rvalid ? ld_bf16x8(qrow + ks * 16) : zero_bf16x8();
-#pragma unroll
-    for (int ks = 0; ks < C::VS; ++ks) of[ks] = rvalid ? ld_bf16x8(orow + ks * 16) : zero_bf16x8();
-  }
-  const float lrow = rvalid ? a.lse[(int64_t)hq * G.T + tok] * kLog2e : INFINITY;
-  const float drow = rvalid ? a.delta[(int64_t)hq * G.T + tok] : 0.0f;
-
-  // lane-constant LDS byte offsets; row-wise reads of K and V share one table (same row length)
-  // per-lane LDS bases; every fragment adds a compile-time immediate
-  const int rbk = l32 * C::KROW + hl * 16;   // row-wise reads of K (key l32, 8 dims at 16ks + 8hl)
-  const int rbv = l32 * C::VROW + hl * 16;   // row-wise reads of V
-  // transposed reads of K: row 4hl + jj/4 (+ 8 sec + 16 hs + 32 kb), column 16 (lane/16 % 2) + 4 (jj % 4) (+ 32 b)
-  const int tbk = (4 * hl + ((lane & 15) >> 2)) * C::KROW + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-
-  const int pt0 = sp * a.ptiles_per_split;
-  const int np = max(0, min(a.ptiles, pt0 + a.ptiles_per_split) - pt0);
-  const int t_lo = m0 / g;
-  const int t_hi = (min(M, m0 + C::BM) - 1) / g;
-  const int ns = (sp == a.splits - 1) ? (t_hi / C::BN + 1) : 0;
-  const int nit = np + ns;
-
-  auto tile_info = [&](int it, const uint16_t*& kb, const uint16_t*& vb, int& key0, int& nvalid, bool& sfx) {
-    if (it < np) {
-      key0 = (pt0 + it) * C::BN;
-      nvalid = min(C::BN, G.P - key0);
-      kb = G.Kp + (int64_t)key0 * G.ldk + kvh * D;
-      vb = G.Vp + (int64_t)key0 * G.ldv + kvh * DV;
-      sfx = false;
-    } else {
-      key0 = (it - np) * C::BN;
-      nvalid = min(C::BN, R - key0);
-      kb = G.Ks + (int64_t)(tokb + key0) * G.ldk + kvh * D;
-      vb = G.Vs + (int64_t)(tokb + key0) * G.ldv + kvh * DV;
-      sfx = true;
-    }
-  };
-  auto issue_tile = [&](int it, char* kdst, char* vdst) {
-    const uint16_t *kb, *vb;
-    int key0, nvalid;
-    bool sfx;
-    tile_info(it, kb, vb, key0, nvalid, sfx);
-    dma_tile64<C::KCH, C::KP>(kb, G.ldk, nvalid, kdst, wv, lane);
-    dma_tile64<C::VCH, C::VP>(vb, G.ldv, nvalid, vdst, wv, lane);
-  };
-
-  f32x16 dq[C::DB];
-#pragma unroll
-  for (int b = 0; b < C::DB; ++b) dq[b] = f32x16{};
-  const float c2 = G.scale_log2;
-
-  // MASK is a compile-time flag: only ragged prompt tiles and the response's diagonal tiles take
-  // the masked body; everywhere else the softmax has no per-element conditions at all
-  auto compute_body = [&](auto mask_tag, const char* kbuf, const char* vbuf, int key0, int nvalid, bool causal) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // Fragments stream in groups of four: each group's LDS reads are in flight while the
-      // previous group's MFMAs run, so at most two groups (32 registers) are live at once.
-      // S^T[key][row] = K Q^T, dP^T = V dO^T: lane holds row (lane & 31), keys 8(r/4) + 4hl + r%4
-      constexpr int NG = C::KS / 2;  // fragments per group; equals the number of 32-wide dQ blocks
-      static_assert(C::KS == C::VS && NG == C::DB, "grouping assumes Dqk == Dv");
-      const char* kr = kbuf + kb * 32 * C::KROW;
-      const char* vr = vbuf + kb * 32 * C::VROW;
-      bf16x8 g0[NG], g1[NG];
-#pragma unroll
-      for (int i = 0; i < NG; ++i) g0[i] = lds_b128_at(kr + i * 32, rbk);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NG; ++i) g1[i] = lds_b128_at(kr + (NG + i) * 32, rbk);
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int i = 0; i < NG; ++i) s = mfma32(g0[i], qf[i], s);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NG; ++i) g0[i] = lds_b128_at(vr + i * 32, rbv);
-#pragma unroll
-      for (int i = 0; i < NG; ++i) s = mfma32(g1[i], qf[NG + i], s);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NG; ++i) g1[i] = lds_b128_at(vr + (NG + i) * 32, rbv);
-#pragma unroll
-      for (int i = 0; i < NG; ++i) dp = mfma32(g0[i], of[i], dp);
-      __builtin_amdgcn_sched_barrier(0);
-      // transposed K fragments (first half of the keys) in flight while dS is formed
-      auto tr_frags = [&](int hs, bf16x8* tf) {
-        const char* kt = kbuf + (kb * 32 + 16 * hs) * C::KROW;
-#pragma unroll
-        for (int b = 0; b < C::DB; ++b)
-          tf[b] = join_tr(lds_tr_at(kt + b * 64, tbk), lds_tr_at(kt + 8 * C::KROW + b * 64, tbk));
-      };
-      tr_frags(0, g0);
-#pragma unroll
-      for (int i = 0; i < NG; ++i) dp = mfma32(g1[i], of[NG + i], dp);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 ds;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        float pv = fast_exp2(__builtin_fmaf(s[r], c2, -lrow));
-        if constexpr (MASK) pv = (key >= nvalid || (causal && key0 + key > trow)) ? 0.0f : pv;
-        ds[r] = pv * (dp[r] - drow);
-      }
-      // dQ^T[d][row] += K^T dS^T (second half's fragments load under the first half's MFMAs)
-      tr_frags(1, g1);
-      {
-        const bf16x8 db = c_regs_to_bf16x8(ds, 0);
-#pragma unroll
-        for (int b = 0; b < C::DB; ++b) dq[b] = mfma32(g0[b], db, dq[b]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        const bf16x8 db = c_regs_to_bf16x8(ds, 8);
-#pragma unroll
-        for (int b = 0; b < C::DB; ++b) dq[b] = mfma32(g1[b], db, dq[b]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  auto compute = [&](int it, const char* kbuf, const char* vbuf) {
-    const uint16_t *kbp, *vbp;
-    int key0, nvalid;
-    bool sfx;
-    tile_info(it, kbp, vbp, key0, nvalid, sfx);
-    const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
-    if (causal || nvalid < C::BN) compute_body(std::true_type{}, kbuf, vbuf, key0, nvalid, causal);
-    else compute_body(std::false_type{}, kbuf, vbuf, key0, nvalid, causal);
-  };
-
-  if (nit > 0) issue_tile(0, sK0, sV0);
-  for (int it = 0; it < nit; it += 2) {
-    wait_vmem();
-    __syncthreads();
-    if (it + 1 < nit) issue_tile(it + 1, sK1, sV1);
-    compute(it, sK0, sV0);
-    if (it + 1 >= nit) break;
-    wait_vmem();
-    __syncthreads();
-    if (it + 2 < nit) issue_tile(it + 2, sK0, sV0);
-    compute(it + 1, sK1, sV1);
-  }
-
-  if (!rvalid) return;
-  // C layout of dQ^T: lane holds row (lane & 31), dims 32b + 8(r/4) + 4hl + r%4
-  const float sc = G.scale;
-  if (a.splits == 1) {
-    uint16_t* dst = a.dQ + (tok * G.Hq + hq) * D + 4 * hl;
-#pragma unroll
-    for (int b = 0; b < C::DB; ++b)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x2 v = {pack_bf16x2(dq[b][4 * q] * sc, dq[b][4 * q + 1] * sc),
-                         pack_bf16x2(dq[b][4 * q + 2] * sc, dq[b][4 * q + 3] * sc)};
-        *reinterpret_cast<u32x2*>(dst + b * 32 + 8 * q) = v;
-      }
-  } else {
-    float* dst = a.dq_part + (((int64_t)sp * G.T + tok) * G.Hq + hq) * D + 4 * hl;
-#pragma unroll
-    for (int b = 0; b < C::DB; ++b)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = {dq[b][4 * q], dq[b][4 * q + 1], dq[b][4 * q + 2], dq[b][4 * q + 3]};
-        *reinterpret_cast<f32x4*>(dst + b * 32 + 8 * q) = v;
-      }
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void replay_bwd_dq_reduce(BwdArgs a) {
-  const AttnGeom& G = a.geo;
-  const int64_t n4 = (int64_t)G.T * G.Hq * D / 4;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= n4) return;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.splits; ++s) acc += reinterpret_cast<const f32x4*>(a.dq_part)[(int64_t)s * n4 + idx];
-  acc *= G.scale;
-  const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-  reinterpret_cast<u32x2*>(a.dQ)[idx] = v;
-}
-
 template <int D, int DV>
 hipError_t bwd_go(BwdArgs& a, hipStream_t st) {
   const AttnGeom& G = a.geo;
@@ -591,21 +344,7 @@ hipError_t bwd_go(BwdArgs& a, hipStream_t st) {
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  {
-    const long long W = (long long)a.qtiles * G.Hkv * a.splits;
-    if (W > 0) {
-      timer_mark(LS_KERNEL_DQ, st, false);
-      hipLaunchKernelGGL((replay_bwd_dq<D, DV>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(256), 0, st, a);
-      timer_mark(LS_KERNEL_DQ, st, true);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-  }
-  if (a.splits > 1) {
-    const long long n4 = (long long)G.T * G.Hq * D / 4;
-    hipLaunchKernelGGL((replay_bwd_dq_reduce<D>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  return hipSuccess;
+  return launch_bwd_dq(a, D, DV, st);
 }
 
 }  // namespace

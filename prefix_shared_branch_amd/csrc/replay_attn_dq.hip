@@ -1,0 +1,350 @@
+// Replay attention backward, dQ part, on gfx950 (LongStraw study notes, §2-1 step 4 and §2-2):
+// with P = exp(S scale - LSE), dP = dO V^T, Delta = rowsum(dO * O) and dS = P (dP - Delta),
+//   dQ_r = scale sum_j dS_rj K_j
+// over the prompt keys and the response's own (causal) keys. Query-tile owner with split-K over
+// the prompt, like the forward; split partials are summed in a fixed order by
+// replay_bwd_dq_reduce (deterministic), which also applies the scale and rounds to bf16.
+#include "common.h"
+#include "kernels.h"
+
+namespace lsr {
+
+namespace {
+
+// ------------------------------------------------------------------ dQ (query owner, split-K)
+template <int D, int DV>
+struct DqCfg {
+  static constexpr int RB = 2;                // 32-row blocks per wave
+  static constexpr int BM = 4 * 32 * RB;      // packed query rows per workgroup
+  static constexpr int BN = 64;               // keys per tile
+  static constexpr int KCH = D / 8;           // 16-byte chunks per K row
+  static constexpr int VCH = DV / 8;
+  static constexpr int KROW = D * 2;
+  static constexpr int VROW = DV * 2;
+  static constexpr int TROW = BN * 2;         // bytes per packed K^T row (one dim, 64 keys)
+  static constexpr int KBYTES = BN * KROW;
+  static constexpr int VBYTES = BN * VROW;
+  static constexpr int TBYTES = D * TROW;
+  static constexpr int STAGE = KBYTES + VBYTES + TBYTES;
+  static constexpr int NSTAGE = 3;
+  static constexpr int KINS = KBYTES / 4096;  // 1 KB direct loads per wave per tile
+  static constexpr int VINS = VBYTES / 4096;
+  static constexpr int TINS = TBYTES / 4096;
+  static constexpr int KS = D / 16;
+  static constexpr int VS = DV / 16;
+  static constexpr int DB = D / 32;
+};
+
+// One workgroup = 4 waves x 64 GQA-packed query rows (one wave per SIMD) over the key tiles of one
+// split. Per 64-key tile, K and V (key-major) and the packed K^T (dimension-major, pack.hip layout)
+// stream global -> LDS by direct DMA into a three-stage ring of XOR-swizzled tiles. Per 32-key
+// block each wave recomputes S^T = K Q^T and dP^T = V dO^T for its two row blocks (Q and dO
+// fragments stay in AGPRs; every K or V fragment feeds two MFMAs), forms dS = P (dP - Delta) with
+// P = exp(S scale - LSE), and accumulates dQ^T += K^T dS^T with every K^T fragment a single
+// 16-byte LDS read feeding two MFMAs.
+template <int D, int DV>
+__global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
+  using C = DqCfg<D, DV>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE];
+
+  const AttnGeom& G = a.geo;
+  const int W = a.qtiles * G.Hkv * a.splits;
+  const int per_xcd = (W + 7) >> 3;
+  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (w >= W) return;
+  const int strm = w / a.qtiles;
+  const int qt = w - strm * a.qtiles;
+  const int kvh = strm / a.splits;
+  const int sp = strm - kvh * a.splits;
+  int ri = 0;
+  while (qt >= a.tile0[ri + 1]) ++ri;
+  const int tokb = G.tok0[ri];
+  const int R = G.tok0[ri + 1] - tokb;
+  const int g = G.g;
+  const int M = R * g;
+  const int m0 = (qt - a.tile0[ri]) * C::BM;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+
+  bool rvalid[C::RB];
+  int trow[C::RB], hq[C::RB];
+  float lrow[C::RB], drow[C::RB];
+  bf16x8 qf[C::RB][C::KS], of[C::RB][C::VS];
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb) {
+    const int mrow = m0 + wv * 32 * C::RB + rb * 32 + l32;
+    rvalid[rb] = mrow < M;
+    trow[rb] = rvalid[rb] ? mrow / g : 0;
+    hq[rb] = kvh * g + (rvalid[rb] ? mrow - trow[rb] * g : 0);
+    const int64_t tok = tokb + trow[rb];
+    const uint16_t* qrow = G.Q + (tok * G.Hq + hq[rb]) * D + hl * 8;
+    const uint16_t* orow = a.dO + (tok * G.Hq + hq[rb]) * DV + hl * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      qf[rb][ks] = rvalid[rb] ? ld_bf16x8(qrow + ks * 16) : zero_bf16x8();
+      asm volatile("" : "+a"(qf[rb][ks]));  // MFMA operands only: AGPRs
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::VS; ++ks) {
+      of[rb][ks] = rvalid[rb] ? ld_bf16x8(orow + ks * 16) : zero_bf16x8();
+      asm volatile("" : "+a"(of[rb][ks]));
+    }
+    // padding rows: LSE = +inf makes P = 0
+    lrow[rb] = rvalid[rb] ? a.lse[(int64_t)hq[rb] * G.T + tok] * kLog2e : INFINITY;
+    drow[rb] = rvalid[rb] ? a.delta[(int64_t)hq[rb] * G.T + tok] : 0.0f;
+  }
+
+  // lane-constant LDS byte offsets within a stage (block offsets are immediates)
+  int koff[C::KS], voff[C::VS], toff[2][2];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = l32 * C::KROW + (((2 * ks + hl) ^ swz<C::KCH>(l32)) << 4);
+#pragma unroll
+  for (int ks = 0; ks < C::VS; ++ks) voff[ks] = C::KBYTES + l32 * C::VROW + (((2 * ks + hl) ^ swz<C::VCH>(l32)) << 4);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      toff[kb][h] = C::KBYTES + C::VBYTES + l32 * C::TROW + (((4 * kb + 2 * h + hl) ^ swz<8>(l32)) << 4);
+
+  const int pt0 = sp * a.ptiles_per_split;
+  const int np = max(0, min(a.ptiles, pt0 + a.ptiles_per_split) - pt0);
+  const int t_lo = m0 / g;
+  const int t_hi = (min(M, m0 + C::BM) - 1) / g;
+  const int ns = (sp == a.splits - 1) ? (t_hi / C::BN + 1) : 0;
+  const int nit = np + ns;
+
+  // global -> LDS for tile `it`: K and V rows (rows past the valid keys re-read the last valid
+  // row: finite data, masked out), packed K^T rows (slots past the keys hold zeros)
+  auto issue_tile = [&](int it, char* buf) {
+    const bool pr = it < np;
+    const int key0 = pr ? (pt0 + it) * C::BN : (it - np) * C::BN;
+    const int nvalid = min(C::BN, (pr ? G.P : R) - key0);
+    const uint16_t* kb = pr ? G.Kp + (int64_t)key0 * G.ldk + kvh * D
+                            : G.Ks + (int64_t)(tokb + key0) * G.ldk + kvh * D;
+    const uint16_t* vb = pr ? G.Vp + (int64_t)key0 * G.ldv + kvh * DV
+                            : G.Vs + (int64_t)(tokb + key0) * G.ldv + kvh * DV;
+    const uint16_t* tb = pr ? a.KTp + (int64_t)kvh * D * a.ppad + key0
+                            : a.KTs + (int64_t)kvh * D * a.tpad + a.spos[ri] + key0;
+    const int64_t tld = pr ? a.ppad : a.tpad;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recompute per tile rather than pin registers for the whole loop
+#pragma unroll
+    for (int u = 0; u < C::KINS; ++u) {
+      const int ins = wv * C::KINS + u;
+      const int row = ins * (64 / C::KCH) + ln / C::KCH;
+      const int c = (ln % C::KCH) ^ swz<C::KCH>(row);
+      lds_dma16(kb + (int64_t)min(row, nvalid - 1) * G.ldk + c * 8, buf + ins * 1024);
+    }
+#pragma unroll
+    for (int u = 0; u < C::VINS; ++u) {
+      const int ins = wv * C::VINS + u;
+      const int row = ins * (64 / C::VCH) + ln / C::VCH;
+      const int c = (ln % C::VCH) ^ swz<C::VCH>(row);
+      lds_dma16(vb + (int64_t)min(row, nvalid - 1) * G.ldv + c * 8, buf + C::KBYTES + ins * 1024);
+    }
+#pragma unroll
+    for (int u = 0; u < C::TINS; ++u) {
+      const int ins = wv * C::TINS + u;
+      const int row = ins * 8 + (ln >> 3);
+      const int c = (ln & 7) ^ swz<8>(row);
+      lds_dma16(tb + (int64_t)row * tld + c * 8, buf + C::KBYTES + C::VBYTES + ins * 1024);
+    }
+  };
+
+  f32x16 dq[C::RB][C::DB];
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+    for (int b = 0; b < C::DB; ++b) dq[rb][b] = f32x16{};
+  const float c2 = G.scale_log2;
+
+  auto compute = [&](const char* buf, bool masked, int key0, int nvalid, bool causal) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // S^T = K Q^T, then dP^T = V dO^T, for both row blocks (each fragment feeds two MFMAs)
+      f32x16 st[C::RB], dp[C::RB];
+      {
+        bf16x8 kf[C::KS];
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) kf[ks] = lds_b128_at(buf, kb * 32 * C::KROW + koff[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) {
+          st[rb] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) st[rb] = mfma32(kf[ks], qf[rb][ks], st[rb]);
+        }
+      }
+      {
+        bf16x8 vf[C::VS];
+#pragma unroll
+        for (int ks = 0; ks < C::VS; ++ks) vf[ks] = lds_b128_at(buf, kb * 32 * C::VROW + voff[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) {
+          dp[rb] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < C::VS; ++ks) dp[rb] = mfma32(vf[ks], of[rb][ks], dp[rb]);
+        }
+      }
+      if (__builtin_expect(masked, 0)) {
+        asm volatile("");  // a real (wave-uniform) branch, not per-element selects
+        // register r holds tile key kb*32 + 8(r/4) + 4hl + r%4: visible iff below nvalid and
+        // (causal tiles) key0 + key <= the row's token. Hidden keys get S = -inf, so P = 0.
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) {
+          const int lim = min(nvalid, causal ? trow[rb] - key0 + 1 : nvalid) - kb * 32 - 4 * hl;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st[rb][r] = (8 * (r >> 2) + (r & 3)) < lim ? st[rb][r] : -INFINITY;
+        }
+      }
+      // dS = P (dP - Delta), as the bf16 B operands of dQ^T += K^T dS^T
+      bf16x8 db[C::RB][2];
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = fast_exp2(__builtin_fmaf(st[rb][r], c2, -lrow[rb]));
+          st[rb][r] = pv * (dp[rb][r] - drow[rb]);
+        }
+        db[rb][0] = c_regs_to_bf16x8(st[rb], 0);
+        db[rb][1] = c_regs_to_bf16x8(st[rb], 8);
+      }
+      // K^T fragments: one 16-byte read of packed slots each, feeding two MFMAs
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 tf[C::DB];
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b) tf[b] = lds_b128_at(buf, b * 32 * C::TROW + toff[kb][h]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+          for (int rb = 0; rb < C::RB; ++rb) dq[rb][b] = mfma32(tf[b], db[rb][h], dq[rb][b]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  char* const st0 = smem;
+  char* const st1 = smem + C::STAGE;
+  char* const st2 = smem + 2 * C::STAGE;
+  constexpr int kPerTile = C::KINS + C::VINS + C::TINS;
+  if (nit > 0) issue_tile(0, st0);
+  if (nit > 1) issue_tile(1, st1);
+  for (int it = 0; it < nit; it += 3) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int t = it + j;
+      if (t >= nit) break;
+      char* cur = j == 0 ? st0 : (j == 1 ? st1 : st2);
+      char* nxt = j == 0 ? st2 : (j == 1 ? st0 : st1);
+      if (t + 1 < nit) wait_vmem_le<kPerTile>();
+      else wait_vmem();
+      __syncthreads();
+      if (t + 2 < nit) issue_tile(t + 2, nxt);
+      const bool sfx = t >= np;
+      const int key0 = sfx ? (t - np) * C::BN : (pt0 + t) * C::BN;
+      const int nvalid = min(C::BN, (sfx ? R : G.P) - key0);
+      const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
+      compute(cur, causal || nvalid < C::BN, key0, nvalid, causal);
+    }
+  }
+
+  // C layout of dQ^T: lane holds row (lane & 31), dims 32b + 8(r/4) + 4hl + r%4
+  const float sc = G.scale;
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb) {
+    if (!rvalid[rb]) continue;
+    const int64_t tok = tokb + trow[rb];
+    if (a.splits == 1) {
+      uint16_t* dst = a.dQ + (tok * G.Hq + hq[rb]) * D + 4 * hl;
+#pragma unroll
+      for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x2 v = {pack_bf16x2(dq[rb][b][4 * q] * sc, dq[rb][b][4 * q + 1] * sc),
+                           pack_bf16x2(dq[rb][b][4 * q + 2] * sc, dq[rb][b][4 * q + 3] * sc)};
+          *reinterpret_cast<u32x2*>(dst + b * 32 + 8 * q) = v;
+        }
+    } else {
+      float* dst = a.dq_part + (((int64_t)sp * G.T + tok) * G.Hq + hq[rb]) * D + 4 * hl;
+#pragma unroll
+      for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {dq[rb][b][4 * q], dq[rb][b][4 * q + 1], dq[rb][b][4 * q + 2], dq[rb][b][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(dst + b * 32 + 8 * q) = v;
+        }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void replay_bwd_dq_reduce(BwdArgs a) {
+  const AttnGeom& G = a.geo;
+  const int64_t n4 = (int64_t)G.T * G.Hq * D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n4) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.splits; ++s) acc += reinterpret_cast<const f32x4*>(a.dq_part)[(int64_t)s * n4 + idx];
+  acc *= G.scale;
+  const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  reinterpret_cast<u32x2*>(a.dQ)[idx] = v;
+}
+
+template <int D, int DV>
+hipError_t dq_go(BwdArgs& a, hipStream_t st) {
+  const AttnGeom& G = a.geo;
+  const long long W = (long long)a.qtiles * G.Hkv * a.splits;
+  if (W == 0) return hipSuccess;
+  hipError_t e;
+  // dimension-major packed K of the prompt and of every response (dQ^T = K^T dS^T operand)
+  PackArgs p;
+  p.src = G.Kp;
+  p.ld = G.ldk;
+  p.dim = D;
+  p.heads = G.Hkv;
+  p.out_ld = a.ppad;
+  p.cols = a.ppad;
+  p.out = const_cast<uint16_t*>(a.KTp);
+  p.nseg = 1;
+  p.row0[0] = 0;
+  p.n[0] = G.P;
+  p.col0[0] = 0;
+  if (G.P > 0 && (e = launch_pack_keys_t(p, st)) != hipSuccess) return e;
+  p.src = G.Ks;
+  p.out_ld = a.tpad;
+  p.cols = a.tpad;
+  p.out = const_cast<uint16_t*>(a.KTs);
+  p.nseg = G.n_resp;
+  for (int i = 0; i < G.n_resp; ++i) {
+    p.row0[i] = G.tok0[i];
+    p.n[i] = G.tok0[i + 1] - G.tok0[i];
+    p.col0[i] = a.spos[i];
+  }
+  if ((e = launch_pack_keys_t(p, st)) != hipSuccess) return e;
+  timer_mark(LS_KERNEL_DQ, st, false);
+  hipLaunchKernelGGL((replay_bwd_dq<D, DV>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(256), 0, st, a);
+  timer_mark(LS_KERNEL_DQ, st, true);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.splits > 1) {
+    const long long n4 = (long long)G.T * G.Hq * D / 4;
+    hipLaunchKernelGGL((replay_bwd_dq_reduce<D>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq(BwdArgs& a, int Dqk, int Dv, hipStream_t st) {
+  if (Dqk == 64 && Dv == 64) return dq_go<64, 64>(a, st);
+  if (Dqk == 128 && Dv == 128) return dq_go<128, 128>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lsr

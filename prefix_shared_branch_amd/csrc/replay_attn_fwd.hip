@@ -51,7 +51,7 @@ __device__ __forceinline__ float max3f(float a, float b, float c) { return __bui
 // with a commutative operation gives both lanes the same bits.
 __device__ __forceinline__ float pair_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -123,42 +123,58 @@ __global__ __launch_bounds__(256, 1) void replay_fwd(FwdArgs a) {
   const int ns = (sp == a.splits - 1) ? (t_hi / C::BN + 1) : 0;
   const int nit = np + ns;
 
+  // Per-lane byte offsets of the direct loads within a full tile (32-bit, added to a wave-uniform
+  // tile base): K rows are key-major (1024 / KROW rows per 1 KB instruction), packed V^T rows
+  // are dimension-major (8 rows of 128 bytes per instruction).
+  uint32_t kdo[C::KINS], vdo[C::VINS];
+#pragma unroll
+  for (int u = 0; u < C::KINS; ++u) {
+    const int row = (wv * C::KINS + u) * (64 / C::KCH) + lane / C::KCH;
+    kdo[u] = (uint32_t)(row * G.ldk * 2 + (((lane % C::KCH) ^ swz<C::KCH>(row)) << 4));
+  }
+#pragma unroll
+  for (int u = 0; u < C::VINS; ++u) {
+    const int row = (wv * C::VINS + u) * 8 + (lane >> 3);
+    vdo[u] = (uint32_t)(row * a.ppad * 2 + (((lane & 7) ^ swz<8>(row)) << 4));
+  }
+
   // global -> LDS for tile `it` into stage buffer `buf`
   auto issue_tile = [&](int it, char* buf) {
-    const uint16_t* kb;
-    const uint16_t* vb;
-    int nvalid;
     if (it < np) {
       const int key0 = (pt0 + it) * C::BN;
-      nvalid = min(C::BN, G.P - key0);
-      kb = G.Kp + (int64_t)key0 * G.ldk + kvh * D;
-      vb = a.VTp + (int64_t)kvh * DV * a.ppad + key0;
-    } else {
-      const int key0 = (it - np) * C::BN;
-      nvalid = min(C::BN, R - key0);
-      kb = G.Ks + (int64_t)(tokb + key0) * G.ldk + kvh * D;
-      vb = a.VTs + (int64_t)kvh * DV * a.tpad + a.spos[ri] + key0;
+      const int nvalid = min(C::BN, G.P - key0);
+      const char* kb = reinterpret_cast<const char*>(G.Kp + (int64_t)key0 * G.ldk + kvh * D);
+      const char* vb = reinterpret_cast<const char*>(a.VTp + (int64_t)kvh * DV * a.ppad + key0);
+      if (nvalid == C::BN) {
+#pragma unroll
+        for (int u = 0; u < C::KINS; ++u) lds_dma16(kb + kdo[u], buf + (wv * C::KINS + u) * 1024);
+#pragma unroll
+        for (int u = 0; u < C::VINS; ++u) lds_dma16(vb + vdo[u], buf + C::KBYTES + (wv * C::VINS + u) * 1024);
+        return;
+      }
     }
-    const int64_t vld = it < np ? a.ppad : a.tpad;
-    // an opaque copy of the lane id: the per-lane row/chunk arithmetic below is redone for every
-    // tile (a few VALU ops) instead of being hoisted out of the tile loop into pinned registers
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    // K: each 1 KB instruction fills 1024 / KROW rows; rows past the valid keys re-read the last
-    // valid row (finite data, masked out of the softmax)
+    // ragged prompt tail or response keys: rows past the valid keys re-read the last valid row
+    // (finite data, masked out of the softmax); packed V^T slots past the keys hold zeros
+    const bool pr = it < np;
+    const int key0 = pr ? (pt0 + it) * C::BN : (it - np) * C::BN;
+    const int nvalid = min(C::BN, (pr ? G.P : R) - key0);
+    const uint16_t* kb = pr ? G.Kp + (int64_t)key0 * G.ldk + kvh * D
+                            : G.Ks + (int64_t)(tokb + key0) * G.ldk + kvh * D;
+    const uint16_t* vb = pr ? a.VTp + (int64_t)kvh * DV * a.ppad + key0
+                            : a.VTs + (int64_t)kvh * DV * a.tpad + a.spos[ri] + key0;
+    const int64_t vld = pr ? a.ppad : a.tpad;
 #pragma unroll
     for (int u = 0; u < C::KINS; ++u) {
       const int ins = wv * C::KINS + u;
-      const int row = ins * (64 / C::KCH) + ln / C::KCH;
-      const int c = (ln % C::KCH) ^ swz<C::KCH>(row);
+      const int row = ins * (64 / C::KCH) + lane / C::KCH;
+      const int c = (lane % C::KCH) ^ swz<C::KCH>(row);
       lds_dma16(kb + (int64_t)min(row, nvalid - 1) * G.ldk + c * 8, buf + ins * 1024);
     }
-    // V^T: 8 dim rows of 128 bytes per instruction; slots past the keys hold zeros
 #pragma unroll
     for (int u = 0; u < C::VINS; ++u) {
       const int ins = wv * C::VINS + u;
-      const int row = ins * 8 + (ln >> 3);
-      const int c = (ln & 7) ^ swz<8>(row);
+      const int row = ins * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz<8>(row);
       lds_dma16(vb + (int64_t)row * vld + c * 8, buf + C::KBYTES + ins * 1024);
     }
   };
@@ -174,32 +190,60 @@ __global__ __launch_bounds__(256, 1) void replay_fwd(FwdArgs a) {
   }
   const float c2 = G.scale_log2;
 
-  auto compute = [&](int it, const char* buf) {
-    int key0, nvalid;
-    bool sfx;
-    if (it < np) {
-      key0 = (pt0 + it) * C::BN;
-      nvalid = min(C::BN, G.P - key0);
-      sfx = false;
-    } else {
-      key0 = (it - np) * C::BN;
-      nvalid = min(C::BN, R - key0);
-      sfx = true;
+  // online softmax of one 32-row block (one query row per lane; the other half-wave holds the
+  // row's other keys); returns the probabilities as the two bf16 B operands of the PV product
+  auto softmax = [&](int rb, f32x16& st, bf16x8& p0, bf16x8& p1) {
+    float mx = __builtin_elementwise_maximum(st[0], st[1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, st[r]);
+    mx = pair_max(mx) * c2;
+    const bool move = mx > mu[rb] + C::kStale;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(move) != 0, 0)) {
+      asm volatile("");  // rare: a real branch, never speculated into unconditional multiplies
+      const float mnew = move ? mx : mu[rb];
+      const float alpha = move ? fast_exp2(mu[rb] - mnew) : 1.0f;   // 0 on a row's first visible keys
+      mu[rb] = mnew;
+      l_run[rb] *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) o[rb][nb] *= alpha;
     }
-    const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
-    const bool masked = causal || nvalid < C::BN;
+    const float msub = mu[rb] == -INFINITY ? 0.0f : mu[rb];
+    // the row sum is taken in fp32 (the LSE must hold to ~1e-6 even over a few keys)
+    float ls0 = 0.0f, ls1 = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      st[r] = fast_exp2(__builtin_fmaf(st[r], c2, -msub));
+      st[r + 1] = fast_exp2(__builtin_fmaf(st[r + 1], c2, -msub));
+      ls0 += st[r];
+      ls1 += st[r + 1];
+    }
+    l_run[rb] += ls0 + ls1;
+    p0 = c_regs_to_bf16x8(st, 0);
+    p1 = c_regs_to_bf16x8(st, 8);
+  };
+
+  auto compute = [&](const char* buf, bool masked, int key0, int nvalid, bool causal) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      // S^T = K Q^T for both row blocks; each K fragment feeds two MFMAs
+      // S^T = K Q^T for both row blocks; every K fragment feeds two MFMAs
+      bf16x8 kf[C::KS];
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) kf[ks] = lds_b128_at(buf, kb * 32 * C::KROW + koff[ks]);
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 st[C::RB];
 #pragma unroll
-      for (int rb = 0; rb < C::RB; ++rb) st[rb] = f32x16{};
+      for (int rb = 0; rb < C::RB; ++rb) {
+        st[rb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 kf = lds_b128_at(buf, kb * 32 * C::KROW + koff[ks]);
-#pragma unroll
-        for (int rb = 0; rb < C::RB; ++rb) st[rb] = mfma32(kf, qf[rb][ks], st[rb]);
+        for (int ks = 0; ks < C::KS; ++ks) st[rb] = mfma32(kf[ks], qf[rb][ks], st[rb]);
       }
+      // V^T fragments (one 16-byte read of packed slots each) arrive while the scores are formed
+      bf16x8 vf[2][C::NB];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) vf[h][nb] = lds_b128_at(buf, nb * 32 * C::VTROW + voff[kb][h]);
+      __builtin_amdgcn_sched_barrier(0);
       if (__builtin_expect(masked, 0)) {
         asm volatile("");  // keeps this a real (wave-uniform) branch instead of per-element selects
         // register r holds tile key kb*32 + 8(r/4) + 4hl + r%4; it is visible iff that key is below
@@ -211,48 +255,23 @@ __global__ __launch_bounds__(256, 1) void replay_fwd(FwdArgs a) {
           for (int r = 0; r < 16; ++r) st[rb][r] = (8 * (r >> 2) + (r & 3)) < lim ? st[rb][r] : -INFINITY;
         }
       }
-      // online softmax, one query row per lane (the other half-wave holds the row's other keys)
+      // row block 0's softmax runs under row block 1's score MFMAs, row block 1's under
+      // row block 0's PV MFMAs
       bf16x8 pb[C::RB][2];
-#pragma unroll
-      for (int rb = 0; rb < C::RB; ++rb) {
-        float mx = max3f(st[rb][0], st[rb][1], st[rb][2]);
-#pragma unroll
-        for (int r = 3; r < 15; r += 2) mx = max3f(mx, st[rb][r], st[rb][r + 1]);
-        mx = __builtin_fmaxf(mx, st[rb][15]);
-        mx = pair_max(mx) * c2;
-        const bool move = mx > mu[rb] + C::kStale;
-        if (__builtin_expect(__builtin_amdgcn_ballot_w64(move) != 0, 0)) {
-          asm volatile("");  // rare: a real branch, never speculated into unconditional multiplies
-          const float mnew = move ? mx : mu[rb];
-          const float alpha = move ? fast_exp2(mu[rb] - mnew) : 1.0f;   // 0 on a row's first visible keys
-          mu[rb] = mnew;
-          l_run[rb] *= alpha;
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) o[rb][nb] *= alpha;
-        }
-        const float msub = mu[rb] == -INFINITY ? 0.0f : mu[rb];
-        // probabilities; the row sum is taken in fp32 (the LSE must hold to ~1e-5 even over a few keys)
-        float ls0 = 0.0f, ls1 = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          st[rb][r] = fast_exp2(__builtin_fmaf(st[rb][r], c2, -msub));
-          st[rb][r + 1] = fast_exp2(__builtin_fmaf(st[rb][r + 1], c2, -msub));
-          ls0 += st[rb][r];
-          ls1 += st[rb][r + 1];
-        }
-        l_run[rb] += ls0 + ls1;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) pb[rb][h] = c_regs_to_bf16x8(st[rb], 8 * h);
-      }
-      // O^T += V^T P^T; each V^T fragment (one 16-byte read of packed slots) feeds two MFMAs
+      softmax(0, st[0], pb[0][0], pb[0][1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          const bf16x8 vf = lds_b128_at(buf, nb * 32 * C::VTROW + voff[kb][h]);
+        for (int nb = 0; nb < C::NB; ++nb) o[0][nb] = mfma32(vf[h][nb], pb[0][h], o[0][nb]);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(1, st[1], pb[1][0], pb[1][1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int rb = 0; rb < C::RB; ++rb) o[rb][nb] = mfma32(vf, pb[rb][h], o[rb][nb]);
-        }
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) o[1][nb] = mfma32(vf[h][nb], pb[1][h], o[1][nb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -276,7 +295,11 @@ __global__ __launch_bounds__(256, 1) void replay_fwd(FwdArgs a) {
       else wait_vmem();
       __syncthreads();
       if (t + 2 < nit) issue_tile(t + 2, nxt);
-      compute(t, cur);
+      const bool sfx = t >= np;
+      const int key0 = sfx ? (t - np) * C::BN : (pt0 + t) * C::BN;
+      const int nvalid = min(C::BN, (sfx ? R : G.P) - key0);
+      const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
+      compute(cur, causal || nvalid < C::BN, key0, nvalid, causal);
     }
   }
 
