@@ -46,6 +46,8 @@ int plan_for(const ls_attn_desc* d, int32_t n_resp, const int32_t* cu, int which
   const int64_t T = cu[n_resp];
   const int64_t g = d->Hq / d->Hkv;
   if (T * d->Hq > INT32_MAX || T * g > INT32_MAX / 2 || (int64_t)d->P + T > INT32_MAX / 2) return LS_ERR_UNSUPPORTED;
+  // the backward's packed query-row tiles use 32-bit per-lane offsets: Dqk rows of T * g slots
+  if ((T * g + 64) * (int64_t)(d->Dqk > d->Dv ? d->Dqk : d->Dv) * 2 > INT32_MAX) return LS_ERR_UNSUPPORTED;
   if (!lsr::plan_attn(which, d->P, d->Hq, d->Hkv, d->Dqk, d->Dv, n_resp, cu, pl)) return LS_ERR_UNSUPPORTED;
   return LS_OK;
 }
@@ -170,6 +172,12 @@ int ls_replay_attn_bwd(void* stream, const ls_attn_desc* desc, const void* Kp, c
   a.ptiles_per_split = pl.ptiles_per_split;
   a.qtiles = pl.qtiles;
   for (int i = 0; i <= kMaxResp; ++i) a.tile0[i] = pl.tile0[i];
+  a.Qr = reinterpret_cast<uint16_t*>(ws + pl.off_qr);
+  a.dOr = reinterpret_cast<uint16_t*>(ws + pl.off_or);
+  a.QT = reinterpret_cast<uint16_t*>(ws + pl.off_qt);
+  a.dOT = reinterpret_cast<uint16_t*>(ws + pl.off_ot);
+  a.rowstat = reinterpret_cast<float*>(ws + pl.off_rs);
+  a.mpad = pl.mpad;
   a.KTp = reinterpret_cast<const uint16_t*>(ws + pl.off_c);
   a.KTs = reinterpret_cast<const uint16_t*>(ws + pl.off_d);
   a.ppad = pl.ppad;

@@ -93,6 +93,18 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
     off = align256(off + (size_t)Hkv * Dqk * pl->ppad * 2);
     pl->off_d = off;
     off = align256(off + (size_t)Hkv * Dqk * pl->tpad * 2);
+    // packed query rows of every kv head (dK/dV kernels)
+    pl->mpad = (T * g + 63) / 64 * 64;
+    pl->off_qr = off;
+    off = align256(off + (size_t)Hkv * pl->mpad * Dqk * 2);
+    pl->off_or = off;
+    off = align256(off + (size_t)Hkv * pl->mpad * Dv * 2);
+    pl->off_qt = off;
+    off = align256(off + (size_t)Hkv * pl->mpad * Dqk * 2);
+    pl->off_ot = off;
+    off = align256(off + (size_t)Hkv * pl->mpad * Dv * 2);
+    pl->off_rs = off;
+    off = align256(off + (size_t)Hkv * pl->mpad * 8);
   }
   pl->ws_bytes = off;
   return true;

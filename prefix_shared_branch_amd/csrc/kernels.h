@@ -50,10 +50,15 @@ struct AttnGeom {
   int32_t tok0[kMaxResp + 1];   // cu_seqlens
 };
 
-// Dimension-major repacking of key-major K or V rows (pack.hip): see launch_pack_keys_t.
+// Repacking of per-token rows (pack.hip). Logical row r of head h, dim d is read from
+//   src[(r / grp) * ld + (r % grp) * gstride + h * hstride + d]
+// (K or V rows: grp = 1, hstride = dim; GQA-packed query rows r = t * g + j of kv head h:
+// grp = g, ld = Hq * dim, gstride = dim, hstride = g * dim).
 struct PackArgs {
-  const uint16_t* src;   // [rows, ld] bf16; head h, dim d of row r at src[r * ld + h * dim + d]
+  const uint16_t* src;   // bf16
   int64_t ld;
+  int32_t grp;
+  int64_t gstride, hstride;
   int32_t dim, heads;    // dim a multiple of 64
   int32_t nseg;          // 1 .. kMaxResp segments
   int64_t row0[kMaxResp];  // first source row of each segment
@@ -63,7 +68,19 @@ struct PackArgs {
   int64_t out_ld;        // slots per output row (multiple of 64)
   int64_t cols;          // slots written per row (= out_ld)
 };
+// dimension-major, slot-permuted: out[(h * dim + d) * out_ld + col0_s + p] (see pack.hip)
 hipError_t launch_pack_keys_t(const PackArgs& a, hipStream_t st);
+// row-major: out[(h * out_ld + col0_s + r) * dim + d], zero rows past each segment's n_s rows
+hipError_t launch_pack_rows(const PackArgs& a, hipStream_t st);
+// per packed query row: {LSE * log2 e, Delta} as two floats; padding rows get {+inf, 0}
+struct RowStatArgs {
+  const float* lse;      // [Hq, T]
+  const float* delta;    // [Hq, T]
+  float* out;            // [Hkv, mpad, 2]
+  int32_t T, Hq, g, Hkv;
+  int64_t M, mpad;       // packed rows per kv head (T * g) and their padded count
+};
+hipError_t launch_pack_rowstats(const RowStatArgs& a, hipStream_t st);
 
 struct FwdArgs {
   AttnGeom geo;
@@ -94,6 +111,12 @@ struct BwdArgs {
   float* dVp;
   float* delta;         // workspace [Hq, T]: rowsum(dO * O)
   float* dq_part;       // workspace [S, T, Hq, Dqk] fp32 (S > 1)
+  uint16_t* Qr;         // packed query rows per kv head, row-major: [Hkv, mpad, Dqk]
+  uint16_t* dOr;        // [Hkv, mpad, Dv]
+  uint16_t* QT;         // dimension-major, slot-permuted: [Hkv * Dqk, mpad]
+  uint16_t* dOT;        // [Hkv * Dv, mpad]
+  float* rowstat;       // [Hkv, mpad, 2]: {LSE log2 e, Delta}
+  int64_t mpad;         // packed query rows per kv head (T * g) rounded up to 64
   const uint16_t* KTp;  // packed prompt K: [Hkv * Dqk, ppad] (pack.hip layout)
   const uint16_t* KTs;  // packed response K: [Hkv * Dqk, tpad], response i from slot spos[i]
   int64_t ppad, tpad;
@@ -114,8 +137,10 @@ struct AttnPlan {
   int ktile0[kMaxResp + 1];
   int64_t ppad, tpad;           // packed prompt / response key slots (multiples of 64)
   int spos[kMaxResp + 1];       // first packed slot of each response
+  int64_t mpad;                 // packed query rows per kv head, rounded up to 64
   size_t ws_bytes;
   size_t off_a, off_b, off_c, off_d;   // workspace sub-buffer offsets
+  size_t off_qr, off_or, off_qt, off_ot, off_rs;
 };
 
 // which: 0 fwd, 1 bwd exact, 2 bwd response-only. Returns false if (Dqk, Dv) has no kernel.
@@ -124,6 +149,8 @@ hipError_t launch_attn_fwd(FwdArgs& a, int Dqk, int Dv, hipStream_t st);
 hipError_t launch_attn_bwd(BwdArgs& a, int Dqk, int Dv, hipStream_t st);
 // dQ part of the backward (replay_attn_dq.hip): K packing, dQ kernel, split reduction
 hipError_t launch_bwd_dq(BwdArgs& a, int Dqk, int Dv, hipStream_t st);
+// dK/dV part (replay_attn_dkdv.hip): query-row packing, prompt and response dK/dV kernels
+hipError_t launch_bwd_dkdv(BwdArgs& a, int Dqk, int Dv, hipStream_t st);
 
 // Kernel timer hooks (timer.cpp): bracket a launch; no-ops unless the timer is armed for `kernel`
 // (an ls_kernel_id value).

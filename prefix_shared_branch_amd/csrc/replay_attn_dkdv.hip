@@ -1,0 +1,447 @@
+// Replay attention backward, dK/dV part, on gfx950. The prompt-side gradient is the d l / d z_P
+// term of the gradient decomposition in the LongStraw study notes (§2-2); serial replay adds it
+// into resident accumulators response after response (§2-1 step 4, §3-2 (4)), and each
+// accumulator element is owned by the prompt page it belongs to (§4-3 (2), page-owner dK/dV).
+//
+// With P = exp(S scale - LSE), dP = dO V^T, Delta = rowsum(dO * O), dS = P (dP - Delta):
+//   dV_j += sum_rows P_rj dO_r,   dK_j += scale sum_rows dS_rj Q_r.
+//
+// replay_bwd_dkdv: key-tile owner. One workgroup = 4 waves x 32 keys of one kv head (one wave per
+// SIMD); the wave keeps its keys' K and V fragments (AGPRs) and dK^T, dV^T accumulators for the
+// whole sweep over every query row that sees those keys, 32 GQA-packed rows per step. The rows
+// were repacked per kv head before the launch (pack.hip): row-major Q and dO (A operands of
+// S = Q K^T and dP = dO V^T) and dimension-major, slot-permuted Q^T and dO^T (A operands of
+// dV^T += dO^T P and dK^T += Q^T dS, whose B operands come straight from the S / dP accumulators),
+// plus each row's {LSE log2 e, Delta}. Per step all of them stream global -> LDS by direct DMA into
+// a three-stage ring of XOR-swizzled tiles, so every MFMA operand is one 16-byte LDS read.
+// Prompt keys: P and dS enter the dV / dK MFMAs as a bf16 hi/lo pair, so the fp32 accumulators keep
+// about 16 significant bits per term (one bf16 rounding would cost ~1.7e-3 relative error over
+// 10^6-10^7 terms); the sums are then added to dKp / dVp in place (each element is read and
+// written by exactly one workgroup per call). Response keys: causal, single bf16 operands, bf16
+// dKs / dVs stores.
+#include "common.h"
+#include "kernels.h"
+
+namespace lsr {
+
+namespace {
+
+template <int D, int DV>
+struct DkvCfg {
+  static constexpr int BN = 128;              // keys per workgroup (32 per wave)
+  static constexpr int BR = 32;               // query rows per step
+  static constexpr int QCH = D / 8;           // 16-byte chunks per Q row
+  static constexpr int OCH = DV / 8;
+  static constexpr int QROW = D * 2;
+  static constexpr int OROW = DV * 2;
+  static constexpr int TROW = BR * 2;         // bytes per packed Q^T / dO^T row of a step (32 slots)
+  static constexpr int QBYTES = BR * QROW;
+  static constexpr int OBYTES = BR * OROW;
+  static constexpr int QTBYTES = D * TROW;
+  static constexpr int OTBYTES = DV * TROW;
+  static constexpr int LDBYTES = BR * 8;      // {LSE log2 e, Delta} per row
+  static constexpr int OFF_O = QBYTES;
+  static constexpr int OFF_QT = OFF_O + OBYTES;
+  static constexpr int OFF_OT = OFF_QT + QTBYTES;
+  static constexpr int OFF_LD = OFF_OT + OTBYTES;
+  static constexpr int STAGE = OFF_LD + 1024;  // row statistics padded to 1 KB
+  static constexpr int NSTAGE = 3;
+  static constexpr int QINS = QBYTES / 4096;  // 1 KB direct loads per wave per step
+  static constexpr int OINS = OBYTES / 4096;
+  static constexpr int QTINS = QTBYTES / 4096;
+  static constexpr int OTINS = OTBYTES / 4096;
+  static constexpr int KS = D / 16;
+  static constexpr int VS = DV / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int VB = DV / 32;
+};
+
+// swizzle of the 16-byte chunks of 64-byte rows (4 chunks): conflict-free 16-byte reads of one
+// chunk column by 8 consecutive rows
+__device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
+
+// x = hi + lo with hi = bf16 truncation of x (exact split), lo rounded to bf16; 8 consecutive
+// accumulator registers r0..r0+7 -> two bf16x8 operands
+__device__ __forceinline__ void split8(const f32x16& c, int r0, bf16x8& hi, bf16x8& lo) {
+  u32x4 h;
+  bf16x8 l;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t a = __float_as_uint(c[r0 + 2 * j]) & 0xffff0000u;
+    const uint32_t b = __float_as_uint(c[r0 + 2 * j + 1]) & 0xffff0000u;
+    h[j] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+    l[2 * j] = (__bf16)(c[r0 + 2 * j] - __uint_as_float(a));
+    l[2 * j + 1] = (__bf16)(c[r0 + 2 * j + 1] - __uint_as_float(b));
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = l;
+}
+
+template <int D, int DV, bool PROMPT>
+__global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
+  using C = DkvCfg<D, DV>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE];
+
+  const AttnGeom& G = a.geo;
+  const int nk = PROMPT ? a.ktiles_prompt : a.ktile0[G.n_resp];
+  const int W = nk * G.Hkv;
+  const int per_xcd = (W + 7) >> 3;
+  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (w >= W) return;
+  const int kvh = w / nk;
+  const int kt = w - kvh * nk;
+  const int g = G.g;
+
+  int key0, nkeys, tokb = 0, R = 0, row_begin, row_end;
+  if (PROMPT) {
+    key0 = kt * C::BN;
+    nkeys = min(C::BN, G.P - key0);
+    row_begin = 0;
+    row_end = G.T * g;
+  } else {
+    int ri = 0;
+    while (kt >= a.ktile0[ri + 1]) ++ri;
+    tokb = G.tok0[ri];
+    R = G.tok0[ri + 1] - tokb;
+    key0 = (kt - a.ktile0[ri]) * C::BN;  // within the response
+    nkeys = min(C::BN, R - key0);
+    // steps start on 32-row boundaries of the packed rows (the slot permutation of the packed
+    // Q^T / dO^T repeats every 16 rows); rows of other responses are masked below
+    row_begin = ((tokb + key0) * g) & ~(C::BR - 1);
+    row_end = (tokb + R) * g;
+  }
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+  const int mykey = wv * 32 + l32;  // within the tile
+  const bool kvalid = mykey < nkeys;
+
+  // K, V fragments of this wave's 32 keys (B operands of S = Q K^T and dP = dO V^T), in AGPRs
+  bf16x8 kf[C::KS], vf[C::VS];
+  {
+    const uint16_t* kr = PROMPT ? G.Kp + (int64_t)(key0 + mykey) * G.ldk + kvh * D
+                                : G.Ks + (int64_t)(tokb + key0 + mykey) * G.ldk + kvh * D;
+    const uint16_t* vr = PROMPT ? G.Vp + (int64_t)(key0 + mykey) * G.ldv + kvh * DV
+                                : G.Vs + (int64_t)(tokb + key0 + mykey) * G.ldv + kvh * DV;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      kf[ks] = kvalid ? ld_bf16x8(kr + ks * 16 + hl * 8) : zero_bf16x8();
+      asm volatile("" : "+a"(kf[ks]));
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::VS; ++ks) {
+      vf[ks] = kvalid ? ld_bf16x8(vr + ks * 16 + hl * 8) : zero_bf16x8();
+      asm volatile("" : "+a"(vf[ks]));
+    }
+  }
+
+  f32x16 dk[C::DB], dv[C::VB];
+#pragma unroll
+  for (int b = 0; b < C::DB; ++b) dk[b] = f32x16{};
+#pragma unroll
+  for (int b = 0; b < C::VB; ++b) dv[b] = f32x16{};
+
+  // lane-constant LDS byte offsets within a stage
+  int qoff[C::KS], ooff[C::VS], toff[2];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) qoff[ks] = l32 * C::QROW + (((2 * ks + hl) ^ swz<C::QCH>(l32)) << 4);
+#pragma unroll
+  for (int ks = 0; ks < C::VS; ++ks) ooff[ks] = C::OFF_O + l32 * C::OROW + (((2 * ks + hl) ^ swz<C::OCH>(l32)) << 4);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) toff[h] = l32 * C::TROW + (((2 * h + hl) ^ swz4(l32)) << 4);
+
+  // per-lane global byte offsets of the direct loads within one step's slabs
+  const int64_t mpad = a.mpad;
+  const char* Qr = reinterpret_cast<const char*>(a.Qr + (int64_t)kvh * mpad * D);
+  const char* Or = reinterpret_cast<const char*>(a.dOr + (int64_t)kvh * mpad * DV);
+  const char* QT = reinterpret_cast<const char*>(a.QT + (int64_t)kvh * D * mpad);
+  const char* OT = reinterpret_cast<const char*>(a.dOT + (int64_t)kvh * DV * mpad);
+  const char* LD = reinterpret_cast<const char*>(a.rowstat + (int64_t)kvh * mpad * 2);
+  // lane-constant byte offsets of the direct loads within one step's slabs (the slab bases are
+  // wave-uniform): Q / dO rows row-major with XOR-swizzled chunks, Q^T / dO^T rows of 32 slots
+  uint32_t qdo[C::QINS], odo[C::OINS], qtdo[C::QTINS], otdo[C::OTINS];
+#pragma unroll
+  for (int u = 0; u < C::QINS; ++u) {
+    const int row = (wv * C::QINS + u) * (64 / C::QCH) + lane / C::QCH;
+    qdo[u] = (uint32_t)(row * C::QROW + (((lane % C::QCH) ^ swz<C::QCH>(row)) << 4));
+  }
+#pragma unroll
+  for (int u = 0; u < C::OINS; ++u) {
+    const int row = (wv * C::OINS + u) * (64 / C::OCH) + lane / C::OCH;
+    odo[u] = (uint32_t)(row * C::OROW + (((lane % C::OCH) ^ swz<C::OCH>(row)) << 4));
+  }
+#pragma unroll
+  for (int u = 0; u < C::QTINS; ++u) {
+    const int row = (wv * C::QTINS + u) * 16 + (lane >> 2);
+    qtdo[u] = (uint32_t)(row * mpad * 2 + (((lane & 3) ^ swz4(row)) << 4));
+  }
+#pragma unroll
+  for (int u = 0; u < C::OTINS; ++u) {
+    const int row = (wv * C::OTINS + u) * 16 + (lane >> 2);
+    otdo[u] = (uint32_t)(row * mpad * 2 + (((lane & 3) ^ swz4(row)) << 4));
+  }
+  const uint32_t ldo = (uint32_t)lane * 4;
+  auto issue_step = [&](int m0, char* buf) {
+    const char* q = Qr + (int64_t)m0 * C::QROW;
+    const char* o = Or + (int64_t)m0 * C::OROW;
+    const char* qt = QT + (int64_t)m0 * 2;
+    const char* ot = OT + (int64_t)m0 * 2;
+#pragma unroll
+    for (int u = 0; u < C::QINS; ++u) lds_dma16(q + qdo[u], buf + (wv * C::QINS + u) * 1024);
+#pragma unroll
+    for (int u = 0; u < C::OINS; ++u) lds_dma16(o + odo[u], buf + C::OFF_O + (wv * C::OINS + u) * 1024);
+#pragma unroll
+    for (int u = 0; u < C::QTINS; ++u) lds_dma16(qt + qtdo[u], buf + C::OFF_QT + (wv * C::QTINS + u) * 1024);
+#pragma unroll
+    for (int u = 0; u < C::OTINS; ++u) lds_dma16(ot + otdo[u], buf + C::OFF_OT + (wv * C::OTINS + u) * 1024);
+    // row statistics: 32 rows x 8 bytes, one 4-byte load per lane of the first wave
+    if (wv == 0)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(LD + (int64_t)m0 * 8 + ldo),
+                                       (__attribute__((address_space(3))) void*)(buf + C::OFF_LD), 4, 0, 0);
+  };
+
+  const float c2 = G.scale_log2;
+  const int nsteps = row_end > row_begin ? (row_end - row_begin + C::BR - 1) / C::BR : 0;
+
+  // One step: S and dP MFMAs; P (and its hi/lo split) under the dP MFMAs; dV MFMAs; dS (and its
+  // split) under the dV MFMAs; dK MFMAs. Fragments are read in batches ahead of their MFMAs.
+  auto compute = [&](const char* buf, int m0) {
+    // S[row][key] = Q K^T and dP = dO V^T: lane holds key (lane & 31), rows 8(r/4) + 4hl + r%4
+    f32x16 s, dp;
+    {
+      bf16x8 af[C::KS], bfr[C::VS];
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) af[ks] = lds_b128_at(buf, qoff[ks]);
+#pragma unroll
+      for (int ks = 0; ks < C::VS; ++ks) bfr[ks] = lds_b128_at(buf, ooff[ks]);
+      __builtin_amdgcn_sched_barrier(0);
+      s = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) s = mfma32(af[ks], kf[ks], s);
+      dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::VS; ++ks) dp = mfma32(bfr[ks], vf[ks], dp);
+    }
+    // row statistics of rows 8q + 4hl + 0..3: {l0, d0, l1, d1}, {l2, d2, l3, d3}
+    f32x4 st[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      st[q][0] = __builtin_bit_cast(f32x4, lds_b128_at(buf, C::OFF_LD + (8 * q + 4 * hl) * 8));
+      st[q][1] = __builtin_bit_cast(f32x4, lds_b128_at(buf, C::OFF_LD + (8 * q + 4 * hl) * 8 + 16));
+    }
+    // dO^T fragments for the dV MFMAs
+    bf16x8 ot[2][C::VB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < C::VB; ++b) ot[h][b] = lds_b128_at(buf, C::OFF_OT + b * 32 * C::TROW + toff[h]);
+    __builtin_amdgcn_sched_barrier(0);
+    // P = exp2(S scale log2 e - LSE log2 e), under the dP MFMAs
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int q = r >> 2, e = r & 3;
+      float pv = fast_exp2(__builtin_fmaf(s[r], c2, -st[q][e >> 1][2 * (e & 1)]));
+      if (!PROMPT) {
+        // causal within the response; rows of other responses see none of these keys
+        const int t = (m0 + 8 * q + 4 * hl + e) / g - tokb;
+        pv = (key0 + mykey <= t && t < R) ? pv : 0.0f;
+      }
+      s[r] = pv;
+    }
+    // dV^T[dv][key] += dO^T P (A operands: one 16-byte read of packed slots)
+    if (PROMPT) {
+      bf16x8 ph[2], pl[2];
+      split8(s, 0, ph[0], pl[0]);
+      split8(s, 8, ph[1], pl[1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int b = 0; b < C::VB; ++b) {
+          dv[b] = mfma32(ot[h][b], ph[h], dv[b]);
+          dv[b] = mfma32(ot[h][b], pl[h], dv[b]);
+        }
+    } else {
+      const bf16x8 p0 = c_regs_to_bf16x8(s, 0), p1 = c_regs_to_bf16x8(s, 8);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < C::VB; ++b) dv[b] = mfma32(ot[0][b], p0, dv[b]);
+#pragma unroll
+      for (int b = 0; b < C::VB; ++b) dv[b] = mfma32(ot[1][b], p1, dv[b]);
+    }
+    // Q^T fragments for the dK MFMAs
+    bf16x8 qt[2][C::DB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < C::DB; ++b) qt[h][b] = lds_b128_at(buf, C::OFF_QT + b * 32 * C::TROW + toff[h]);
+    __builtin_amdgcn_sched_barrier(0);
+    // dS = P (dP - Delta), under the dV MFMAs
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int q = r >> 2, e = r & 3;
+      dp[r] = s[r] * (dp[r] - st[q][e >> 1][2 * (e & 1) + 1]);
+    }
+    // dK^T[d][key] += Q^T dS
+    if (PROMPT) {
+      bf16x8 dh[2], dl[2];
+      split8(dp, 0, dh[0], dl[0]);
+      split8(dp, 8, dh[1], dl[1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b) {
+          dk[b] = mfma32(qt[h][b], dh[h], dk[b]);
+          dk[b] = mfma32(qt[h][b], dl[h], dk[b]);
+        }
+    } else {
+      const bf16x8 d0 = c_regs_to_bf16x8(dp, 0), d1 = c_regs_to_bf16x8(dp, 8);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < C::DB; ++b) dk[b] = mfma32(qt[0][b], d0, dk[b]);
+#pragma unroll
+      for (int b = 0; b < C::DB; ++b) dk[b] = mfma32(qt[1][b], d1, dk[b]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // three-stage ring over the steps (same protocol as the forward)
+  char* const st0 = smem;
+  char* const st1 = smem + C::STAGE;
+  char* const st2 = smem + 2 * C::STAGE;
+  constexpr int kPerStep = C::QINS + C::OINS + C::QTINS + C::OTINS;  // + 1 on wave 0
+  if (nsteps > 0) issue_step(row_begin, st0);
+  if (nsteps > 1) issue_step(row_begin + C::BR, st1);
+  for (int it = 0; it < nsteps; it += 3) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int t = it + j;
+      if (t >= nsteps) break;
+      char* cur = j == 0 ? st0 : (j == 1 ? st1 : st2);
+      char* nxt = j == 0 ? st2 : (j == 1 ? st0 : st1);
+      // wave 0 issues one extra load per step; waiting for <= kPerStep outstanding is then
+      // conservative for it (it also waits for part of the next step)
+      if (t + 1 < nsteps) wait_vmem_le<kPerStep>();
+      else wait_vmem();
+      __syncthreads();
+      if (t + 2 < nsteps) issue_step(row_begin + (t + 2) * C::BR, nxt);
+      compute(cur, row_begin + t * C::BR);
+    }
+  }
+
+  if (!kvalid) return;
+  // C layout of dV^T / dK^T: lane holds key (lane & 31), dims 32b + 8(r/4) + 4hl + r%4
+  const float sc = G.scale;
+  if (PROMPT) {
+    float* dvr = a.dVp + ((int64_t)(key0 + mykey) * G.Hkv + kvh) * DV + 4 * hl;
+    float* dkr = a.dKp + ((int64_t)(key0 + mykey) * G.Hkv + kvh) * D + 4 * hl;
+#pragma unroll
+    for (int b = 0; b < C::VB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4* ptr = reinterpret_cast<f32x4*>(dvr + b * 32 + 8 * q);
+        const f32x4 add = {dv[b][4 * q], dv[b][4 * q + 1], dv[b][4 * q + 2], dv[b][4 * q + 3]};
+        *ptr = *ptr + add;
+      }
+#pragma unroll
+    for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4* ptr = reinterpret_cast<f32x4*>(dkr + b * 32 + 8 * q);
+        const f32x4 add = {dk[b][4 * q] * sc, dk[b][4 * q + 1] * sc, dk[b][4 * q + 2] * sc, dk[b][4 * q + 3] * sc};
+        *ptr = *ptr + add;
+      }
+  } else {
+    const int64_t tok = tokb + key0 + mykey;
+    uint16_t* dvr = a.dVs + (tok * G.Hkv + kvh) * DV + 4 * hl;
+    uint16_t* dkr = a.dKs + (tok * G.Hkv + kvh) * D + 4 * hl;
+#pragma unroll
+    for (int b = 0; b < C::VB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 v = {pack_bf16x2(dv[b][4 * q], dv[b][4 * q + 1]), pack_bf16x2(dv[b][4 * q + 2], dv[b][4 * q + 3])};
+        *reinterpret_cast<u32x2*>(dvr + b * 32 + 8 * q) = v;
+      }
+#pragma unroll
+    for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 v = {pack_bf16x2(dk[b][4 * q] * sc, dk[b][4 * q + 1] * sc),
+                         pack_bf16x2(dk[b][4 * q + 2] * sc, dk[b][4 * q + 3] * sc)};
+        *reinterpret_cast<u32x2*>(dkr + b * 32 + 8 * q) = v;
+      }
+  }
+}
+
+template <int D, int DV>
+hipError_t dkdv_go(BwdArgs& a, hipStream_t st) {
+  const AttnGeom& G = a.geo;
+  hipError_t e;
+  // packed query rows of every kv head: row-major Q / dO, dimension-major Q^T / dO^T, statistics
+  const int64_t M = (int64_t)G.T * G.g;
+  PackArgs p;
+  p.ld = (int64_t)G.Hq * D;
+  p.grp = G.g;
+  p.gstride = D;
+  p.hstride = (int64_t)G.g * D;
+  p.dim = D;
+  p.heads = G.Hkv;
+  p.nseg = 1;
+  p.row0[0] = 0;
+  p.n[0] = (int32_t)M;
+  p.col0[0] = 0;
+  p.out_ld = a.mpad;
+  p.cols = a.mpad;
+  p.src = G.Q;
+  p.out = a.Qr;
+  if ((e = launch_pack_rows(p, st)) != hipSuccess) return e;
+  p.out = a.QT;
+  if ((e = launch_pack_keys_t(p, st)) != hipSuccess) return e;
+  p.ld = (int64_t)G.Hq * DV;
+  p.gstride = DV;
+  p.hstride = (int64_t)G.g * DV;
+  p.dim = DV;
+  p.src = a.dO;
+  p.out = a.dOr;
+  if ((e = launch_pack_rows(p, st)) != hipSuccess) return e;
+  p.out = a.dOT;
+  if ((e = launch_pack_keys_t(p, st)) != hipSuccess) return e;
+  RowStatArgs r;
+  r.lse = a.lse;
+  r.delta = a.delta;
+  r.out = a.rowstat;
+  r.T = G.T;
+  r.Hq = G.Hq;
+  r.g = G.g;
+  r.Hkv = G.Hkv;
+  r.M = M;
+  r.mpad = a.mpad;
+  if ((e = launch_pack_rowstats(r, st)) != hipSuccess) return e;
+
+  if (a.ktiles_prompt > 0) {
+    const long long W = (long long)a.ktiles_prompt * G.Hkv;
+    timer_mark(LS_KERNEL_DKDV_PROMPT, st, false);
+    hipLaunchKernelGGL((replay_bwd_dkdv<D, DV, true>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(256), 0, st, a);
+    timer_mark(LS_KERNEL_DKDV_PROMPT, st, true);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const long long W = (long long)a.ktile0[G.n_resp] * G.Hkv;
+  if (W > 0) {
+    hipLaunchKernelGGL((replay_bwd_dkdv<D, DV, false>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dkdv(BwdArgs& a, int Dqk, int Dv, hipStream_t st) {
+  if (Dqk == 64 && Dv == 64) return dkdv_go<64, 64>(a, st);
+  if (Dqk == 128 && Dv == 128) return dkdv_go<128, 128>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lsr

@@ -308,6 +308,9 @@ hipError_t dq_go(BwdArgs& a, hipStream_t st) {
   p.ld = G.ldk;
   p.dim = D;
   p.heads = G.Hkv;
+  p.grp = 1;
+  p.gstride = 0;
+  p.hstride = D;
   p.out_ld = a.ppad;
   p.cols = a.ppad;
   p.out = const_cast<uint16_t*>(a.KTp);

@@ -375,6 +375,9 @@ hipError_t fwd_go(FwdArgs& a, hipStream_t st) {
     p.ld = G.ldv;
     p.dim = DV;
     p.heads = G.Hkv;
+    p.grp = 1;
+    p.gstride = 0;
+    p.hstride = DV;
     p.nseg = 1;
     p.row0[0] = 0;
     p.n[0] = G.P;
@@ -391,6 +394,9 @@ hipError_t fwd_go(FwdArgs& a, hipStream_t st) {
     p.ld = G.ldv;
     p.dim = DV;
     p.heads = G.Hkv;
+    p.grp = 1;
+    p.gstride = 0;
+    p.hstride = DV;
     p.nseg = G.n_resp;
     for (int i = 0; i < G.n_resp; ++i) {
       p.row0[i] = G.tok0[i];
