@@ -198,7 +198,7 @@ def cpu_baseline(cfg, rows):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {"replay_bwd_dkdv_prompt": ["replay_attn_bwd.hip", "common.h", "kernels.h"]}
+KERNEL_SOURCES = {"replay_bwd_dkdv_prompt": ["replay_attn_dkdv.hip", "common.h", "kernels.h"]}
 
 
 def source_digest(kernel):

@@ -178,6 +178,8 @@ int ls_replay_attn_bwd(void* stream, const ls_attn_desc* desc, const void* Kp, c
   a.dOT = reinterpret_cast<uint16_t*>(ws + pl.off_ot);
   a.rowstat = reinterpret_cast<float*>(ws + pl.off_rs);
   a.mpad = pl.mpad;
+  a.scale_part = reinterpret_cast<float*>(ws + pl.off_sc);
+  a.scales = a.scale_part + lsr::kScaleBlocks * 4;
   a.KTp = reinterpret_cast<const uint16_t*>(ws + pl.off_c);
   a.KTs = reinterpret_cast<const uint16_t*>(ws + pl.off_d);
   a.ppad = pl.ppad;

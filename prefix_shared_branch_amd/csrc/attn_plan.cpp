@@ -105,6 +105,8 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
     off = align256(off + (size_t)Hkv * pl->mpad * Dv * 2);
     pl->off_rs = off;
     off = align256(off + (size_t)Hkv * pl->mpad * 8);
+    pl->off_sc = off;  // fp16 operand scales: partial maxima, then the 4 scales
+    off = align256(off + (size_t)(kScaleBlocks + 1) * 4 * 4);
   }
   pl->ws_bytes = off;
   return true;

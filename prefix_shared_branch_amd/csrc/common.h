@@ -27,6 +27,8 @@ namespace lsr {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -44,6 +46,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
@@ -140,6 +146,18 @@ template <int N>
 __device__ __forceinline__ void wait_vmem_le() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// 8 consecutive registers of a C tile (r0..r0+7) -> fp16 B/A operand (round to nearest even).
+__device__ __forceinline__ f16x8 c_regs_to_f16x8(const f32x16& c, int r0) {
+  f16x8 v;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (_Float16)c[r0 + j];
+  return v;
+}
+
+__device__ __forceinline__ f16x8 lds_h128_at(const char* base, int byte_off) {
+  return *reinterpret_cast<const LSR_LDS f16x8*>(reinterpret_cast<uintptr_t>(base + byte_off));
 }
 
 __device__ __forceinline__ bf16x8 lds_b128_at(const char* base, int byte_off) {

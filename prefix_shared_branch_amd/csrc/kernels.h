@@ -55,6 +55,7 @@ struct AttnGeom {
 // (K or V rows: grp = 1, hstride = dim; GQA-packed query rows r = t * g + j of kv head h:
 // grp = g, ld = Hq * dim, gstride = dim, hstride = g * dim).
 struct PackArgs {
+  const float* f16_scale;  // null: bf16 copy; else fp16 output of value * (*f16_scale) (pack_keys_t)
   const uint16_t* src;   // bf16
   int64_t ld;
   int32_t grp;
@@ -76,11 +77,30 @@ hipError_t launch_pack_rows(const PackArgs& a, hipStream_t st);
 struct RowStatArgs {
   const float* lse;      // [Hq, T]
   const float* delta;    // [Hq, T]
+  const float* scales;   // BwdScales (Delta is stored multiplied by the dS scale)
   float* out;            // [Hkv, mpad, 2]
   int32_t T, Hq, g, Hkv;
   int64_t M, mpad;       // packed rows per kv head (T * g) and their padded count
 };
 hipError_t launch_pack_rowstats(const RowStatArgs& a, hipStream_t st);
+
+// Power-of-two scales of the fp16 operands of the dK/dV products (pack.hip), in device memory:
+//   [0] s_dO: dO * s_dO has |values| <= 2^15      [1] s_Q: Q * s_Q has |values| <= 2^15
+//   [2] s_dS: 2^15 P (dP - Delta) * s_dS has |values| <= 2^15, from the bound
+//       |dP - Delta| <= 2 max_r |dO_r| max_j |V_j|  (Euclidean row norms)
+constexpr int kScaleBlocks = 512;
+struct ScaleArgs {
+  const uint16_t* dO;    // [T, Hq, Dv]
+  const uint16_t* Q;     // [T, Hq, Dqk]
+  const uint16_t* Vp;    // prompt V rows (stride ldv), may be null when P == 0
+  const uint16_t* Vs;    // response V rows (stride ldv)
+  int64_t ldv;
+  int64_t T, P;
+  int32_t Hq, Hkv, Dqk, Dv;
+  float* partial;        // [kScaleBlocks, 4]
+  float* scales;         // [4]
+};
+hipError_t launch_bwd_scales(const ScaleArgs& a, hipStream_t st);
 
 struct FwdArgs {
   AttnGeom geo;
@@ -115,7 +135,9 @@ struct BwdArgs {
   uint16_t* dOr;        // [Hkv, mpad, Dv]
   uint16_t* QT;         // dimension-major, slot-permuted: [Hkv * Dqk, mpad]
   uint16_t* dOT;        // [Hkv * Dv, mpad]
-  float* rowstat;       // [Hkv, mpad, 2]: {LSE log2 e, Delta}
+  float* rowstat;       // [Hkv, mpad, 2]: {LSE log2 e - 15, Delta * s_dS}
+  float* scale_part;    // [kScaleBlocks, 4] partial maxima
+  float* scales;        // [4] fp16 operand scales (see ScaleArgs)
   int64_t mpad;         // packed query rows per kv head (T * g) rounded up to 64
   const uint16_t* KTp;  // packed prompt K: [Hkv * Dqk, ppad] (pack.hip layout)
   const uint16_t* KTs;  // packed response K: [Hkv * Dqk, tpad], response i from slot spos[i]
@@ -140,7 +162,7 @@ struct AttnPlan {
   int64_t mpad;                 // packed query rows per kv head, rounded up to 64
   size_t ws_bytes;
   size_t off_a, off_b, off_c, off_d;   // workspace sub-buffer offsets
-  size_t off_qr, off_or, off_qt, off_ot, off_rs;
+  size_t off_qr, off_or, off_qt, off_ot, off_rs, off_sc;
 };
 
 // which: 0 fwd, 1 bwd exact, 2 bwd response-only. Returns false if (Dqk, Dv) has no kernel.

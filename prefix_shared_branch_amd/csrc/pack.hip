@@ -53,6 +53,7 @@ __global__ __launch_bounds__(256) void pack_keys_t(PackArgs a) {
     *reinterpret_cast<u32x4*>(&tile[key * kPackPitch + ch * 8]) = v;
   }
   __syncthreads();
+  const float f16s = a.f16_scale ? *a.f16_scale : 0.0f;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int q = threadIdx.x + u * 256;   // 64 dims x 8 chunks of 8 slots
@@ -62,7 +63,15 @@ __global__ __launch_bounds__(256) void pack_keys_t(PackArgs a) {
     for (int e = 0; e < 4; ++e) {
       const uint32_t lo = tile[slot_key(pc * 8 + 2 * e) * kPackPitch + d];
       const uint32_t hi = tile[slot_key(pc * 8 + 2 * e + 1) * kPackPitch + d];
-      w[e] = lo | (hi << 16);
+      if (a.f16_scale) {
+        // power-of-two scaling is exact; the fp16 rounding is to nearest even
+        f16x2 h;
+        h[0] = (_Float16)(bf16_to_f32((uint16_t)lo) * f16s);
+        h[1] = (_Float16)(bf16_to_f32((uint16_t)hi) * f16s);
+        w[e] = __builtin_bit_cast(uint32_t, h);
+      } else {
+        w[e] = lo | (hi << 16);
+      }
     }
     *reinterpret_cast<u32x4*>(a.out + ((int64_t)h * a.dim + d0 + d) * a.out_ld + c0 + pc * 8) =
         u32x4{w[0], w[1], w[2], w[3]};
@@ -93,13 +102,115 @@ __global__ __launch_bounds__(256) void pack_rowstats(RowStatArgs a) {
   if (m < a.M) {
     const int64_t t = m / a.g;
     const int h = k * a.g + (int)(m - t * a.g);
-    l = a.lse[(int64_t)h * a.T + t] * kLog2e;
-    d = a.delta[(int64_t)h * a.T + t];
+    // 2^15 P = exp2(S scale log2 e - (LSE log2 e - 15)); Delta in the units of the scaled dS
+    l = a.lse[(int64_t)h * a.T + t] * kLog2e - 15.0f;
+    d = a.delta[(int64_t)h * a.T + t] * a.scales[2];
   }
   reinterpret_cast<float2*>(a.out)[(int64_t)k * a.mpad + m] = make_float2(l, d);
 }
 
+// Partial maxima for the fp16 operand scales: {max |dO|, max row norm of dO, max |Q|, max row norm
+// of V over the prompt and the responses}. Rows are read 16 bytes per thread; a row's squared
+// norm is summed over the DIM / 8 consecutive lanes that hold it.
+template <int DIM>
+__device__ __forceinline__ void rows_max(const uint16_t* base, int64_t nrows, int64_t ld, int heads, int64_t start,
+                                         int64_t stride, float& amax, float& nmax) {
+  constexpr int TPR = DIM / 8;  // threads per row
+  const int64_t nchunks = nrows * heads * TPR;
+  for (int64_t c = start; c < nchunks; c += stride) {
+    const int64_t rh = c / TPR;
+    const int part = (int)(c - rh * TPR);
+    const int64_t r = rh / heads;
+    const int h = (int)(rh - r * heads);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(base + r * ld + (int64_t)h * DIM + part * 8);
+    float ss = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float x0 = bf16_lo(v[q]), x1 = bf16_hi(v[q]);
+      amax = __builtin_elementwise_maximum(amax, __builtin_elementwise_maximum(__builtin_fabsf(x0), __builtin_fabsf(x1)));
+      ss = __builtin_fmaf(x0, x0, __builtin_fmaf(x1, x1, ss));
+    }
+    // the TPR lanes of a row are consecutive (stride and start are multiples of TPR per lane group)
+#pragma unroll
+    for (int o = TPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    nmax = __builtin_elementwise_maximum(nmax, __builtin_sqrtf(ss));
+  }
+}
+
+template <int D, int DV>
+__global__ __launch_bounds__(256) void bwd_scale_partials(ScaleArgs a) {
+  const int64_t start = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float dummy = 0.0f;
+  rows_max<DV>(a.dO, a.T, (int64_t)a.Hq * DV, a.Hq, start, stride, v[0], v[1]);
+  rows_max<D>(a.Q, a.T, (int64_t)a.Hq * D, a.Hq, start, stride, v[2], dummy);
+  if (a.P > 0) rows_max<DV>(a.Vp, a.P, a.ldv, a.Hkv, start, stride, dummy, v[3]);
+  rows_max<DV>(a.Vs, a.T, a.ldv, a.Hkv, start, stride, dummy, v[3]);
+  __shared__ float red[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x = v[i];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = __builtin_elementwise_maximum(x, __shfl_xor(x, o, 64));
+    if ((threadIdx.x & 63) == 0) red[i][threadIdx.x >> 6] = x;
+  }
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    const int i = threadIdx.x;
+    a.partial[blockIdx.x * 4 + i] = __builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(red[i][0], red[i][1]), __builtin_elementwise_maximum(red[i][2], red[i][3]));
+  }
+}
+
+// exponent k (as the float 2^k) with x * 2^k <= 2^15, clamped; 1 for x == 0
+__device__ __forceinline__ float pow2_fit(float x) {
+  if (!(x > 0.0f)) return 1.0f;                       // zero: any scale; NaN: propagates anyway
+  int e;
+  (void)frexpf(x, &e);                               // x = m 2^e, 0.5 <= m < 1, so x < 2^e
+  const int k = min(60, max(-60, 15 - e));
+  return ldexpf(1.0f, k);
+}
+
+__global__ __launch_bounds__(256) void bwd_scale_final(ScaleArgs a) {
+  __shared__ float red[4][4];
+  float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int b = threadIdx.x; b < kScaleBlocks; b += 256)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_elementwise_maximum(v[i], a.partial[b * 4 + i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x = v[i];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = __builtin_elementwise_maximum(x, __shfl_xor(x, o, 64));
+    if ((threadIdx.x & 63) == 0) red[i][threadIdx.x >> 6] = x;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      m[i] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(red[i][0], red[i][1]),
+                                           __builtin_elementwise_maximum(red[i][2], red[i][3]));
+    a.scales[0] = pow2_fit(m[0]);
+    a.scales[1] = pow2_fit(m[2]);
+    // |2^15 P (dP - Delta)| <= 2^15 * 2 * max|dO_r| * max|V_j|: scale that bound down to 2^15
+    a.scales[2] = pow2_fit(2.0f * m[1] * m[3]) * 0x1p-15f;
+    a.scales[3] = 0.0f;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_bwd_scales(const ScaleArgs& a, hipStream_t st) {
+  if (a.Dqk == 64 && a.Dv == 64) hipLaunchKernelGGL((bwd_scale_partials<64, 64>), dim3(kScaleBlocks), dim3(256), 0, st, a);
+  else if (a.Dqk == 128 && a.Dv == 128) hipLaunchKernelGGL((bwd_scale_partials<128, 128>), dim3(kScaleBlocks), dim3(256), 0, st, a);
+  else return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_scale_final, dim3(1), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_rows(const PackArgs& a, hipStream_t st) {
   if (a.cols == 0) return hipSuccess;

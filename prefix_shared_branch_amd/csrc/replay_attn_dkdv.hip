@@ -14,11 +14,13 @@
 // dV^T += dO^T P and dK^T += Q^T dS, whose B operands come straight from the S / dP accumulators),
 // plus each row's {LSE log2 e, Delta}. Per step all of them stream global -> LDS by direct DMA into
 // a three-stage ring of XOR-swizzled tiles, so every MFMA operand is one 16-byte LDS read.
-// Prompt keys: P and dS enter the dV / dK MFMAs as a bf16 hi/lo pair, so the fp32 accumulators keep
-// about 16 significant bits per term (one bf16 rounding would cost ~1.7e-3 relative error over
-// 10^6-10^7 terms); the sums are then added to dKp / dVp in place (each element is read and
-// written by exactly one workgroup per call). Response keys: causal, single bf16 operands, bf16
-// dKs / dVs stores.
+// The dV / dK products run in fp16 (11 significant bits; bf16's 8 would cost ~1.7e-3 relative error
+// in the fp32 sums over 10^6-10^7 terms, fp16 ~2e-4) with exact power-of-two scaling so every
+// operand sits in fp16's normal range: 2^15 P (folded into the exponent), dO s_dO and Q s_Q
+// (s from max |dO|, max |Q|), and 2^15 P (dP - Delta) s_dS with s_dS from the bound
+// |dP - Delta| <= 2 max_r |dO_r| max_j |V_j| (pack.hip computes the scales per call). Prompt keys:
+// the sums are added to dKp / dVp in place (each element is read and written by exactly one
+// workgroup per call). Response keys: causal, bf16 dKs / dVs stores.
 #include "common.h"
 #include "kernels.h"
 
@@ -59,23 +61,6 @@ struct DkvCfg {
 // swizzle of the 16-byte chunks of 64-byte rows (4 chunks): conflict-free 16-byte reads of one
 // chunk column by 8 consecutive rows
 __device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
-
-// x = hi + lo with hi = bf16 truncation of x (exact split), lo rounded to bf16; 8 consecutive
-// accumulator registers r0..r0+7 -> two bf16x8 operands
-__device__ __forceinline__ void split8(const f32x16& c, int r0, bf16x8& hi, bf16x8& lo) {
-  u32x4 h;
-  bf16x8 l;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t a = __float_as_uint(c[r0 + 2 * j]) & 0xffff0000u;
-    const uint32_t b = __float_as_uint(c[r0 + 2 * j + 1]) & 0xffff0000u;
-    h[j] = __builtin_amdgcn_perm(b, a, 0x07060302u);
-    l[2 * j] = (__bf16)(c[r0 + 2 * j] - __uint_as_float(a));
-    l[2 * j + 1] = (__bf16)(c[r0 + 2 * j + 1] - __uint_as_float(b));
-  }
-  hi = __builtin_bit_cast(bf16x8, h);
-  lo = l;
-}
 
 template <int D, int DV, bool PROMPT>
 __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
@@ -205,8 +190,11 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
   const float c2 = G.scale_log2;
   const int nsteps = row_end > row_begin ? (row_end - row_begin + C::BR - 1) / C::BR : 0;
 
-  // One step: S and dP MFMAs; P (and its hi/lo split) under the dP MFMAs; dV MFMAs; dS (and its
-  // split) under the dV MFMAs; dK MFMAs. Fragments are read in batches ahead of their MFMAs.
+  // fp16 operand scales of this call
+  const float s_ds = a.scales[2];
+
+  // One step: S and dP MFMAs; 2^15 P under the dP MFMAs; dV MFMAs; scaled dS under the dV MFMAs;
+  // dK MFMAs. Fragments are read in batches ahead of their MFMAs.
   auto compute = [&](const char* buf, int m0) {
     // S[row][key] = Q K^T and dP = dO V^T: lane holds key (lane & 31), rows 8(r/4) + 4hl + r%4
     f32x16 s, dp;
@@ -231,14 +219,14 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
       st[q][0] = __builtin_bit_cast(f32x4, lds_b128_at(buf, C::OFF_LD + (8 * q + 4 * hl) * 8));
       st[q][1] = __builtin_bit_cast(f32x4, lds_b128_at(buf, C::OFF_LD + (8 * q + 4 * hl) * 8 + 16));
     }
-    // dO^T fragments for the dV MFMAs
-    bf16x8 ot[2][C::VB];
+    // dO^T fragments (fp16, scaled) for the dV MFMAs
+    f16x8 ot[2][C::VB];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int b = 0; b < C::VB; ++b) ot[h][b] = lds_b128_at(buf, C::OFF_OT + b * 32 * C::TROW + toff[h]);
+      for (int b = 0; b < C::VB; ++b) ot[h][b] = lds_h128_at(buf, C::OFF_OT + b * 32 * C::TROW + toff[h]);
     __builtin_amdgcn_sched_barrier(0);
-    // P = exp2(S scale log2 e - LSE log2 e), under the dP MFMAs
+    // 2^15 P = exp2(S scale log2 e - (LSE log2 e - 15)), under the dP MFMAs
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int q = r >> 2, e = r & 3;
@@ -251,59 +239,35 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
       s[r] = pv;
     }
     // dV^T[dv][key] += dO^T P (A operands: one 16-byte read of packed slots)
-    if (PROMPT) {
-      bf16x8 ph[2], pl[2];
-      split8(s, 0, ph[0], pl[0]);
-      split8(s, 8, ph[1], pl[1]);
+    {
+      const f16x8 p0 = c_regs_to_f16x8(s, 0), p1 = c_regs_to_f16x8(s, 8);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int b = 0; b < C::VB; ++b) dv[b] = mfma32h(ot[0][b], p0, dv[b]);
 #pragma unroll
-        for (int b = 0; b < C::VB; ++b) {
-          dv[b] = mfma32(ot[h][b], ph[h], dv[b]);
-          dv[b] = mfma32(ot[h][b], pl[h], dv[b]);
-        }
-    } else {
-      const bf16x8 p0 = c_regs_to_bf16x8(s, 0), p1 = c_regs_to_bf16x8(s, 8);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int b = 0; b < C::VB; ++b) dv[b] = mfma32(ot[0][b], p0, dv[b]);
-#pragma unroll
-      for (int b = 0; b < C::VB; ++b) dv[b] = mfma32(ot[1][b], p1, dv[b]);
+      for (int b = 0; b < C::VB; ++b) dv[b] = mfma32h(ot[1][b], p1, dv[b]);
     }
-    // Q^T fragments for the dK MFMAs
-    bf16x8 qt[2][C::DB];
+    // Q^T fragments (fp16, scaled) for the dK MFMAs
+    f16x8 qt[2][C::DB];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int b = 0; b < C::DB; ++b) qt[h][b] = lds_b128_at(buf, C::OFF_QT + b * 32 * C::TROW + toff[h]);
+      for (int b = 0; b < C::DB; ++b) qt[h][b] = lds_h128_at(buf, C::OFF_QT + b * 32 * C::TROW + toff[h]);
     __builtin_amdgcn_sched_barrier(0);
-    // dS = P (dP - Delta), under the dV MFMAs
+    // scaled dS = 2^15 P (dP s_dS - Delta s_dS), under the dV MFMAs
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int q = r >> 2, e = r & 3;
-      dp[r] = s[r] * (dp[r] - st[q][e >> 1][2 * (e & 1) + 1]);
+      dp[r] = s[r] * __builtin_fmaf(dp[r], s_ds, -st[q][e >> 1][2 * (e & 1) + 1]);
     }
     // dK^T[d][key] += Q^T dS
-    if (PROMPT) {
-      bf16x8 dh[2], dl[2];
-      split8(dp, 0, dh[0], dl[0]);
-      split8(dp, 8, dh[1], dl[1]);
+    {
+      const f16x8 d0 = c_regs_to_f16x8(dp, 0), d1 = c_regs_to_f16x8(dp, 8);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int b = 0; b < C::DB; ++b) dk[b] = mfma32h(qt[0][b], d0, dk[b]);
 #pragma unroll
-        for (int b = 0; b < C::DB; ++b) {
-          dk[b] = mfma32(qt[h][b], dh[h], dk[b]);
-          dk[b] = mfma32(qt[h][b], dl[h], dk[b]);
-        }
-    } else {
-      const bf16x8 d0 = c_regs_to_bf16x8(dp, 0), d1 = c_regs_to_bf16x8(dp, 8);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int b = 0; b < C::DB; ++b) dk[b] = mfma32(qt[0][b], d0, dk[b]);
-#pragma unroll
-      for (int b = 0; b < C::DB; ++b) dk[b] = mfma32(qt[1][b], d1, dk[b]);
+      for (int b = 0; b < C::DB; ++b) dk[b] = mfma32h(qt[1][b], d1, dk[b]);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -333,8 +297,10 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
   }
 
   if (!kvalid) return;
-  // C layout of dV^T / dK^T: lane holds key (lane & 31), dims 32b + 8(r/4) + 4hl + r%4
-  const float sc = G.scale;
+  // C layout of dV^T / dK^T: lane holds key (lane & 31), dims 32b + 8(r/4) + 4hl + r%4.
+  // Undo the operand scales: dV = sum / (2^15 s_dO), dK = scale * sum / (2^15 s_dS s_Q).
+  const float fv = 0x1p-15f / a.scales[0];
+  const float sc = G.scale * 0x1p-15f / (s_ds * a.scales[1]);
   if (PROMPT) {
     float* dvr = a.dVp + ((int64_t)(key0 + mykey) * G.Hkv + kvh) * DV + 4 * hl;
     float* dkr = a.dKp + ((int64_t)(key0 + mykey) * G.Hkv + kvh) * D + 4 * hl;
@@ -343,7 +309,7 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         f32x4* ptr = reinterpret_cast<f32x4*>(dvr + b * 32 + 8 * q);
-        const f32x4 add = {dv[b][4 * q], dv[b][4 * q + 1], dv[b][4 * q + 2], dv[b][4 * q + 3]};
+        const f32x4 add = {dv[b][4 * q] * fv, dv[b][4 * q + 1] * fv, dv[b][4 * q + 2] * fv, dv[b][4 * q + 3] * fv};
         *ptr = *ptr + add;
       }
 #pragma unroll
@@ -362,7 +328,8 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
     for (int b = 0; b < C::VB; ++b)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const u32x2 v = {pack_bf16x2(dv[b][4 * q], dv[b][4 * q + 1]), pack_bf16x2(dv[b][4 * q + 2], dv[b][4 * q + 3])};
+        const u32x2 v = {pack_bf16x2(dv[b][4 * q] * fv, dv[b][4 * q + 1] * fv),
+                         pack_bf16x2(dv[b][4 * q + 2] * fv, dv[b][4 * q + 3] * fv)};
         *reinterpret_cast<u32x2*>(dvr + b * 32 + 8 * q) = v;
       }
 #pragma unroll
@@ -380,9 +347,27 @@ template <int D, int DV>
 hipError_t dkdv_go(BwdArgs& a, hipStream_t st) {
   const AttnGeom& G = a.geo;
   hipError_t e;
-  // packed query rows of every kv head: row-major Q / dO, dimension-major Q^T / dO^T, statistics
+  // fp16 operand scales of this call
+  ScaleArgs sa;
+  sa.dO = a.dO;
+  sa.Q = G.Q;
+  sa.Vp = G.Vp;
+  sa.Vs = G.Vs;
+  sa.ldv = G.ldv;
+  sa.T = G.T;
+  sa.P = G.P;
+  sa.Hq = G.Hq;
+  sa.Hkv = G.Hkv;
+  sa.Dqk = D;
+  sa.Dv = DV;
+  sa.partial = a.scale_part;
+  sa.scales = a.scales;
+  if ((e = launch_bwd_scales(sa, st)) != hipSuccess) return e;
+  // packed query rows of every kv head: row-major Q / dO (bf16), dimension-major Q^T / dO^T (fp16,
+  // scaled), statistics
   const int64_t M = (int64_t)G.T * G.g;
   PackArgs p;
+  p.f16_scale = nullptr;
   p.ld = (int64_t)G.Hq * D;
   p.grp = G.g;
   p.gstride = D;
@@ -399,7 +384,9 @@ hipError_t dkdv_go(BwdArgs& a, hipStream_t st) {
   p.out = a.Qr;
   if ((e = launch_pack_rows(p, st)) != hipSuccess) return e;
   p.out = a.QT;
+  p.f16_scale = a.scales + 1;
   if ((e = launch_pack_keys_t(p, st)) != hipSuccess) return e;
+  p.f16_scale = nullptr;
   p.ld = (int64_t)G.Hq * DV;
   p.gstride = DV;
   p.hstride = (int64_t)G.g * DV;
@@ -408,10 +395,12 @@ hipError_t dkdv_go(BwdArgs& a, hipStream_t st) {
   p.out = a.dOr;
   if ((e = launch_pack_rows(p, st)) != hipSuccess) return e;
   p.out = a.dOT;
+  p.f16_scale = a.scales + 0;
   if ((e = launch_pack_keys_t(p, st)) != hipSuccess) return e;
   RowStatArgs r;
   r.lse = a.lse;
   r.delta = a.delta;
+  r.scales = a.scales;
   r.out = a.rowstat;
   r.T = G.T;
   r.Hq = G.Hq;

@@ -304,6 +304,7 @@ hipError_t dq_go(BwdArgs& a, hipStream_t st) {
   hipError_t e;
   // dimension-major packed K of the prompt and of every response (dQ^T = K^T dS^T operand)
   PackArgs p;
+  p.f16_scale = nullptr;
   p.src = G.Kp;
   p.ld = G.ldk;
   p.dim = D;

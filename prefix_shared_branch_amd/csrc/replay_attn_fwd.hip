@@ -371,6 +371,7 @@ hipError_t fwd_go(FwdArgs& a, hipStream_t st) {
   const AttnGeom& G = a.geo;
   if (G.P > 0) {
     PackArgs p;
+    p.f16_scale = nullptr;
     p.src = G.Vp;
     p.ld = G.ldv;
     p.dim = DV;
@@ -390,6 +391,7 @@ hipError_t fwd_go(FwdArgs& a, hipStream_t st) {
   }
   {
     PackArgs p;
+    p.f16_scale = nullptr;
     p.src = G.Vs;
     p.ld = G.ldv;
     p.dim = DV;
