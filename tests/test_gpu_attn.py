@@ -205,3 +205,32 @@ def test_kernel_timer_counts_launches():
     case.fwd()
     ms, n = L.ls_kernel_timer_stop()
     assert n == 1 and ms > 0.0, (ms, n)
+
+
+@pytest.mark.parametrize("do_scale,q_scale", [(3e-7, 1.0), (5e4, 1.0), (1.0, 0.05), (0.0, 1.0)])
+def test_backward_operand_scaling(do_scale, q_scale):
+    """The dK/dV products run in fp16 on operands scaled by per-call powers of two; gradients of
+    realistic (tiny) or large magnitude, small queries and an all-zero dO must keep the accumulator
+    bar. Scaled inputs are re-rounded to bf16 and the oracle sees those values."""
+    cfg = inputs.replace(inputs.CONFIGS["tiny"], P=3000, seed=36)
+    case = Case(cfg, [77, 120])
+
+    def rescale(bits, f):
+        return inputs.f32_to_bf16_bits((inputs.bf16_bits_to_f32(bits) * np.float32(f)).astype(np.float32))
+
+    T = int(case.cu[-1])
+    do_bits = rescale(inputs.suffix_do(cfg, 0, T), do_scale)
+    q_bits = rescale(inputs.suffix_q(cfg, 0, T), q_scale)
+    case.do, case.h["dO"] = dev_bf16(do_bits), inputs.bf16_bits_to_f64(do_bits)
+    case.q, case.h["Q"] = dev_bf16(q_bits), inputs.bf16_bits_to_f64(q_bits)
+    t = case.torch
+    dkp, dvp = case.accums()
+    o, lse = case.fwd()
+    dq, dks, dvs = case.bwd(o, lse, dkp, dvp)
+    t.cuda.synchronize()
+    ref = case.oracle()
+    if do_scale == 0.0:
+        for x in (dkp, dvp, dq, dks, dvs):
+            assert not bool(x.any()), "a zero dO must give exactly zero gradients"
+        return
+    _check_all(dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp), ref, literal_abs=False)
