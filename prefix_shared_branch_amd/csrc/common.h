@@ -93,13 +93,17 @@ __device__ __forceinline__ bf16x8 join_tr(const s16x4& a, const s16x4& b) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// ---- LDS tiles without padding: logical 16-byte chunk c of row r is stored at chunk c ^ swz(r).
-// Conflict-free on gfx950 both for 16-byte row reads (8 lanes on 8 consecutive rows, same chunk)
-// and for ds_read_b64_tr_b16 (4 consecutive rows x 64 contiguous bytes per 32 lanes).
-template <int CH>  // 16-byte chunks per row (power of two)
+// ---- LDS tiles without padding: logical 16-byte chunk c of row r is stored at chunk c ^ swz<CH>(r),
+// CH = chunks per row. ds_read_b128 serves 16 lanes (256 bytes, all 64 banks) per phase; for 16
+// consecutive rows reading the same logical chunk the swizzle puts the 16 reads in 16 distinct
+// 16-byte bank groups, for rows of 16 chunks (256 B), 8 chunks (128 B) and 4 chunks (64 B).
+// (The 16-chunk form is also conflict-free for ds_read_b64_tr_b16, 4 rows x 64 contiguous bytes.)
+template <int CH>
 __device__ __forceinline__ int swz(int r) {
-  const int f = ((r & 3) << 2) ^ ((r >> 2) & 3) ^ (r & 2);
-  return f & (CH - 1);
+  static_assert(CH == 4 || CH == 8 || CH == 16, "row length");
+  if constexpr (CH == 16) return (((r & 3) << 2) ^ ((r >> 2) & 3) ^ (r & 2)) & 15;
+  else if constexpr (CH == 8) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
 }
 
 // ---- Padded LDS tiles of 64 rows: row r starts at byte 16 * PCH * r (PCH >= CH chunks of 16 B).

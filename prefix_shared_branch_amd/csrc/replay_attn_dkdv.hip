@@ -58,10 +58,6 @@ struct DkvCfg {
   static constexpr int VB = DV / 32;
 };
 
-// swizzle of the 16-byte chunks of 64-byte rows (4 chunks): conflict-free 16-byte reads of one
-// chunk column by 8 consecutive rows
-__device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
-
 template <int D, int DV, bool PROMPT>
 __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
   using C = DkvCfg<D, DV>;
@@ -135,7 +131,7 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
 #pragma unroll
   for (int ks = 0; ks < C::VS; ++ks) ooff[ks] = C::OFF_O + l32 * C::OROW + (((2 * ks + hl) ^ swz<C::OCH>(l32)) << 4);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) toff[h] = l32 * C::TROW + (((2 * h + hl) ^ swz4(l32)) << 4);
+  for (int h = 0; h < 2; ++h) toff[h] = l32 * C::TROW + (((2 * h + hl) ^ swz<4>(l32)) << 4);
 
   // per-lane global byte offsets of the direct loads within one step's slabs
   const int64_t mpad = a.mpad;
@@ -160,12 +156,12 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
 #pragma unroll
   for (int u = 0; u < C::QTINS; ++u) {
     const int row = (wv * C::QTINS + u) * 16 + (lane >> 2);
-    qtdo[u] = (uint32_t)(row * mpad * 2 + (((lane & 3) ^ swz4(row)) << 4));
+    qtdo[u] = (uint32_t)(row * mpad * 2 + (((lane & 3) ^ swz<4>(row)) << 4));
   }
 #pragma unroll
   for (int u = 0; u < C::OTINS; ++u) {
     const int row = (wv * C::OTINS + u) * 16 + (lane >> 2);
-    otdo[u] = (uint32_t)(row * mpad * 2 + (((lane & 3) ^ swz4(row)) << 4));
+    otdo[u] = (uint32_t)(row * mpad * 2 + (((lane & 3) ^ swz<4>(row)) << 4));
   }
   const uint32_t ldo = (uint32_t)lane * 4;
   auto issue_step = [&](int m0, char* buf) {

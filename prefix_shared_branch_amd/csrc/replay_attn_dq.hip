@@ -161,10 +161,12 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
     for (int b = 0; b < C::DB; ++b) dq[rb][b] = f32x16{};
   const float c2 = G.scale_log2;
 
+  // Per 32-key block: S MFMAs; dP MFMAs with P formed under them; then per row block dS and its dQ
+  // MFMAs, row block 1's dS formed under row block 0's MFMAs.
   auto compute = [&](const char* buf, bool masked, int key0, int nvalid, bool causal) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      // S^T = K Q^T, then dP^T = V dO^T, for both row blocks (each fragment feeds two MFMAs)
+      // S^T = K Q^T for both row blocks (each K fragment feeds two MFMAs)
       f32x16 st[C::RB], dp[C::RB];
       {
         bf16x8 kf[C::KS];
@@ -178,6 +180,7 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
           for (int ks = 0; ks < C::KS; ++ks) st[rb] = mfma32(kf[ks], qf[rb][ks], st[rb]);
         }
       }
+      // dP^T = V dO^T
       {
         bf16x8 vf[C::VS];
 #pragma unroll
@@ -201,29 +204,29 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
           for (int r = 0; r < 16; ++r) st[rb][r] = (8 * (r >> 2) + (r & 3)) < lim ? st[rb][r] : -INFINITY;
         }
       }
-      // dS = P (dP - Delta), as the bf16 B operands of dQ^T += K^T dS^T
-      bf16x8 db[C::RB][2];
+      // P = exp(S scale - LSE), under the dP MFMAs
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[rb][r] = fast_exp2(__builtin_fmaf(st[rb][r], c2, -lrow[rb]));
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rb = 0; rb < C::RB; ++rb) {
+        // dS = P (dP - Delta) as the bf16 B operands of dQ^T += K^T dS^T
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(__builtin_fmaf(st[rb][r], c2, -lrow[rb]));
-          st[rb][r] = pv * (dp[rb][r] - drow[rb]);
-        }
-        db[rb][0] = c_regs_to_bf16x8(st[rb], 0);
-        db[rb][1] = c_regs_to_bf16x8(st[rb], 8);
-      }
-      // K^T fragments: one 16-byte read of packed slots each, feeding two MFMAs
+        for (int r = 0; r < 16; ++r) st[rb][r] = st[rb][r] * (dp[rb][r] - drow[rb]);
+        const bf16x8 d0 = c_regs_to_bf16x8(st[rb], 0), d1 = c_regs_to_bf16x8(st[rb], 8);
+        // K^T fragments: one 16-byte read of packed slots each
+        bf16x8 tf[2][C::DB];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 tf[C::DB];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int b = 0; b < C::DB; ++b) tf[b] = lds_b128_at(buf, b * 32 * C::TROW + toff[kb][h]);
+          for (int b = 0; b < C::DB; ++b) tf[h][b] = lds_b128_at(buf, b * 32 * C::TROW + toff[kb][h]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int b = 0; b < C::DB; ++b)
+        for (int b = 0; b < C::DB; ++b) dq[rb][b] = mfma32(tf[0][b], d0, dq[rb][b]);
 #pragma unroll
-          for (int rb = 0; rb < C::RB; ++rb) dq[rb][b] = mfma32(tf[b], db[rb][h], dq[rb][b]);
+        for (int b = 0; b < C::DB; ++b) dq[rb][b] = mfma32(tf[1][b], d1, dq[rb][b]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
