@@ -18,8 +18,6 @@
 namespace lsr {
 
 namespace {
-constexpr int kQTileFwd = 256;  // packed query rows per forward workgroup (64 per wave)
-constexpr int kQTileDq = 256;   // packed query rows per dQ workgroup (64 per wave)
 constexpr int kKTile = 64;    // keys per forward / dQ tile
 constexpr int kDKTile = 128;  // keys per dK/dV workgroup
 constexpr int kTargetBlocks = 2048;

@@ -117,6 +117,16 @@ __device__ __forceinline__ void dma_tile64(const uint16_t* base, int64_t ld, int
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane i's bytes land at
 // lds_wave_base + 16 i. lds_wave_base must be wave-uniform.
+// Raw buffer resource over the `bytes` bytes from `base` (clamped to 2^32 - 1): loads at offsets past
+// the end return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)(uint32_t)n, kBufferWord3);
+}
+// 16 bytes per lane from buffer offset voff into LDS at lds_wave_base + 16 * lane (direct load)
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LSR_LDS void*)lds_wave_base, 16, (int)voff, 0, 0, 0);
+}
 __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
                                    (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
@@ -145,6 +155,15 @@ __device__ __forceinline__ void dma_tile64(const uint16_t* base, int64_t ld, int
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima): this wave's LDS reads have returned
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// workgroup barrier that orders this wave's memory operations in program order around it but
+// waits for nothing (no s_waitcnt); callers wait for the counters they need first
+__device__ __forceinline__ void bare_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 // s_waitcnt vmcnt(N): at most N vector-memory operations of this wave still outstanding
 template <int N>
 __device__ __forceinline__ void wait_vmem_le() {

@@ -10,6 +10,9 @@
 namespace lsr {
 
 constexpr int kMaxResp = 64;
+// packed query rows per workgroup of the forward and dQ kernels (the plan's query tiles)
+constexpr int kQTileFwd = 256;
+constexpr int kQTileDq = 256;
 
 // ---------------------------------------------------------------- GRPO token loss
 struct GrpoArgs {

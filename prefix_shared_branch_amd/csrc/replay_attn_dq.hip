@@ -16,6 +16,7 @@ template <int D, int DV>
 struct DqCfg {
   static constexpr int RB = 2;                // 32-row blocks per wave
   static constexpr int BM = 4 * 32 * RB;      // packed query rows per workgroup
+  static_assert(BM == kQTileDq, "dQ tile must match the plan");
   static constexpr int BN = 64;               // keys per tile
   static constexpr int KCH = D / 8;           // 16-byte chunks per K row
   static constexpr int VCH = DV / 8;

@@ -2,14 +2,15 @@
 // the queries of one response attend to all prompt keys and, causally, to the response's
 // own keys.
 //
-// replay_fwd: one workgroup = 4 waves x 64 = 256 GQA-packed query rows of one kv head (one wave
-// per SIMD), over the prompt key tiles of one split (plus, in the last split, the response's
-// causal key tiles). Per 64-key tile, K (key-major) and V (dimension-major, packed by pack.hip)
-// stream global -> LDS by direct DMA into a three-stage ring of XOR-swizzled tiles. Per 32-key
-// block each wave computes S^T = K Q^T for its two 32-row blocks (MFMA 32x32x16 bf16; Q fragments
-// stay in registers; every K fragment read from LDS feeds two MFMAs), an online softmax whose row
-// statistics are lane-local (one query row per lane), and O^T += V^T P^T where P^T comes straight
-// from the score accumulators and every V^T fragment is one 16-byte LDS read feeding two MFMAs.
+// replay_fwd: one workgroup = 8 waves x 32 = 256 GQA-packed query rows of one kv head, over the
+// prompt key tiles of one split (plus, in the last split, the response's causal key tiles). Per
+// 64-key tile, K (key-major) and V (dimension-major, packed by pack.hip) stream global -> LDS by
+// direct buffer loads into a four-stage ring of XOR-swizzled tiles. Per 32-key block each wave
+// computes S^T = K Q^T for its 32 rows (MFMA 32x32x16 bf16; Q fragments stay in registers), an
+// online softmax whose row statistics are lane-local (one query row per lane), and O^T += V^T P^T
+// where P^T comes straight from the score accumulators and every V^T fragment is one 16-byte LDS
+// read. Two waves share each SIMD and run half a step apart, so one wave's softmax (VALU) overlaps
+// the other's MFMAs.
 // The softmax stabiliser is only moved when a row maximum exceeds it by more than 2^8 (in exp2
 // units), so the O rescale is rare; probabilities stay <= 256, far inside fp32/bf16 range.
 // Workgroup ids are mapped so that each XCD owns a contiguous run of (kv head, split) streams:
@@ -25,10 +26,18 @@ namespace lsr {
 
 namespace {
 
+// Eight waves per workgroup, two per SIMD (waves w and w + 4 share a SIMD), 32 query rows each.
+// The waves form two groups, 0-3 and 4-7, that run half a step apart: while one group's wave on a
+// SIMD issues MFMAs, the other group's wave on the same SIMD runs its softmax on the VALU (on gfx950
+// a wave's MFMAs keep their full rate while the SIMD's other wave executes VALU work; within one
+// wave the two serialise). Workgroup barriers separate the phases and keep the groups in step.
+constexpr int kFwdWaves = 8;
+
 template <int D, int DV>
 struct FwdCfg {
-  static constexpr int RB = 2;                // 32-row blocks per wave
-  static constexpr int BM = 4 * 32 * RB;      // packed query rows per workgroup
+  static constexpr int NW = kFwdWaves;
+  static constexpr int BM = NW * 32;          // packed query rows per workgroup
+  static_assert(BM == kQTileFwd, "forward tile must match the plan");
   static constexpr int BN = 64;               // keys per tile
   static constexpr int KCH = D / 8;           // 16-byte chunks per K row
   static constexpr int KROW = D * 2;          // bytes per K row in LDS
@@ -36,15 +45,16 @@ struct FwdCfg {
   static constexpr int KBYTES = BN * KROW;
   static constexpr int VBYTES = DV * VTROW;
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int NSTAGE = 3;
-  static constexpr int KINS = KBYTES / 1024 / 4;  // 1 KB direct loads per wave per tile
-  static constexpr int VINS = VBYTES / 1024 / 4;
+  static constexpr int NSTAGE = 4;
+  static constexpr int KP = KBYTES / 1024;     // 1 KB direct-load pieces of a tile: K pieces first,
+  static constexpr int NP = STAGE / 1024;      // then V^T pieces
+  static constexpr int PPW = NP / NW;          // pieces per wave per tile (one after each of PPW barriers)
+  static_assert(NP % NW == 0 && KP % NW == 0 && PPW <= 4, "pieces split evenly over the waves");
+  static_assert(STAGE % (16 * 64 * NW) == 0, "a stage is zero-filled in whole 16-byte stores");
   static constexpr int KS = D / 16;           // MFMA k-steps over the head dim
   static constexpr int NB = DV / 32;          // 32-wide blocks of the value dim
   static constexpr float kStale = 8.0f;       // stabiliser slack (exp2 units)
 };
-
-__device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
 
 // max / sum of a value over lanes l and l ^ 32. The swap of two copies of v leaves, in each lane,
 // the lane's own value in one result and its partner's in the other; combining the two results
@@ -58,8 +68,15 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// compile-time selector of one part of an MFMA phase: present or not, and which 32-key half of a tile
+template <bool ON, int HALF>
+struct Part {
+  static constexpr bool on = ON;
+  static constexpr int half = HALF;
+};
+
 template <int D, int DV>
-__global__ __launch_bounds__(256, 1) void replay_fwd(FwdArgs a) {
+__global__ __launch_bounds__(64 * kFwdWaves, 1) void replay_fwd(FwdArgs a) {
   using C = FwdCfg<D, DV>;
   __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE];
 
@@ -81,34 +98,29 @@ __global__ __launch_bounds__(256, 1) void replay_fwd(FwdArgs a) {
   const int m0 = (qt - a.tile0[ri]) * C::BM;
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int hl = lane >> 5;
   const int l32 = lane & 31;
+  const bool lead = wv < 4;  // group 0 (waves 0-3) runs half a step ahead of group 1
 
-  // query rows: block rb of wave wv holds packed rows m0 + 64 wv + 32 rb + (lane % 32)
-  bool rvalid[C::RB];
-  int trow[C::RB], hq[C::RB];
-  bf16x8 qf[C::RB][C::KS];
+  // query row of this lane: packed row m0 + 32 wv + (lane % 32); Q stays in registers
+  const int mrow = m0 + wv * 32 + l32;
+  const bool rvalid = mrow < M;
+  const int trow = rvalid ? mrow / g : 0;
+  const int hq = kvh * g + (rvalid ? mrow - trow * g : 0);
+  bf16x8 qf[C::KS];
+  {
+    const uint16_t* qrow = G.Q + ((int64_t)(tokb + trow) * G.Hq + hq) * D + hl * 8;
 #pragma unroll
-  for (int rb = 0; rb < C::RB; ++rb) {
-    const int mrow = m0 + wv * 32 * C::RB + rb * 32 + l32;
-    rvalid[rb] = mrow < M;
-    trow[rb] = rvalid[rb] ? mrow / g : 0;
-    hq[rb] = kvh * g + (rvalid[rb] ? mrow - trow[rb] * g : 0);
-    const uint16_t* qrow = G.Q + ((int64_t)(tokb + trow[rb]) * G.Hq + hq[rb]) * D + hl * 8;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      if (rvalid[rb]) qf[rb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + ks * 16));
-      else qf[rb][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      // Q fragments are only ever MFMA operands: keep them in AGPRs
-      asm volatile("" : "+a"(qf[rb][ks]));
-    }
+    for (int ks = 0; ks < C::KS; ++ks)
+      qf[ks] = rvalid ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + ks * 16))
+                      : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
 
   // lane-constant LDS byte offsets within a stage (block and tile offsets are immediates)
-  int koff[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = l32 * C::KROW + (((2 * ks + hl) ^ swz<C::KCH>(l32)) << 4);
+  // K fragment ks of a lane sits at chunk (2 ks + hl) ^ swz(l32) of row l32; since 2 ks and hl
+  // occupy different bits, its offset is kbase ^ (ks << 5) (only chunk bits change)
+  const int kbase = l32 * C::KROW + ((hl ^ swz<C::KCH>(l32)) << 4);
   int voff[2][2];  // [32-key block][16-key half]: packed slots 32 kb + 16 h + 8 hl .. +7 of dim row l32
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -123,91 +135,143 @@ __global__ __launch_bounds__(256, 1) void replay_fwd(FwdArgs a) {
   const int ns = (sp == a.splits - 1) ? (t_hi / C::BN + 1) : 0;
   const int nit = np + ns;
 
-  // Per-lane byte offsets of the direct loads within a full tile (32-bit, added to a wave-uniform
-  // tile base): K rows are key-major (1024 / KROW rows per 1 KB instruction), packed V^T rows
-  // are dimension-major (8 rows of 128 bytes per instruction).
-  uint32_t kdo[C::KINS], vdo[C::VINS];
+  // Direct loads: a tile is NP pieces of 1 KB (one 16-byte load per lane), K pieces first, then
+  // packed V^T pieces. Wave wv moves pieces wv, wv + NW, wv + 2 NW, ... (piece k of the wave). K rows
+  // are key-major (1024 / KROW rows per piece), packed V^T rows dimension-major (8 rows of 128 bytes
+  // per piece); lane byte offsets within the tile are 32-bit and fixed per piece (prompt pitch).
+  uint32_t pdo[C::PPW], rdo[C::PPW];  // prompt pitch; V^T pieces of response tiles: response pitch
 #pragma unroll
-  for (int u = 0; u < C::KINS; ++u) {
-    const int row = (wv * C::KINS + u) * (64 / C::KCH) + lane / C::KCH;
-    kdo[u] = (uint32_t)(row * G.ldk * 2 + (((lane % C::KCH) ^ swz<C::KCH>(row)) << 4));
-  }
-#pragma unroll
-  for (int u = 0; u < C::VINS; ++u) {
-    const int row = (wv * C::VINS + u) * 8 + (lane >> 3);
-    vdo[u] = (uint32_t)(row * a.ppad * 2 + (((lane & 7) ^ swz<8>(row)) << 4));
+  for (int k = 0; k < C::PPW; ++k) {
+    const int pc = k * C::NW + wv;
+    if (pc < C::KP) {
+      const int row = pc * (64 / C::KCH) + lane / C::KCH;
+      pdo[k] = rdo[k] = (uint32_t)(row * G.ldk * 2 + (((lane % C::KCH) ^ swz<C::KCH>(row)) << 4));
+    } else {
+      const int row = (pc - C::KP) * 8 + (lane >> 3);
+      pdo[k] = (uint32_t)(row * a.ppad * 2 + (((lane & 7) ^ swz<8>(row)) << 4));
+      rdo[k] = (uint32_t)(row * a.tpad * 2 + (((lane & 7) ^ swz<8>(row)) << 4));
+    }
   }
 
-  // global -> LDS for tile `it` into stage buffer `buf`
-  auto issue_tile = [&](int it, char* buf) {
-    if (it < np) {
-      const int key0 = (pt0 + it) * C::BN;
-      const int nvalid = min(C::BN, G.P - key0);
-      const char* kb = reinterpret_cast<const char*>(G.Kp + (int64_t)key0 * G.ldk + kvh * D);
-      const char* vb = reinterpret_cast<const char*>(a.VTp + (int64_t)kvh * DV * a.ppad + key0);
-      if (nvalid == C::BN) {
-#pragma unroll
-        for (int u = 0; u < C::KINS; ++u) lds_dma16(kb + kdo[u], buf + (wv * C::KINS + u) * 1024);
-#pragma unroll
-        for (int u = 0; u < C::VINS; ++u) lds_dma16(vb + vdo[u], buf + C::KBYTES + (wv * C::VINS + u) * 1024);
-        return;
-      }
-    }
-    // ragged prompt tail or response keys: rows past the valid keys re-read the last valid row
-    // (finite data, masked out of the softmax); packed V^T slots past the keys hold zeros
-    const bool pr = it < np;
-    const int key0 = pr ? (pt0 + it) * C::BN : (it - np) * C::BN;
-    const int nvalid = min(C::BN, (pr ? G.P : R) - key0);
-    const uint16_t* kb = pr ? G.Kp + (int64_t)key0 * G.ldk + kvh * D
-                            : G.Ks + (int64_t)(tokb + key0) * G.ldk + kvh * D;
-    const uint16_t* vb = pr ? a.VTp + (int64_t)kvh * DV * a.ppad + key0
-                            : a.VTs + (int64_t)kvh * DV * a.tpad + a.spos[ri] + key0;
-    const int64_t vld = pr ? a.ppad : a.tpad;
-#pragma unroll
-    for (int u = 0; u < C::KINS; ++u) {
-      const int ins = wv * C::KINS + u;
-      const int row = ins * (64 / C::KCH) + lane / C::KCH;
-      const int c = (lane % C::KCH) ^ swz<C::KCH>(row);
-      lds_dma16(kb + (int64_t)min(row, nvalid - 1) * G.ldk + c * 8, buf + ins * 1024);
-    }
-#pragma unroll
-    for (int u = 0; u < C::VINS; ++u) {
-      const int ins = wv * C::VINS + u;
-      const int row = ins * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz<8>(row);
-      lds_dma16(vb + (int64_t)row * vld + c * 8, buf + C::KBYTES + ins * 1024);
+  // global -> LDS sources of a tile: buffer resources that end with the key arrays, so K rows past
+  // the last key read as zeros (those keys are masked out of the softmax); packed V^T slots past the
+  // keys hold zeros. Bases and extents are formed once; per tile only the start moves.
+  const char* const kp0 = reinterpret_cast<const char*>(G.Kp + kvh * D);
+  const char* const ks0 = reinterpret_cast<const char*>(G.Ks + (int64_t)tokb * G.ldk + kvh * D);
+  const char* const vp0 = reinterpret_cast<const char*>(a.VTp + (int64_t)kvh * DV * a.ppad);
+  const char* const vs0 = reinterpret_cast<const char*>(a.VTs + (int64_t)kvh * DV * a.tpad + a.spos[ri]);
+  const int64_t kp_end = ((int64_t)(G.P - 1) * G.ldk + (int64_t)(G.Hkv - kvh) * D) * 2;
+  const int64_t ks_end = ((int64_t)(G.T - 1 - tokb) * G.ldk + (int64_t)(G.Hkv - kvh) * D) * 2;
+  const int64_t vp_end = (int64_t)(G.Hkv - kvh) * DV * a.ppad * 2;
+  const int64_t vs_end = ((int64_t)(G.Hkv - kvh) * DV * a.tpad - a.spos[ri]) * 2;
+  const int64_t ldk2 = G.ldk * 2;
+  struct TileSrc {
+    __amdgpu_buffer_rsrc_t k, v;
+    bool prompt;
+  };
+  auto tile_src = [&](int it) {
+    TileSrc ts;
+    ts.prompt = it < np;
+    const int key0 = ts.prompt ? (pt0 + it) * C::BN : (it - np) * C::BN;
+    const int64_t ko = key0 * ldk2, vo = (int64_t)key0 * 2;
+    ts.k = buf_rsrc((ts.prompt ? kp0 : ks0) + ko, (ts.prompt ? kp_end : ks_end) - ko);
+    ts.v = buf_rsrc((ts.prompt ? vp0 : vs0) + vo, (ts.prompt ? vp_end : vs_end) - vo);
+    return ts;
+  };
+  // piece k of this wave for tile `it` (branch-free: it is issued between MFMAs)
+  auto issue_piece = [&](int it, const TileSrc& ts, auto kc) {
+    constexpr int k = decltype(kc)::value;
+    char* dst = smem + (it % C::NSTAGE) * C::STAGE + (k * C::NW + wv) * 1024;
+    if constexpr (k * C::NW < C::KP) lds_dma16_buf(ts.k, pdo[k], dst);
+    else {
+      // a bit blend rather than a select, which the compiler would turn into a select of array
+      // addresses (and move both arrays to scratch memory)
+      const uint32_t m = ts.prompt ? 0xFFFFFFFFu : 0u;
+      lds_dma16_buf(ts.v, (pdo[k] & m) | (rdo[k] & ~m), dst);
     }
   };
 
-  f32x16 o[C::RB][C::NB];
-  float mu[C::RB], l_run[C::RB];   // stabiliser (score * scale * log2 e) and row sum of this lane's keys
+  f32x16 o[C::NB];
 #pragma unroll
-  for (int rb = 0; rb < C::RB; ++rb) {
-    mu[rb] = -INFINITY;
-    l_run[rb] = 0.0f;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) o[rb][nb] = f32x16{};
-  }
+  for (int nb = 0; nb < C::NB; ++nb) o[nb] = f32x16{};
+  float mu = -INFINITY;  // stabiliser (score * scale * log2 e)
+  float l_run = 0.0f;    // row sum of this lane's keys
+  f32x16 st;             // S^T of the 32-key block whose softmax comes next
+  bf16x8 p0, p1;         // P^T of the block whose PV product comes next (two 16-key B operands)
   const float c2 = G.scale_log2;
 
-  // online softmax of one 32-row block (one query row per lane; the other half-wave holds the
-  // row's other keys); returns the probabilities as the two bf16 B operands of the PV product
-  auto softmax = [&](int rb, f32x16& st, bf16x8& p0, bf16x8& p1) {
+  // MFMA phase of 32-key block j = 2t + h: S^T = K Q^T for block j (tile t, half h) and
+  // O^T += V^T P^T for block j - 1 (its probabilities from the previous softmax phase). Block -1 has
+  // zero probabilities and reads a zero-filled stage; the scores of block 2 nit (past the last tile)
+  // are formed from stale LDS data and never used.
+  // The phase also issues this wave's direct-load pieces K0 .. K0 + NK - 1 of tile `pt` (source ts),
+  // spread between its MFMAs so that the loads enter the memory pipeline one at a time.
+  auto mma = [&](int t, auto half, int pt, const TileSrc& ts, auto k0c, auto nkc) {
+    constexpr int hs = decltype(half)::value, hp = 1 - hs;
+    constexpr int K0 = decltype(k0c)::value, NK = decltype(nkc)::value;
+    const int bs = (int)((t % C::NSTAGE) * C::STAGE + hs * 32 * C::KROW) + kbase;  // no chunk bits
+    const char* bp = smem + ((hs == 0 ? t + C::NSTAGE - 1 : t) % C::NSTAGE) * C::STAGE;
+    bf16x8 kf[C::KS], vf[2][C::NB];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) kf[ks] = lds_b128_at(smem, bs ^ (ks << 5));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) vf[h][nb] = lds_b128_at(bp, nb * 32 * C::VTROW + voff[hp][h]);
+    if constexpr (NK > 0) issue_piece(pt, ts, std::integral_constant<int, K0>{});
+    if constexpr (NK > 1) issue_piece(pt, ts, std::integral_constant<int, K0 + 1>{});
+    st = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) st = mfma32(kf[ks], qf[ks], st);
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) o[nb] = mfma32(vf[0][nb], p0, o[nb]);
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) o[nb] = mfma32(vf[1][nb], p1, o[nb]);
+    // Issue order: the K fragment reads, then the score MFMAs each followed by V^T fragment reads
+    // (a direct load after the second and the sixth), then the PV MFMAs; LDS latency hides under
+    // the MFMA chain.
+    static_assert(NK <= 2, "at most two direct loads per MFMA phase");
+    __builtin_amdgcn_sched_group_barrier(0x100, C::KS, 0);
+#pragma unroll
+    for (int i = 0; i < C::KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, (2 * C::NB) / C::KS, 0);
+      if ((NK > 0 && i == 1) || (NK > 1 && i == C::KS - 3)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::NB, 0);
+    __builtin_amdgcn_sched_barrier(0);  // the waits that follow stay after the MFMAs
+  };
+
+  // softmax phase of 32-key block j (tile t = j / 2, half kb = j % 2): mask, online softmax of the
+  // lane's row (the other half-wave holds the row's other keys), P^T as bf16 B operands
+  auto softmax = [&](int t, int kb) {
+    const bool sfx = t >= np;
+    const int key0 = sfx ? (t - np) * C::BN : (pt0 + t) * C::BN;
+    const int nvalid = min(C::BN, (sfx ? R : G.P) - key0);
+    const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
+    if (__builtin_expect(causal || nvalid < C::BN, 0)) {
+      asm volatile("");  // keeps this a real (wave-uniform) branch instead of per-element selects
+      // register r holds tile key 32 kb + 8(r/4) + 4hl + r%4; it is visible iff that key is below
+      // nvalid and (causal tiles) key0 + key <= the row's token
+      const int lim = min(nvalid, causal ? trow - key0 + 1 : nvalid) - kb * 32 - 4 * hl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[r] = (8 * (r >> 2) + (r & 3)) < lim ? st[r] : -INFINITY;
+    }
     float mx = __builtin_elementwise_maximum(st[0], st[1]);
 #pragma unroll
     for (int r = 2; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, st[r]);
     mx = pair_max(mx) * c2;
-    const bool move = mx > mu[rb] + C::kStale;
+    const bool move = mx > mu + C::kStale;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(move) != 0, 0)) {
       asm volatile("");  // rare: a real branch, never speculated into unconditional multiplies
-      const float mnew = move ? mx : mu[rb];
-      const float alpha = move ? fast_exp2(mu[rb] - mnew) : 1.0f;   // 0 on a row's first visible keys
-      mu[rb] = mnew;
-      l_run[rb] *= alpha;
+      const float mnew = move ? mx : mu;
+      const float alpha = move ? fast_exp2(mu - mnew) : 1.0f;   // 0 on a row's first visible keys
+      mu = mnew;
+      l_run *= alpha;
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) o[rb][nb] *= alpha;
+      for (int nb = 0; nb < C::NB; ++nb) o[nb] *= alpha;
     }
-    const float msub = mu[rb] == -INFINITY ? 0.0f : mu[rb];
+    const float msub = mu == -INFINITY ? 0.0f : mu;
     // the row sum is taken in fp32 (the LSE must hold to ~1e-6 even over a few keys)
     float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
@@ -217,122 +281,106 @@ __global__ __launch_bounds__(256, 1) void replay_fwd(FwdArgs a) {
       ls0 += st[r];
       ls1 += st[r + 1];
     }
-    l_run[rb] += ls0 + ls1;
+    l_run += ls0 + ls1;
     p0 = c_regs_to_bf16x8(st, 0);
     p1 = c_regs_to_bf16x8(st, 8);
   };
 
-  auto compute = [&](const char* buf, bool masked, int key0, int nvalid, bool causal) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // S^T = K Q^T for both row blocks; every K fragment feeds two MFMAs
-      bf16x8 kf[C::KS];
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) kf[ks] = lds_b128_at(buf, kb * 32 * C::KROW + koff[ks]);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 st[C::RB];
-#pragma unroll
-      for (int rb = 0; rb < C::RB; ++rb) {
-        st[rb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) st[rb] = mfma32(kf[ks], qf[rb][ks], st[rb]);
-      }
-      // V^T fragments (one 16-byte read of packed slots each) arrive while the scores are formed
-      bf16x8 vf[2][C::NB];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) vf[h][nb] = lds_b128_at(buf, nb * 32 * C::VTROW + voff[kb][h]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (__builtin_expect(masked, 0)) {
-        asm volatile("");  // keeps this a real (wave-uniform) branch instead of per-element selects
-        // register r holds tile key kb*32 + 8(r/4) + 4hl + r%4; it is visible iff that key is below
-        // nvalid and (causal tiles) key0 + key <= the row's token
-#pragma unroll
-        for (int rb = 0; rb < C::RB; ++rb) {
-          const int lim = min(nvalid, causal ? trow[rb] - key0 + 1 : nvalid) - kb * 32 - 4 * hl;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) st[rb][r] = (8 * (r >> 2) + (r & 3)) < lim ? st[rb][r] : -INFINITY;
-        }
-      }
-      // row block 0's softmax runs under row block 1's score MFMAs, row block 1's under
-      // row block 0's PV MFMAs
-      bf16x8 pb[C::RB][2];
-      softmax(0, st[0], pb[0][0], pb[0][1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) o[0][nb] = mfma32(vf[h][nb], pb[0][h], o[0][nb]);
-      __builtin_amdgcn_sched_barrier(0);
-      softmax(1, st[1], pb[1][0], pb[1][1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) o[1][nb] = mfma32(vf[h][nb], pb[1][h], o[1][nb]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  // Both groups run the same program: per 32-key block j, an MFMA phase then a softmax phase, each
+  // opened by a workgroup barrier. The trailing group passes one extra barrier first, so at every
+  // barrier the groups swap roles: while the leading group forms the scores of block j, the
+  // trailing group runs the softmax of block j - 1, and so on. Barrier n (counted over the
+  // workgroup) opens block n / 2 for the leading group.
+  // Ring of four stages: tiles 0-2 are loaded up front; in loop step t (four barriers, two blocks of
+  // tile t) every wave issues its pieces of tile t + 3 into the stage of tile t - 1, which no wave
+  // reads after barrier 4t + 2: half of them inside its MFMA phase after the first barrier of the
+  // step, the rest inside its MFMA phase after the third. Past the last tile the same pieces of
+  // the last tile are loaded again into the unused stage, so every step issues the same number of
+  // loads and the waits below are fixed. Tile t + 1 is first read after barrier 4t + 4; before the
+  // second barrier of step t each wave waits until its pieces of tile t + 1 have landed (only
+  // later tiles' pieces may still be in flight), so that barrier publishes the whole tile for both
+  // groups. Every MFMA phase ends with its LDS reads retired.
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
+  using N0 = std::integral_constant<int, 0>;
+  constexpr int PA = (C::PPW + 1) / 2, PB = C::PPW - PA;  // pieces in the first / second MFMA phase
+  using KA = std::integral_constant<int, 0>;
+  using NA = std::integral_constant<int, PA>;
+  using KB = std::integral_constant<int, PA>;
+  using NB2 = std::integral_constant<int, PB>;
+  auto issue_tile = [&](int t) {
+    const int tt = min(t, nit - 1);
+    const TileSrc ts = tile_src(tt);
+    issue_piece(t, ts, std::integral_constant<int, 0>{});
+    if constexpr (C::PPW > 1) issue_piece(t, ts, std::integral_constant<int, 1>{});
+    if constexpr (C::PPW > 2) issue_piece(t, ts, std::integral_constant<int, 2>{});
+    if constexpr (C::PPW > 3) issue_piece(t, ts, std::integral_constant<int, 3>{});
   };
-
-  // three-stage ring: tile it+2 streams in while tile it is computed. Before computing tile it,
-  // wait for this wave's loads of tile it (tile it+1's stay in flight), then a barrier makes every
-  // wave's part visible and retires all reads of the stage refilled next (tile it-1's).
-  char* const st0 = smem;
-  char* const st1 = smem + C::STAGE;
-  char* const st2 = smem + 2 * C::STAGE;
-  constexpr int kPerTile = C::KINS + C::VINS;
-  if (nit > 0) issue_tile(0, st0);
-  if (nit > 1) issue_tile(1, st1);
-  for (int it = 0; it < nit; it += 3) {
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int t = it + j;
-      if (t >= nit) break;
-      char* cur = j == 0 ? st0 : (j == 1 ? st1 : st2);
-      char* nxt = j == 0 ? st2 : (j == 1 ? st0 : st1);
-      if (t + 1 < nit) wait_vmem_le<kPerTile>();
-      else wait_vmem();
-      __syncthreads();
-      if (t + 2 < nit) issue_tile(t + 2, nxt);
-      const bool sfx = t >= np;
-      const int key0 = sfx ? (t - np) * C::BN : (pt0 + t) * C::BN;
-      const int nvalid = min(C::BN, (sfx ? R : G.P) - key0);
-      const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
-      compute(cur, causal || nvalid < C::BN, key0, nvalid, causal);
-    }
+  if (nit > 0) {
+    issue_tile(0);
+    issue_tile(1);
+    issue_tile(2);
   }
+  {  // the stage read as "tile -1" holds zeros
+    char* z = smem + (C::NSTAGE - 1) * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::STAGE / (16 * 64 * C::NW); ++i)
+      *reinterpret_cast<LSR_LDS u32x4*>(reinterpret_cast<uintptr_t>(z + (i * 64 * C::NW + threadIdx.x) * 16)) =
+          u32x4{0u, 0u, 0u, 0u};
+  }
+  p0 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  p1 = p0;
+  wait_lds();
+  wait_vmem_le<2 * C::PPW>();  // tile 0 before barrier 0: tiles 1 and 2 may be in flight
+  if (!lead) bare_barrier();
+  bare_barrier();
+  const TileSrc ts0 = tile_src(0);
+  mma(0, H0{}, 0, ts0, N0{}, N0{});
+  wait_lds();
+  bare_barrier();
+  for (int t = 0; t < nit; ++t) {
+    const TileSrc ts = tile_src(min(t + 3, nit - 1));
+    softmax(t, 0);
+    bare_barrier();
+    mma(t, H1{}, t + 3, ts, KA{}, NA{});
+    wait_lds();
+    wait_vmem_le<C::PPW + PA>();  // tile t + 1: tile t + 2's pieces and PA of tile t + 3 may be in flight
+    bare_barrier();
+    softmax(t, 1);
+    bare_barrier();
+    mma(t + 1, H0{}, t + 3, ts, KB{}, NB2{});
+    wait_lds();
+    bare_barrier();
+  }
+  if (lead) bare_barrier();
 
+  const float l = pair_sum(l_run);
+  if (!rvalid) return;
+  const int64_t tok = tokb + trow;
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const float lse = l > 0.0f ? (mu + fast_log2(l)) * kLn2 : -INFINITY;
+  if (a.splits == 1) {
+    uint16_t* orow = a.O + (tok * G.Hq + hq) * DV + 4 * hl;
 #pragma unroll
-  for (int rb = 0; rb < C::RB; ++rb) {
-    const float l = pair_sum(l_run[rb]);
-    if (!rvalid[rb]) continue;
-    const int64_t tok = tokb + trow[rb];
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const float lse = l > 0.0f ? (mu[rb] + fast_log2(l)) * kLn2 : -INFINITY;
-    if (a.splits == 1) {
-      uint16_t* orow = a.O + (tok * G.Hq + hq[rb]) * DV + 4 * hl;
+    for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 v = {pack_bf16x2(o[nb][4 * q] * inv, o[nb][4 * q + 1] * inv),
+                         pack_bf16x2(o[nb][4 * q + 2] * inv, o[nb][4 * q + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + nb * 32 + 8 * q) = v;
+      }
+    if (hl == 0) a.lse[(int64_t)hq * G.T + tok] = lse;
+  } else {
+    float* orow = a.o_part + (((int64_t)sp * G.T + tok) * G.Hq + hq) * DV + 4 * hl;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x2 v = {pack_bf16x2(o[rb][nb][4 * q] * inv, o[rb][nb][4 * q + 1] * inv),
-                           pack_bf16x2(o[rb][nb][4 * q + 2] * inv, o[rb][nb][4 * q + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + nb * 32 + 8 * q) = v;
-        }
-      if (hl == 0) a.lse[(int64_t)hq[rb] * G.T + tok] = lse;
-    } else {
-      float* orow = a.o_part + (((int64_t)sp * G.T + tok) * G.Hq + hq[rb]) * DV + 4 * hl;
+    for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = {o[rb][nb][4 * q] * inv, o[rb][nb][4 * q + 1] * inv, o[rb][nb][4 * q + 2] * inv,
-                           o[rb][nb][4 * q + 3] * inv};
-          *reinterpret_cast<f32x4*>(orow + nb * 32 + 8 * q) = v;
-        }
-      if (hl == 0) a.lse_part[((int64_t)sp * G.Hq + hq[rb]) * G.T + tok] = lse;
-    }
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {o[nb][4 * q] * inv, o[nb][4 * q + 1] * inv, o[nb][4 * q + 2] * inv,
+                         o[nb][4 * q + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + nb * 32 + 8 * q) = v;
+      }
+    if (hl == 0) a.lse_part[((int64_t)sp * G.Hq + hq) * G.T + tok] = lse;
   }
 }
 
@@ -413,7 +461,7 @@ hipError_t fwd_go(FwdArgs& a, hipStream_t st) {
   }
   const long long per_xcd = (W + 7) / 8;
   timer_mark(LS_KERNEL_ATTN_FWD, st, false);
-  hipLaunchKernelGGL((replay_fwd<D, DV>), dim3((unsigned)(per_xcd * 8)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((replay_fwd<D, DV>), dim3((unsigned)(per_xcd * 8)), dim3(64 * kFwdWaves), 0, st, a);
   timer_mark(LS_KERNEL_ATTN_FWD, st, true);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
