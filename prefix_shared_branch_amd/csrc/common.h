@@ -123,9 +123,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int
   const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)(uint32_t)n, kBufferWord3);
 }
-// 16 bytes per lane from buffer offset voff into LDS at lds_wave_base + 16 * lane (direct load)
-__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LSR_LDS void*)lds_wave_base, 16, (int)voff, 0, 0, 0);
+// 16 bytes per lane from buffer offset voff + soff into LDS at lds_wave_base + 16 * lane (direct load)
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_wave_base,
+                                              int soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LSR_LDS void*)lds_wave_base, 16, (int)voff, soff, 0, 0);
 }
 __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,

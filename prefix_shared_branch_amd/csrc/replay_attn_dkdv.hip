@@ -133,15 +133,16 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) toff[h] = l32 * C::TROW + (((2 * h + hl) ^ swz<4>(l32)) << 4);
 
-  // per-lane global byte offsets of the direct loads within one step's slabs
+  // Direct loads of a step go through buffer resources over this kv head's packed slabs (one base
+  // per slab; the step moves the scalar offset; loads past a slab's end read as zeros).
   const int64_t mpad = a.mpad;
-  const char* Qr = reinterpret_cast<const char*>(a.Qr + (int64_t)kvh * mpad * D);
-  const char* Or = reinterpret_cast<const char*>(a.dOr + (int64_t)kvh * mpad * DV);
-  const char* QT = reinterpret_cast<const char*>(a.QT + (int64_t)kvh * D * mpad);
-  const char* OT = reinterpret_cast<const char*>(a.dOT + (int64_t)kvh * DV * mpad);
-  const char* LD = reinterpret_cast<const char*>(a.rowstat + (int64_t)kvh * mpad * 2);
-  // lane-constant byte offsets of the direct loads within one step's slabs (the slab bases are
-  // wave-uniform): Q / dO rows row-major with XOR-swizzled chunks, Q^T / dO^T rows of 32 slots
+  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(a.Qr + (int64_t)kvh * mpad * D, mpad * C::QROW);
+  const __amdgpu_buffer_rsrc_t ro = buf_rsrc(a.dOr + (int64_t)kvh * mpad * DV, mpad * C::OROW);
+  const __amdgpu_buffer_rsrc_t rqt = buf_rsrc(a.QT + (int64_t)kvh * D * mpad, (int64_t)D * mpad * 2);
+  const __amdgpu_buffer_rsrc_t rot = buf_rsrc(a.dOT + (int64_t)kvh * DV * mpad, (int64_t)DV * mpad * 2);
+  const __amdgpu_buffer_rsrc_t rld = buf_rsrc(a.rowstat + (int64_t)kvh * mpad * 2, mpad * 8);
+  // lane-constant byte offsets of the direct loads within one step's slabs: Q / dO rows row-major
+  // with XOR-swizzled chunks, Q^T / dO^T rows of 32 slots, 4 bytes of row statistics per lane
   uint32_t qdo[C::QINS], odo[C::OINS], qtdo[C::QTINS], otdo[C::OTINS];
 #pragma unroll
   for (int u = 0; u < C::QINS; ++u) {
@@ -164,23 +165,28 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
     otdo[u] = (uint32_t)(row * mpad * 2 + (((lane & 3) ^ swz<4>(row)) << 4));
   }
   const uint32_t ldo = (uint32_t)lane * 4;
+  // load i of this wave's kPerStep loads of the step at packed row m0 into stage buffer buf. Every
+  // wave also loads the 256 bytes of row statistics (the same bytes; no branch on the wave).
+  constexpr int kPerStep = C::QINS + C::OINS + C::QTINS + C::OTINS + 1;
+  auto issue_load = [&](int i, int m0, char* buf) {
+    if (i < C::QINS) {
+      lds_dma16_buf(rq, qdo[i], buf + (wv * C::QINS + i) * 1024, m0 * C::QROW);
+    } else if (i < C::QINS + C::OINS) {
+      const int u = i - C::QINS;
+      lds_dma16_buf(ro, odo[u], buf + C::OFF_O + (wv * C::OINS + u) * 1024, m0 * C::OROW);
+    } else if (i < C::QINS + C::OINS + C::QTINS) {
+      const int u = i - C::QINS - C::OINS;
+      lds_dma16_buf(rqt, qtdo[u], buf + C::OFF_QT + (wv * C::QTINS + u) * 1024, m0 * 2);
+    } else if (i < kPerStep - 1) {
+      const int u = i - C::QINS - C::OINS - C::QTINS;
+      lds_dma16_buf(rot, otdo[u], buf + C::OFF_OT + (wv * C::OTINS + u) * 1024, m0 * 2);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (LSR_LDS void*)(buf + C::OFF_LD), 4, (int)ldo, m0 * 8, 0, 0);
+    }
+  };
   auto issue_step = [&](int m0, char* buf) {
-    const char* q = Qr + (int64_t)m0 * C::QROW;
-    const char* o = Or + (int64_t)m0 * C::OROW;
-    const char* qt = QT + (int64_t)m0 * 2;
-    const char* ot = OT + (int64_t)m0 * 2;
 #pragma unroll
-    for (int u = 0; u < C::QINS; ++u) lds_dma16(q + qdo[u], buf + (wv * C::QINS + u) * 1024);
-#pragma unroll
-    for (int u = 0; u < C::OINS; ++u) lds_dma16(o + odo[u], buf + C::OFF_O + (wv * C::OINS + u) * 1024);
-#pragma unroll
-    for (int u = 0; u < C::QTINS; ++u) lds_dma16(qt + qtdo[u], buf + C::OFF_QT + (wv * C::QTINS + u) * 1024);
-#pragma unroll
-    for (int u = 0; u < C::OTINS; ++u) lds_dma16(ot + otdo[u], buf + C::OFF_OT + (wv * C::OTINS + u) * 1024);
-    // row statistics: 32 rows x 8 bytes, one 4-byte load per lane of the first wave
-    if (wv == 0)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(LD + (int64_t)m0 * 8 + ldo),
-                                       (__attribute__((address_space(3))) void*)(buf + C::OFF_LD), 4, 0, 0);
+    for (int i = 0; i < kPerStep; ++i) issue_load(i, m0, buf);
   };
 
   const float c2 = G.scale_log2;
@@ -191,7 +197,9 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
 
   // One step: S and dP MFMAs; 2^15 P under the dP MFMAs; dV MFMAs; scaled dS under the dV MFMAs;
   // dK MFMAs. Fragments are read in batches ahead of their MFMAs.
-  auto compute = [&](const char* buf, int m0) {
+  // The loads of the step two ahead (row mn, stage nbuf) are issued between the S and dP MFMAs,
+  // one at a time, so that they enter the memory pipeline spread out.
+  auto compute = [&](const char* buf, int m0, int mn, char* nbuf) {
     // S[row][key] = Q K^T and dP = dO V^T: lane holds key (lane & 31), rows 8(r/4) + 4hl + r%4
     f32x16 s, dp;
     {
@@ -201,12 +209,20 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < C::VS; ++ks) bfr[ks] = lds_b128_at(buf, ooff[ks]);
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kPerStep; ++i) issue_load(i, mn, nbuf);
       s = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) s = mfma32(af[ks], kf[ks], s);
       dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < C::VS; ++ks) dp = mfma32(bfr[ks], vf[ks], dp);
+      static_assert(kPerStep <= C::KS + C::VS, "one load after each MFMA at most");
+#pragma unroll
+      for (int i = 0; i < C::KS + C::VS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < kPerStep) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
     }
     // row statistics of rows 8q + 4hl + 0..3: {l0, d0, l1, d1}, {l2, d2, l3, d3}
     f32x4 st[4][2];
@@ -268,13 +284,19 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // three-stage ring over the steps (same protocol as the forward)
+  // three-stage ring over the steps: before step t each wave waits for its own loads of step t
+  // (step t + 1's may be in flight) and the barrier publishes the step; every wave is then past
+  // step t - 1, whose stage receives step t + 2 (issued inside the step's MFMAs). Past the last
+  // step the last step's rows are loaded again into that free stage, so every step issues the same
+  // number of loads and the wait count is fixed.
   char* const st0 = smem;
   char* const st1 = smem + C::STAGE;
   char* const st2 = smem + 2 * C::STAGE;
-  constexpr int kPerStep = C::QINS + C::OINS + C::QTINS + C::OTINS;  // + 1 on wave 0
-  if (nsteps > 0) issue_step(row_begin, st0);
-  if (nsteps > 1) issue_step(row_begin + C::BR, st1);
+  auto mrow = [&](int t) { return row_begin + min(t, nsteps - 1) * C::BR; };
+  if (nsteps > 0) {
+    issue_step(mrow(0), st0);
+    issue_step(mrow(1), st1);
+  }
   for (int it = 0; it < nsteps; it += 3) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -282,13 +304,9 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
       if (t >= nsteps) break;
       char* cur = j == 0 ? st0 : (j == 1 ? st1 : st2);
       char* nxt = j == 0 ? st2 : (j == 1 ? st0 : st1);
-      // wave 0 issues one extra load per step; waiting for <= kPerStep outstanding is then
-      // conservative for it (it also waits for part of the next step)
-      if (t + 1 < nsteps) wait_vmem_le<kPerStep>();
-      else wait_vmem();
+      wait_vmem_le<kPerStep>();
       __syncthreads();
-      if (t + 2 < nsteps) issue_step(row_begin + (t + 2) * C::BR, nxt);
-      compute(cur, row_begin + t * C::BR);
+      compute(cur, row_begin + t * C::BR, mrow(t + 2), nxt);
     }
   }
 
