@@ -305,7 +305,8 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
       char* cur = j == 0 ? st0 : (j == 1 ? st1 : st2);
       char* nxt = j == 0 ? st2 : (j == 1 ? st0 : st1);
       wait_vmem_le<kPerStep>();
-      __syncthreads();
+      wait_lds();      // this wave's reads of the stage refilled next have returned
+      bare_barrier();  // no fence: it would wait for every direct load in flight
       compute(cur, row_begin + t * C::BR, mrow(t + 2), nxt);
     }
   }

@@ -117,41 +117,66 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
   const int ns = (sp == a.splits - 1) ? (t_hi / C::BN + 1) : 0;
   const int nit = np + ns;
 
-  // global -> LDS for tile `it`: K and V rows (rows past the valid keys re-read the last valid
-  // row: finite data, masked out), packed K^T rows (slots past the keys hold zeros)
-  auto issue_tile = [&](int it, char* buf) {
+  // Direct loads go through buffer resources that end with the key arrays: K / V rows past the last
+  // key read as zeros (masked out: P = 0 there); packed K^T slots past the keys hold zeros.
+  // Lane-constant byte offsets within a tile: K and V rows key-major with XOR-swizzled chunks,
+  // packed K^T rows dimension-major (prompt and response pitches).
+  uint32_t kdo[C::KINS], vdo[C::VINS], tdo[C::TINS], tdr[C::TINS];
+#pragma unroll
+  for (int u = 0; u < C::KINS; ++u) {
+    const int row = (wv * C::KINS + u) * (64 / C::KCH) + lane / C::KCH;
+    kdo[u] = (uint32_t)(row * G.ldk * 2 + (((lane % C::KCH) ^ swz<C::KCH>(row)) << 4));
+  }
+#pragma unroll
+  for (int u = 0; u < C::VINS; ++u) {
+    const int row = (wv * C::VINS + u) * (64 / C::VCH) + lane / C::VCH;
+    vdo[u] = (uint32_t)(row * G.ldv * 2 + (((lane % C::VCH) ^ swz<C::VCH>(row)) << 4));
+  }
+#pragma unroll
+  for (int u = 0; u < C::TINS; ++u) {
+    const int row = (wv * C::TINS + u) * 8 + (lane >> 3);
+    tdo[u] = (uint32_t)(row * a.ppad * 2 + (((lane & 7) ^ swz<8>(row)) << 4));
+    tdr[u] = (uint32_t)(row * a.tpad * 2 + (((lane & 7) ^ swz<8>(row)) << 4));
+  }
+  const char* const kp0 = reinterpret_cast<const char*>(G.Kp + kvh * D);
+  const char* const ks0 = reinterpret_cast<const char*>(G.Ks + (int64_t)tokb * G.ldk + kvh * D);
+  const char* const vp0 = reinterpret_cast<const char*>(G.Vp + kvh * DV);
+  const char* const vs0 = reinterpret_cast<const char*>(G.Vs + (int64_t)tokb * G.ldv + kvh * DV);
+  const char* const tp0 = reinterpret_cast<const char*>(a.KTp + (int64_t)kvh * D * a.ppad);
+  const char* const ts0 = reinterpret_cast<const char*>(a.KTs + (int64_t)kvh * D * a.tpad + a.spos[ri]);
+  const int64_t kp_end = ((int64_t)(G.P - 1) * G.ldk + (int64_t)(G.Hkv - kvh) * D) * 2;
+  const int64_t ks_end = ((int64_t)(G.T - 1 - tokb) * G.ldk + (int64_t)(G.Hkv - kvh) * D) * 2;
+  const int64_t vp_end = ((int64_t)(G.P - 1) * G.ldv + (int64_t)(G.Hkv - kvh) * DV) * 2;
+  const int64_t vs_end = ((int64_t)(G.T - 1 - tokb) * G.ldv + (int64_t)(G.Hkv - kvh) * DV) * 2;
+  const int64_t tp_end = (int64_t)(G.Hkv - kvh) * D * a.ppad * 2;
+  const int64_t ts_end = ((int64_t)(G.Hkv - kvh) * D * a.tpad - a.spos[ri]) * 2;
+  struct TileSrc {
+    __amdgpu_buffer_rsrc_t k, v, t;
+    uint32_t mask;  // all ones for a prompt tile (prompt pitch of the packed K^T), else zero
+  };
+  auto tile_src = [&](int it) {
+    TileSrc ts;
     const bool pr = it < np;
+    ts.mask = pr ? 0xFFFFFFFFu : 0u;
     const int key0 = pr ? (pt0 + it) * C::BN : (it - np) * C::BN;
-    const int nvalid = min(C::BN, (pr ? G.P : R) - key0);
-    const uint16_t* kb = pr ? G.Kp + (int64_t)key0 * G.ldk + kvh * D
-                            : G.Ks + (int64_t)(tokb + key0) * G.ldk + kvh * D;
-    const uint16_t* vb = pr ? G.Vp + (int64_t)key0 * G.ldv + kvh * DV
-                            : G.Vs + (int64_t)(tokb + key0) * G.ldv + kvh * DV;
-    const uint16_t* tb = pr ? a.KTp + (int64_t)kvh * D * a.ppad + key0
-                            : a.KTs + (int64_t)kvh * D * a.tpad + a.spos[ri] + key0;
-    const int64_t tld = pr ? a.ppad : a.tpad;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));  // recompute per tile rather than pin registers for the whole loop
-#pragma unroll
-    for (int u = 0; u < C::KINS; ++u) {
-      const int ins = wv * C::KINS + u;
-      const int row = ins * (64 / C::KCH) + ln / C::KCH;
-      const int c = (ln % C::KCH) ^ swz<C::KCH>(row);
-      lds_dma16(kb + (int64_t)min(row, nvalid - 1) * G.ldk + c * 8, buf + ins * 1024);
-    }
-#pragma unroll
-    for (int u = 0; u < C::VINS; ++u) {
-      const int ins = wv * C::VINS + u;
-      const int row = ins * (64 / C::VCH) + ln / C::VCH;
-      const int c = (ln % C::VCH) ^ swz<C::VCH>(row);
-      lds_dma16(vb + (int64_t)min(row, nvalid - 1) * G.ldv + c * 8, buf + C::KBYTES + ins * 1024);
-    }
-#pragma unroll
-    for (int u = 0; u < C::TINS; ++u) {
-      const int ins = wv * C::TINS + u;
-      const int row = ins * 8 + (ln >> 3);
-      const int c = (ln & 7) ^ swz<8>(row);
-      lds_dma16(tb + (int64_t)row * tld + c * 8, buf + C::KBYTES + C::VBYTES + ins * 1024);
+    const int64_t ko = key0 * G.ldk * 2, vo = key0 * G.ldv * 2, to = (int64_t)key0 * 2;
+    ts.k = buf_rsrc((pr ? kp0 : ks0) + ko, (pr ? kp_end : ks_end) - ko);
+    ts.v = buf_rsrc((pr ? vp0 : vs0) + vo, (pr ? vp_end : vs_end) - vo);
+    ts.t = buf_rsrc((pr ? tp0 : ts0) + to, (pr ? tp_end : ts_end) - to);
+    return ts;
+  };
+  // load i of this wave's kPerTile loads of a tile into stage buffer buf (branch-free: loads are
+  // issued between MFMAs)
+  constexpr int kPerTile = C::KINS + C::VINS + C::TINS;
+  auto issue_load = [&](int i, const TileSrc& ts, char* buf) {
+    if (i < C::KINS) {
+      lds_dma16_buf(ts.k, kdo[i], buf + (wv * C::KINS + i) * 1024);
+    } else if (i < C::KINS + C::VINS) {
+      const int u = i - C::KINS;
+      lds_dma16_buf(ts.v, vdo[u], buf + C::KBYTES + (wv * C::VINS + u) * 1024);
+    } else {
+      const int u = i - C::KINS - C::VINS;
+      lds_dma16_buf(ts.t, (tdo[u] & ts.mask) | (tdr[u] & ~ts.mask), buf + C::KBYTES + C::VBYTES + (wv * C::TINS + u) * 1024);
     }
   };
 
@@ -164,7 +189,10 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
 
   // Per 32-key block: S MFMAs; dP MFMAs with P formed under them; then per row block dS and its dQ
   // MFMAs, row block 1's dS formed under row block 0's MFMAs.
-  auto compute = [&](const char* buf, bool masked, int key0, int nvalid, bool causal) {
+  // The loads of the tile two ahead (source nts, stage nbuf) are issued between the score MFMAs of
+  // the first 32-key block, one at a time.
+  auto compute = [&](const char* buf, bool masked, int key0, int nvalid, bool causal, const TileSrc& nts,
+                     char* nbuf) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       // S^T = K Q^T for both row blocks (each K fragment feeds two MFMAs)
@@ -174,11 +202,23 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) kf[ks] = lds_b128_at(buf, kb * 32 * C::KROW + koff[ks]);
         __builtin_amdgcn_sched_barrier(0);
+        if (kb == 0) {
+#pragma unroll
+          for (int i = 0; i < kPerTile; ++i) issue_load(i, nts, nbuf);
+        }
 #pragma unroll
         for (int rb = 0; rb < C::RB; ++rb) {
           st[rb] = f32x16{};
 #pragma unroll
           for (int ks = 0; ks < C::KS; ++ks) st[rb] = mfma32(kf[ks], qf[rb][ks], st[rb]);
+        }
+        if (kb == 0) {
+          static_assert(kPerTile <= C::RB * C::KS, "one load after each MFMA at most");
+#pragma unroll
+          for (int i = 0; i < C::RB * C::KS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i < kPerTile) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
         }
       }
       // dP^T = V dO^T
@@ -233,12 +273,20 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
     }
   };
 
+  // Three-stage ring: before tile t each wave waits for its own loads of tile t (tile t + 1's may
+  // be in flight) and the barrier publishes the tile; every wave is then past tile t - 1, whose
+  // stage receives tile t + 2 (issued inside the tile's first MFMAs). Past the last tile the last
+  // tile is loaded again into that free stage, so the wait count is fixed.
   char* const st0 = smem;
   char* const st1 = smem + C::STAGE;
   char* const st2 = smem + 2 * C::STAGE;
-  constexpr int kPerTile = C::KINS + C::VINS + C::TINS;
-  if (nit > 0) issue_tile(0, st0);
-  if (nit > 1) issue_tile(1, st1);
+  if (nit > 0) {
+    const TileSrc t0 = tile_src(0), t1 = tile_src(min(1, nit - 1));
+#pragma unroll
+    for (int i = 0; i < kPerTile; ++i) issue_load(i, t0, st0);
+#pragma unroll
+    for (int i = 0; i < kPerTile; ++i) issue_load(i, t1, st1);
+  }
   for (int it = 0; it < nit; it += 3) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -246,15 +294,15 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
       if (t >= nit) break;
       char* cur = j == 0 ? st0 : (j == 1 ? st1 : st2);
       char* nxt = j == 0 ? st2 : (j == 1 ? st0 : st1);
-      if (t + 1 < nit) wait_vmem_le<kPerTile>();
-      else wait_vmem();
-      __syncthreads();
-      if (t + 2 < nit) issue_tile(t + 2, nxt);
+      const TileSrc nts = tile_src(min(t + 2, nit - 1));
+      wait_vmem_le<kPerTile>();
+      wait_lds();      // this wave's reads of the stage refilled next have returned
+      bare_barrier();  // no fence: it would wait for every direct load in flight
       const bool sfx = t >= np;
       const int key0 = sfx ? (t - np) * C::BN : (pt0 + t) * C::BN;
       const int nvalid = min(C::BN, (sfx ? R : G.P) - key0);
       const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
-      compute(cur, causal || nvalid < C::BN, key0, nvalid, causal);
+      compute(cur, causal || nvalid < C::BN, key0, nvalid, causal, nts, nxt);
     }
   }
 
