@@ -14,8 +14,8 @@ namespace {
 // ------------------------------------------------------------------ dQ (query owner, split-K)
 template <int D, int DV>
 struct DqCfg {
-  static constexpr int RB = 2;                // 32-row blocks per wave
-  static constexpr int BM = 4 * 32 * RB;      // packed query rows per workgroup
+  static constexpr int NW = 8;                // waves per workgroup, two per SIMD
+  static constexpr int BM = NW * 32;          // packed query rows per workgroup (32 per wave)
   static_assert(BM == kQTileDq, "dQ tile must match the plan");
   static constexpr int BN = 64;               // keys per tile
   static constexpr int KCH = D / 8;           // 16-byte chunks per K row
@@ -28,23 +28,31 @@ struct DqCfg {
   static constexpr int TBYTES = D * TROW;
   static constexpr int STAGE = KBYTES + VBYTES + TBYTES;
   static constexpr int NSTAGE = 3;
-  static constexpr int KINS = KBYTES / 4096;  // 1 KB direct loads per wave per tile
-  static constexpr int VINS = VBYTES / 4096;
-  static constexpr int TINS = TBYTES / 4096;
+  static constexpr int KP = KBYTES / 1024;    // 1 KB direct-load pieces: K, then V, then K^T
+  static constexpr int VP = VBYTES / 1024;
+  static constexpr int NP = STAGE / 1024;
+  static constexpr int PPW = NP / NW;         // pieces per wave per tile
+  static_assert(KP % NW == 0 && VP % NW == 0 && NP % NW == 0, "pieces split evenly over the waves");
+  static_assert(STAGE % (16 * 64 * NW) == 0, "a stage is zero-filled in whole 16-byte stores");
   static constexpr int KS = D / 16;
   static constexpr int VS = DV / 16;
   static constexpr int DB = D / 32;
 };
 
-// One workgroup = 4 waves x 64 GQA-packed query rows (one wave per SIMD) over the key tiles of one
-// split. Per 64-key tile, K and V (key-major) and the packed K^T (dimension-major, pack.hip layout)
-// stream global -> LDS by direct DMA into a three-stage ring of XOR-swizzled tiles. Per 32-key
-// block each wave recomputes S^T = K Q^T and dP^T = V dO^T for its two row blocks (Q and dO
-// fragments stay in AGPRs; every K or V fragment feeds two MFMAs), forms dS = P (dP - Delta) with
-// P = exp(S scale - LSE), and accumulates dQ^T += K^T dS^T with every K^T fragment a single
-// 16-byte LDS read feeding two MFMAs.
+// compile-time half (32-key block) of a tile
+template <int H>
+using Half = std::integral_constant<int, H>;
+
+// One workgroup = 8 waves x 32 GQA-packed query rows over the key tiles of one split. Per 64-key
+// tile, K and V (key-major) and the packed K^T (dimension-major, pack.hip layout) stream
+// global -> LDS by direct buffer loads into a three-stage ring of XOR-swizzled tiles. Per 32-key
+// block each wave recomputes S^T = K Q^T and dP^T = V dO^T for its rows (Q and dO fragments stay in
+// registers), forms dS = P (dP - Delta) with P = exp(S scale - LSE), and accumulates
+// dQ^T += K^T dS^T with every K^T fragment a single 16-byte LDS read. The two waves on a SIMD run
+// half a step apart (workgroup barriers between phases): one wave's MFMAs overlap the other's
+// exp / dS VALU work.
 template <int D, int DV>
-__global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
+__global__ __launch_bounds__(64 * 8, 1) void replay_bwd_dq(BwdArgs a) {
   using C = DqCfg<D, DV>;
   __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE];
 
@@ -66,44 +74,36 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
   const int m0 = (qt - a.tile0[ri]) * C::BM;
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int hl = lane >> 5;
   const int l32 = lane & 31;
+  const bool lead = wv < 4;  // waves 0-3 run half a step ahead of waves 4-7
 
-  bool rvalid[C::RB];
-  int trow[C::RB], hq[C::RB];
-  float lrow[C::RB], drow[C::RB];
-  bf16x8 qf[C::RB][C::KS], of[C::RB][C::VS];
+  // query row of this lane: packed row m0 + 32 wv + (lane % 32); Q and dO stay in registers
+  const int mrow = m0 + wv * 32 + l32;
+  const bool rvalid = mrow < M;
+  const int trow = rvalid ? mrow / g : 0;
+  const int hq = kvh * g + (rvalid ? mrow - trow * g : 0);
+  const int64_t tok = tokb + trow;
+  bf16x8 qf[C::KS], of[C::VS];
+  {
+    const uint16_t* qrow = G.Q + (tok * G.Hq + hq) * D + hl * 8;
+    const uint16_t* orow = a.dO + (tok * G.Hq + hq) * DV + hl * 8;
 #pragma unroll
-  for (int rb = 0; rb < C::RB; ++rb) {
-    const int mrow = m0 + wv * 32 * C::RB + rb * 32 + l32;
-    rvalid[rb] = mrow < M;
-    trow[rb] = rvalid[rb] ? mrow / g : 0;
-    hq[rb] = kvh * g + (rvalid[rb] ? mrow - trow[rb] * g : 0);
-    const int64_t tok = tokb + trow[rb];
-    const uint16_t* qrow = G.Q + (tok * G.Hq + hq[rb]) * D + hl * 8;
-    const uint16_t* orow = a.dO + (tok * G.Hq + hq[rb]) * DV + hl * 8;
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = rvalid ? ld_bf16x8(qrow + ks * 16) : zero_bf16x8();
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      qf[rb][ks] = rvalid[rb] ? ld_bf16x8(qrow + ks * 16) : zero_bf16x8();
-      asm volatile("" : "+a"(qf[rb][ks]));  // MFMA operands only: AGPRs
-    }
-#pragma unroll
-    for (int ks = 0; ks < C::VS; ++ks) {
-      of[rb][ks] = rvalid[rb] ? ld_bf16x8(orow + ks * 16) : zero_bf16x8();
-      asm volatile("" : "+a"(of[rb][ks]));
-    }
-    // padding rows: LSE = +inf makes P = 0
-    lrow[rb] = rvalid[rb] ? a.lse[(int64_t)hq[rb] * G.T + tok] * kLog2e : INFINITY;
-    drow[rb] = rvalid[rb] ? a.delta[(int64_t)hq[rb] * G.T + tok] : 0.0f;
+    for (int ks = 0; ks < C::VS; ++ks) of[ks] = rvalid ? ld_bf16x8(orow + ks * 16) : zero_bf16x8();
   }
+  // padding rows: LSE = +inf makes P = 0
+  const float lrow = rvalid ? a.lse[(int64_t)hq * G.T + tok] * kLog2e : INFINITY;
+  const float drow = rvalid ? a.delta[(int64_t)hq * G.T + tok] : 0.0f;
 
-  // lane-constant LDS byte offsets within a stage (block offsets are immediates)
-  int koff[C::KS], voff[C::VS], toff[2][2];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = l32 * C::KROW + (((2 * ks + hl) ^ swz<C::KCH>(l32)) << 4);
-#pragma unroll
-  for (int ks = 0; ks < C::VS; ++ks) voff[ks] = C::KBYTES + l32 * C::VROW + (((2 * ks + hl) ^ swz<C::VCH>(l32)) << 4);
+  // lane-constant LDS byte offsets within a stage. A K (V) fragment ks of a lane sits at chunk
+  // (2 ks + hl) ^ swz(l32) of row l32 of its 32-key half; 2 ks and hl occupy different bits, so its
+  // offset is base ^ (ks << 5).
+  const int kbase = l32 * C::KROW + ((hl ^ swz<C::KCH>(l32)) << 4);
+  const int vbase = C::KBYTES + l32 * C::VROW + ((hl ^ swz<C::VCH>(l32)) << 4);
+  int toff[2][2];  // [32-key half][16-key part]: packed slots 32 kb + 16 h + 8 hl .. +7 of dim row l32
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -117,26 +117,25 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
   const int ns = (sp == a.splits - 1) ? (t_hi / C::BN + 1) : 0;
   const int nit = np + ns;
 
-  // Direct loads go through buffer resources that end with the key arrays: K / V rows past the last
-  // key read as zeros (masked out: P = 0 there); packed K^T slots past the keys hold zeros.
-  // Lane-constant byte offsets within a tile: K and V rows key-major with XOR-swizzled chunks,
-  // packed K^T rows dimension-major (prompt and response pitches).
-  uint32_t kdo[C::KINS], vdo[C::VINS], tdo[C::TINS], tdr[C::TINS];
+  // Direct loads: a tile is NP pieces of 1 KB, wave wv moving pieces wv, wv + NW, ... (piece k of
+  // the wave). They go through buffer resources that end with the key arrays: K / V rows past the
+  // last key read as zeros (masked out: P = 0 there); packed K^T slots past the keys hold zeros.
+  // Lane byte offsets within a tile are fixed per piece (prompt and response pitches of K^T).
+  uint32_t pdo[C::PPW], rdo[C::PPW];
 #pragma unroll
-  for (int u = 0; u < C::KINS; ++u) {
-    const int row = (wv * C::KINS + u) * (64 / C::KCH) + lane / C::KCH;
-    kdo[u] = (uint32_t)(row * G.ldk * 2 + (((lane % C::KCH) ^ swz<C::KCH>(row)) << 4));
-  }
-#pragma unroll
-  for (int u = 0; u < C::VINS; ++u) {
-    const int row = (wv * C::VINS + u) * (64 / C::VCH) + lane / C::VCH;
-    vdo[u] = (uint32_t)(row * G.ldv * 2 + (((lane % C::VCH) ^ swz<C::VCH>(row)) << 4));
-  }
-#pragma unroll
-  for (int u = 0; u < C::TINS; ++u) {
-    const int row = (wv * C::TINS + u) * 8 + (lane >> 3);
-    tdo[u] = (uint32_t)(row * a.ppad * 2 + (((lane & 7) ^ swz<8>(row)) << 4));
-    tdr[u] = (uint32_t)(row * a.tpad * 2 + (((lane & 7) ^ swz<8>(row)) << 4));
+  for (int k = 0; k < C::PPW; ++k) {
+    const int pc = k * C::NW + wv;
+    if (pc < C::KP) {
+      const int row = pc * (64 / C::KCH) + lane / C::KCH;
+      pdo[k] = rdo[k] = (uint32_t)(row * G.ldk * 2 + (((lane % C::KCH) ^ swz<C::KCH>(row)) << 4));
+    } else if (pc < C::KP + C::VP) {
+      const int row = (pc - C::KP) * (64 / C::VCH) + lane / C::VCH;
+      pdo[k] = rdo[k] = (uint32_t)(row * G.ldv * 2 + (((lane % C::VCH) ^ swz<C::VCH>(row)) << 4));
+    } else {
+      const int row = (pc - C::KP - C::VP) * 8 + (lane >> 3);
+      pdo[k] = (uint32_t)(row * a.ppad * 2 + (((lane & 7) ^ swz<8>(row)) << 4));
+      rdo[k] = (uint32_t)(row * a.tpad * 2 + (((lane & 7) ^ swz<8>(row)) << 4));
+    }
   }
   const char* const kp0 = reinterpret_cast<const char*>(G.Kp + kvh * D);
   const char* const ks0 = reinterpret_cast<const char*>(G.Ks + (int64_t)tokb * G.ldk + kvh * D);
@@ -165,173 +164,174 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dq(BwdArgs a) {
     ts.t = buf_rsrc((pr ? tp0 : ts0) + to, (pr ? tp_end : ts_end) - to);
     return ts;
   };
-  // load i of this wave's kPerTile loads of a tile into stage buffer buf (branch-free: loads are
-  // issued between MFMAs)
-  constexpr int kPerTile = C::KINS + C::VINS + C::TINS;
-  auto issue_load = [&](int i, const TileSrc& ts, char* buf) {
-    if (i < C::KINS) {
-      lds_dma16_buf(ts.k, kdo[i], buf + (wv * C::KINS + i) * 1024);
-    } else if (i < C::KINS + C::VINS) {
-      const int u = i - C::KINS;
-      lds_dma16_buf(ts.v, vdo[u], buf + C::KBYTES + (wv * C::VINS + u) * 1024);
-    } else {
-      const int u = i - C::KINS - C::VINS;
-      lds_dma16_buf(ts.t, (tdo[u] & ts.mask) | (tdr[u] & ~ts.mask), buf + C::KBYTES + C::VBYTES + (wv * C::TINS + u) * 1024);
-    }
+  // piece k of this wave for tile `it` (branch-free: pieces are issued between MFMAs)
+  auto issue_piece = [&](int it, const TileSrc& ts, int k) {
+    char* dst = smem + (it % C::NSTAGE) * C::STAGE + (k * C::NW + wv) * 1024;
+    if (k * C::NW < C::KP) lds_dma16_buf(ts.k, pdo[k], dst);
+    else if (k * C::NW < C::KP + C::VP) lds_dma16_buf(ts.v, pdo[k], dst);
+    else lds_dma16_buf(ts.t, (pdo[k] & ts.mask) | (rdo[k] & ~ts.mask), dst);
   };
 
-  f32x16 dq[C::RB][C::DB];
+  f32x16 dq[C::DB];
 #pragma unroll
-  for (int rb = 0; rb < C::RB; ++rb)
-#pragma unroll
-    for (int b = 0; b < C::DB; ++b) dq[rb][b] = f32x16{};
+  for (int b = 0; b < C::DB; ++b) dq[b] = f32x16{};
+  f32x16 st, dp;   // S^T then P; dP^T then dS (block of the next softmax phase)
+  bf16x8 d0, d1;   // dS^T of the block whose dQ MFMAs come next (two 16-key B operands)
   const float c2 = G.scale_log2;
 
-  // Per 32-key block: S MFMAs; dP MFMAs with P formed under them; then per row block dS and its dQ
-  // MFMAs, row block 1's dS formed under row block 0's MFMAs.
-  // The loads of the tile two ahead (source nts, stage nbuf) are issued between the score MFMAs of
-  // the first 32-key block, one at a time.
-  auto compute = [&](const char* buf, bool masked, int key0, int nvalid, bool causal, const TileSrc& nts,
-                     char* nbuf) {
+  // MFMA phase of 32-key block j = 2t + hs: S^T and dP^T of block j, dQ^T += K^T dS^T of block j - 1
+  // (block -1 has dS = 0 and reads a zero-filled stage; the scores of block 2 nit, past the last
+  // tile, come from stale LDS data and are never used). With LOADS, the phase also issues this
+  // wave's pieces of tile pt, one after every few MFMAs.
+  auto mma = [&](int t, auto half, auto loads, int pt, const TileSrc& nts) {
+    constexpr int hs = decltype(half)::value, hp = 1 - hs;
+    constexpr bool LOADS = decltype(loads)::value;
+    const char* bs = smem + (t % C::NSTAGE) * C::STAGE + hs * 32 * C::KROW;
+    const char* bv = smem + (t % C::NSTAGE) * C::STAGE + hs * 32 * C::VROW;
+    const char* bp = smem + ((hs == 0 ? t + C::NSTAGE - 1 : t) % C::NSTAGE) * C::STAGE;
+    // Three MFMA runs, each following the reads of its fragments; the next run's fragment reads
+    // are interleaved with the current run's MFMAs (a read lands in the registers an MFMA has just
+    // consumed), so few fragments are live at once and LDS latency hides under the MFMAs.
+    bf16x8 kf[C::KS], vf[C::VS], tf[2][C::DB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // S^T = K Q^T for both row blocks (each K fragment feeds two MFMAs)
-      f32x16 st[C::RB], dp[C::RB];
-      {
-        bf16x8 kf[C::KS];
+    for (int ks = 0; ks < C::KS; ++ks) kf[ks] = lds_b128_at(bs, kbase ^ (ks << 5));
+    __builtin_amdgcn_sched_barrier(0);
+    st = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) kf[ks] = lds_b128_at(buf, kb * 32 * C::KROW + koff[ks]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (kb == 0) {
+    for (int ks = 0; ks < C::KS; ++ks) st = mfma32(kf[ks], qf[ks], st);
 #pragma unroll
-          for (int i = 0; i < kPerTile; ++i) issue_load(i, nts, nbuf);
-        }
+    for (int ks = 0; ks < C::VS; ++ks) vf[ks] = lds_b128_at(bv, vbase ^ (ks << 5));
+    static_assert(C::KS == C::VS && C::VS == 2 * C::DB, "one fragment read per MFMA of the previous run");
 #pragma unroll
-        for (int rb = 0; rb < C::RB; ++rb) {
-          st[rb] = f32x16{};
+    for (int i = 0; i < C::KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    dp = f32x16{};
 #pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks) st[rb] = mfma32(kf[ks], qf[rb][ks], st[rb]);
-        }
-        if (kb == 0) {
-          static_assert(kPerTile <= C::RB * C::KS, "one load after each MFMA at most");
+    for (int ks = 0; ks < C::VS; ++ks) dp = mfma32(vf[ks], of[ks], dp);
 #pragma unroll
-          for (int i = 0; i < C::RB * C::KS; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (i < kPerTile) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          }
-        }
-      }
-      // dP^T = V dO^T
-      {
-        bf16x8 vf[C::VS];
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int ks = 0; ks < C::VS; ++ks) vf[ks] = lds_b128_at(buf, kb * 32 * C::VROW + voff[ks]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int b = 0; b < C::DB; ++b) tf[h][b] = lds_b128_at(bp, b * 32 * C::TROW + toff[hp][h]);
 #pragma unroll
-        for (int rb = 0; rb < C::RB; ++rb) {
-          dp[rb] = f32x16{};
+    for (int i = 0; i < C::VS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int ks = 0; ks < C::VS; ++ks) dp[rb] = mfma32(vf[ks], of[rb][ks], dp[rb]);
-        }
-      }
-      if (__builtin_expect(masked, 0)) {
-        asm volatile("");  // a real (wave-uniform) branch, not per-element selects
-        // register r holds tile key kb*32 + 8(r/4) + 4hl + r%4: visible iff below nvalid and
-        // (causal tiles) key0 + key <= the row's token. Hidden keys get S = -inf, so P = 0.
+    for (int b = 0; b < C::DB; ++b) dq[b] = mfma32(tf[0][b], d0, dq[b]);
 #pragma unroll
-        for (int rb = 0; rb < C::RB; ++rb) {
-          const int lim = min(nvalid, causal ? trow[rb] - key0 + 1 : nvalid) - kb * 32 - 4 * hl;
+    for (int b = 0; b < C::DB; ++b) dq[b] = mfma32(tf[1][b], d1, dq[b]);
+    if constexpr (LOADS) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) st[rb][r] = (8 * (r >> 2) + (r & 3)) < lim ? st[rb][r] : -INFINITY;
-        }
-      }
-      // P = exp(S scale - LSE), under the dP MFMAs
+      for (int k = 0; k < C::PPW; ++k) issue_piece(pt, nts, k);
 #pragma unroll
-      for (int rb = 0; rb < C::RB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[rb][r] = fast_exp2(__builtin_fmaf(st[rb][r], c2, -lrow[rb]));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < C::RB; ++rb) {
-        // dS = P (dP - Delta) as the bf16 B operands of dQ^T += K^T dS^T
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[rb][r] = st[rb][r] * (dp[rb][r] - drow[rb]);
-        const bf16x8 d0 = c_regs_to_bf16x8(st[rb], 0), d1 = c_regs_to_bf16x8(st[rb], 8);
-        // K^T fragments: one 16-byte read of packed slots each
-        bf16x8 tf[2][C::DB];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int b = 0; b < C::DB; ++b) tf[h][b] = lds_b128_at(buf, b * 32 * C::TROW + toff[kb][h]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int b = 0; b < C::DB; ++b) dq[rb][b] = mfma32(tf[0][b], d0, dq[rb][b]);
-#pragma unroll
-        for (int b = 0; b < C::DB; ++b) dq[rb][b] = mfma32(tf[1][b], d1, dq[rb][b]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 2 * C::DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < C::PPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // the waits that follow stay after the MFMAs
   };
 
-  // Three-stage ring: before tile t each wave waits for its own loads of tile t (tile t + 1's may
-  // be in flight) and the barrier publishes the tile; every wave is then past tile t - 1, whose
-  // stage receives tile t + 2 (issued inside the tile's first MFMAs). Past the last tile the last
-  // tile is loaded again into that free stage, so the wait count is fixed.
-  char* const st0 = smem;
-  char* const st1 = smem + C::STAGE;
-  char* const st2 = smem + 2 * C::STAGE;
+  // softmax phase of block (t, kb): mask, P = exp(S scale - LSE), dS = P (dP - Delta) as bf16
+  auto softmax = [&](int t, int kb) {
+    const bool sfx = t >= np;
+    const int key0 = sfx ? (t - np) * C::BN : (pt0 + t) * C::BN;
+    const int nvalid = min(C::BN, (sfx ? R : G.P) - key0);
+    const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
+    if (__builtin_expect(causal || nvalid < C::BN, 0)) {
+      asm volatile("");  // a real (wave-uniform) branch, not per-element selects
+      // register r holds tile key 32 kb + 8(r/4) + 4hl + r%4: visible iff below nvalid and
+      // (causal tiles) key0 + key <= the row's token. Hidden keys get S = -inf, so P = 0.
+      const int lim = min(nvalid, causal ? trow - key0 + 1 : nvalid) - kb * 32 - 4 * hl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[r] = (8 * (r >> 2) + (r & 3)) < lim ? st[r] : -INFINITY;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dp[r] = fast_exp2(__builtin_fmaf(st[r], c2, -lrow)) * (dp[r] - drow);
+    d0 = c_regs_to_bf16x8(dp, 0);
+    d1 = c_regs_to_bf16x8(dp, 8);
+  };
+
+  // Both groups run the same program: per 32-key block j, an MFMA phase then a softmax phase, each
+  // opened by a workgroup barrier; the trailing group passes one extra barrier first, so at every
+  // barrier the groups swap roles. Barrier n opens block n / 2 for the leading group.
+  // Ring of three stages: tiles 0 and 1 are loaded up front; in loop step t (four barriers, the two
+  // blocks of tile t) every wave issues its pieces of tile t + 2 inside its MFMA phase after the
+  // first barrier of the step, into the stage of tile t - 1, which no wave reads after barrier
+  // 4t + 2. Past the last tile the last tile is loaded again into that free stage, so the waits are
+  // fixed. Tile t + 1 is first read after barrier 4t + 4; before the second barrier of step t each
+  // wave waits until its pieces of tile t + 1 have landed (only tile t + 2's may be in flight), so
+  // that barrier publishes the whole tile for both groups. Every MFMA phase ends with its LDS reads
+  // retired.
+  using Off = std::integral_constant<bool, false>;
+  using On = std::integral_constant<bool, true>;
   if (nit > 0) {
     const TileSrc t0 = tile_src(0), t1 = tile_src(min(1, nit - 1));
 #pragma unroll
-    for (int i = 0; i < kPerTile; ++i) issue_load(i, t0, st0);
+    for (int k = 0; k < C::PPW; ++k) issue_piece(0, t0, k);
 #pragma unroll
-    for (int i = 0; i < kPerTile; ++i) issue_load(i, t1, st1);
+    for (int k = 0; k < C::PPW; ++k) issue_piece(1, t1, k);
   }
-  for (int it = 0; it < nit; it += 3) {
+  {  // the stage read as "tile -1" holds zeros
+    char* z = smem + (C::NSTAGE - 1) * C::STAGE;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int t = it + j;
-      if (t >= nit) break;
-      char* cur = j == 0 ? st0 : (j == 1 ? st1 : st2);
-      char* nxt = j == 0 ? st2 : (j == 1 ? st0 : st1);
-      const TileSrc nts = tile_src(min(t + 2, nit - 1));
-      wait_vmem_le<kPerTile>();
-      wait_lds();      // this wave's reads of the stage refilled next have returned
-      bare_barrier();  // no fence: it would wait for every direct load in flight
-      const bool sfx = t >= np;
-      const int key0 = sfx ? (t - np) * C::BN : (pt0 + t) * C::BN;
-      const int nvalid = min(C::BN, (sfx ? R : G.P) - key0);
-      const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
-      compute(cur, causal || nvalid < C::BN, key0, nvalid, causal, nts, nxt);
-    }
+    for (int i = 0; i < C::STAGE / (16 * 64 * C::NW); ++i)
+      *reinterpret_cast<LSR_LDS u32x4*>(reinterpret_cast<uintptr_t>(z + (i * 64 * C::NW + threadIdx.x) * 16)) =
+          u32x4{0u, 0u, 0u, 0u};
   }
+  d0 = zero_bf16x8();
+  d1 = d0;
+  wait_lds();
+  wait_vmem_le<C::PPW>();  // tile 0 before barrier 0: tile 1 may be in flight
+  if (!lead) bare_barrier();
+  const TileSrc tsz = tile_src(0);
+  bare_barrier();
+  mma(0, Half<0>{}, Off{}, 0, tsz);
+  wait_lds();
+  bare_barrier();
+  for (int t = 0; t < nit; ++t) {
+    const TileSrc nts = tile_src(min(t + 2, nit - 1));
+    softmax(t, 0);
+    bare_barrier();
+    mma(t, Half<1>{}, On{}, t + 2, nts);
+    wait_lds();
+    wait_vmem_le<C::PPW>();  // tile t + 1 landed; tile t + 2's pieces may be in flight
+    bare_barrier();
+    softmax(t, 1);
+    bare_barrier();
+    mma(t + 1, Half<0>{}, Off{}, 0, nts);
+    wait_lds();
+    bare_barrier();
+  }
+  if (lead) bare_barrier();
 
   // C layout of dQ^T: lane holds row (lane & 31), dims 32b + 8(r/4) + 4hl + r%4
+  if (!rvalid) return;
   const float sc = G.scale;
+  if (a.splits == 1) {
+    uint16_t* dst = a.dQ + (tok * G.Hq + hq) * D + 4 * hl;
 #pragma unroll
-  for (int rb = 0; rb < C::RB; ++rb) {
-    if (!rvalid[rb]) continue;
-    const int64_t tok = tokb + trow[rb];
-    if (a.splits == 1) {
-      uint16_t* dst = a.dQ + (tok * G.Hq + hq[rb]) * D + 4 * hl;
+    for (int b = 0; b < C::DB; ++b)
 #pragma unroll
-      for (int b = 0; b < C::DB; ++b)
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 v = {pack_bf16x2(dq[b][4 * q] * sc, dq[b][4 * q + 1] * sc),
+                         pack_bf16x2(dq[b][4 * q + 2] * sc, dq[b][4 * q + 3] * sc)};
+        *reinterpret_cast<u32x2*>(dst + b * 32 + 8 * q) = v;
+      }
+  } else {
+    float* dst = a.dq_part + (((int64_t)sp * G.T + tok) * G.Hq + hq) * D + 4 * hl;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x2 v = {pack_bf16x2(dq[rb][b][4 * q] * sc, dq[rb][b][4 * q + 1] * sc),
-                           pack_bf16x2(dq[rb][b][4 * q + 2] * sc, dq[rb][b][4 * q + 3] * sc)};
-          *reinterpret_cast<u32x2*>(dst + b * 32 + 8 * q) = v;
-        }
-    } else {
-      float* dst = a.dq_part + (((int64_t)sp * G.T + tok) * G.Hq + hq[rb]) * D + 4 * hl;
+    for (int b = 0; b < C::DB; ++b)
 #pragma unroll
-      for (int b = 0; b < C::DB; ++b)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = {dq[rb][b][4 * q], dq[rb][b][4 * q + 1], dq[rb][b][4 * q + 2], dq[rb][b][4 * q + 3]};
-          *reinterpret_cast<f32x4*>(dst + b * 32 + 8 * q) = v;
-        }
-    }
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {dq[b][4 * q], dq[b][4 * q + 1], dq[b][4 * q + 2], dq[b][4 * q + 3]};
+        *reinterpret_cast<f32x4*>(dst + b * 32 + 8 * q) = v;
+      }
   }
 }
 
@@ -384,7 +384,7 @@ hipError_t dq_go(BwdArgs& a, hipStream_t st) {
   }
   if ((e = launch_pack_keys_t(p, st)) != hipSuccess) return e;
   timer_mark(LS_KERNEL_DQ, st, false);
-  hipLaunchKernelGGL((replay_bwd_dq<D, DV>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((replay_bwd_dq<D, DV>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(64 * DqCfg<D, DV>::NW), 0, st, a);
   timer_mark(LS_KERNEL_DQ, st, true);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.splits > 1) {
