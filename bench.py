@@ -292,6 +292,18 @@ def main():
         exe += e
     loss_bytes = tokens * (4 * cfg.V + 12)
 
+    # scoring pass of the loss (old / reference policy: log-probs and loss share, no dlogits),
+    # timed after the steps over the same logits: 2V + 12 bytes per token
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev_s[0].record()
+    for i in range(wl.G):
+        L.ls_grpo_token_loss(wl.logits[i], wl.targets[i], wl.old[i], wl.R, wl.rewards, cfg.eps, i, 1, wl.loss,
+                             workspace=wl.ws, scoring_only=True)
+    ev_s[1].record()
+    torch.cuda.synchronize()
+    t_score = ev_s[0].elapsed_time(ev_s[1])
+    score_bytes = tokens * (2 * cfg.V + 12)
+
     # dominant kernel: the dK/dV prompt kernel, timed by the library's kernel timer (HIP events on
     # the launch stream around every launch in the timed region)
     dkdv_ms = dk_total / max(1, dk_launches)
@@ -329,6 +341,8 @@ def main():
             "fwd_alg_TFLOPs": fwd_alg / (t_fwd * 1e-3) / 1e12,
             "loss_GBps": loss_bytes / (t_loss * 1e-3) / 1e9,
             "loss_frac_hbm": loss_bytes / (t_loss * 1e-3) / PEAK_HBM,
+            "scoring_loss_ms_per_group": t_score,
+            "scoring_loss_GBps": score_bytes / (t_score * 1e-3) / 1e9,
             "peak_mem_GiB": torch.cuda.max_memory_allocated() / 2**30,
             "pages_context": "2.1M token positions on eight H20 GPUs (whole model, end to end; not comparable)",
         },

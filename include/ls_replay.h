@@ -137,7 +137,9 @@ int ls_grpo_workspace_bytes(int64_t T, int32_t V, size_t* bytes);
  *  targets   device int32 [T], sampled token ids. An id outside [0, V) is not read from
  *            memory: that row's logp, loss term and dlogits become NaN.
  *  old_logp  device fp32 [T].
- *  dlogits   device bf16 [T, V], overwritten with dL/dlogits (may not alias logits).
+ *  dlogits   device bf16 [T, V], overwritten with dL/dlogits (may not alias logits), or NULL:
+ *            scoring only (log-probs, clip flags and the loss share, no gradient; the logits
+ *            are read once and nothing of size V is written).
  *  loss_accum  device fp32 scalar; this call ADDS its share of L (ordered, deterministic).
  *  logp_out  device fp32 [T] or NULL; clipped_out device uint8 [T] or NULL (1 where the
  *            clipped branch is strictly smaller, so the token's gradient is zero).

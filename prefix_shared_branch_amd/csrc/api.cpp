@@ -210,14 +210,16 @@ int ls_grpo_token_loss(void* stream, int32_t V, int32_t G, const int32_t* R, con
   int64_t T = 0;
   for (int i = first; i < first + count; ++i) T += R[i];
   if (T > INT32_MAX) return LS_ERR_UNSUPPORTED;
-  if (!logits || !targets || !old_logp || !dlogits || !loss_accum) return LS_ERR_INVALID_ARG;
-  if (!aligned(logits, 2) || !aligned(dlogits, 2) || !aligned(targets, 4) || !aligned(old_logp, 4) ||
+  if (!logits || !targets || !old_logp || !loss_accum) return LS_ERR_INVALID_ARG;
+  if (!aligned(logits, 2) || (dlogits && !aligned(dlogits, 2)) || !aligned(targets, 4) || !aligned(old_logp, 4) ||
       !aligned(loss_accum, 4) || (logp_out && !aligned(logp_out, 4)))
     return LS_ERR_INVALID_ARG;
-  const char* lb = static_cast<const char*>(logits);
-  const char* db = static_cast<const char*>(dlogits);
-  const int64_t nbytes = T * (int64_t)V * 2;
-  if (lb < db + nbytes && db < lb + nbytes) return LS_ERR_INVALID_ARG;  // dlogits may not alias logits
+  if (dlogits) {  // dlogits may not alias logits
+    const char* lb = static_cast<const char*>(logits);
+    const char* db = static_cast<const char*>(dlogits);
+    const int64_t nbytes = T * (int64_t)V * 2;
+    if (lb < db + nbytes && db < lb + nbytes) return LS_ERR_INVALID_ARG;
+  }
   const size_t need = lsr::grpo_workspace_bytes(T);
   if (!workspace || !aligned(workspace, 16)) return LS_ERR_WORKSPACE;
   if (workspace_bytes < need) return LS_ERR_WORKSPACE;
@@ -230,7 +232,7 @@ int ls_grpo_token_loss(void* stream, int32_t V, int32_t G, const int32_t* R, con
   for (int i = 0; i < G; ++i) var += (rewards[i] - mean) * (rewards[i] - mean);
   const double sd = std::sqrt(var / G);
 
-  const bool vec = (V % 8) == 0 && aligned(logits, 16) && aligned(dlogits, 16);
+  const bool vec = (V % 8) == 0 && aligned(logits, 16) && (!dlogits || aligned(dlogits, 16));
   hipStream_t st = static_cast<hipStream_t>(stream);
   // responses are launched in batches of at most kMaxResp
   int64_t row0 = 0;

@@ -12,6 +12,8 @@
 //   clipped = clip(rho) A < rho A  (then the gradient is zero)
 //   dlogits = c (softmax(x) - onehot(y)),  c = clipped ? 0 : w A rho
 // The loss is summed by a second single-workgroup kernel in a fixed order (deterministic).
+// Without a dlogits buffer (scoring old or reference policies) the row kernels stop after the
+// per-row outputs: the logits are read once and nothing of size V is written.
 #include "common.h"
 #include "kernels.h"
 
@@ -107,6 +109,7 @@ __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
   s = block_reduce<NT>(s, red, false);
   const float lse = m + fast_log2(s) * kLn2;
   const float c = row_scalar(a, row, xy_s, y_ok, lse);
+  if (a.dlogits == nullptr) return;  // scoring only: no gradient pass
   const float lb = lse * kLog2e;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) asm volatile("" : "+v"(v[j]));
@@ -149,6 +152,7 @@ __global__ __launch_bounds__(256) void grpo_rows_scalar(GrpoArgs a) {
   const float lse = m + fast_log2(s) * kLn2;
   const float xy = y_ok ? bf16_to_f32(x[y]) : 0.0f;
   const float c = row_scalar(a, row, xy, y_ok, lse);
+  if (a.dlogits == nullptr) return;  // scoring only: no gradient pass
   uint16_t* d = a.dlogits + row * (int64_t)a.V;
   for (int e = threadIdx.x; e < a.V; e += NT) {
     float p = fast_exp2((bf16_to_f32(x[e]) - lse) * kLog2e) - ((e == y) ? 1.0f : 0.0f);

@@ -204,9 +204,10 @@ def ls_grpo_workspace_bytes(T: int, V: int) -> int:
 
 
 def ls_grpo_token_loss(logits, targets, old_logp, R, rewards, eps, first, count, loss_accum, dlogits=None,
-                       logp_out=None, clipped_out=None, workspace=None):
+                       logp_out=None, clipped_out=None, workspace=None, scoring_only=False):
     """Clipped-GRPO loss share of responses [first, first+count) added into loss_accum (fp32 [1]);
-    returns dlogits (bf16 [T,V])."""
+    returns dlogits (bf16 [T,V]), or None with scoring_only (no gradient: log-probs, clip flags and
+    the loss share only)."""
     import torch
     T, V = logits.shape
     _check_tensor(logits, "logits", torch.bfloat16)
@@ -215,8 +216,12 @@ def ls_grpo_token_loss(logits, targets, old_logp, R, rewards, eps, first, count,
     _check_tensor(loss_accum, "loss_accum", torch.float32)
     if not logits.is_contiguous():
         raise ValueError("logits must be contiguous")
-    dlogits = torch.empty_like(logits) if dlogits is None else dlogits
-    _check_tensor(dlogits, "dlogits", torch.bfloat16, (T, V))
+    if scoring_only:
+        if dlogits is not None:
+            raise ValueError("scoring_only takes no dlogits buffer")
+    else:
+        dlogits = torch.empty_like(logits) if dlogits is None else dlogits
+        _check_tensor(dlogits, "dlogits", torch.bfloat16, (T, V))
     if logp_out is not None:
         _check_tensor(logp_out, "logp_out", torch.float32, (T,))
     if clipped_out is not None:

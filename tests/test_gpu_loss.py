@@ -123,3 +123,34 @@ def test_loss_invalid_target_gives_nan_row_only():
     assert np.isnan(loss) and np.isnan(logp[2]) and torch.isnan(dl[2].float()).all().item()
     assert np.all(np.isfinite(np.delete(logp, 2)))
     assert torch.isfinite(dl[[0, 1, 3, 4]].float()).all().item()
+
+
+def _run_scoring(d, first, count):
+    import torch
+    from prefix_shared_branch_amd import lsreplay as L
+    cu = np.concatenate([[0], np.cumsum(d["R"])])
+    r0, r1 = cu[first], cu[first + count]
+    T = r1 - r0
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    logp = torch.empty(T, dtype=torch.float32, device="cuda")
+    clip = torch.empty(T, dtype=torch.uint8, device="cuda")
+    dl = L.ls_grpo_token_loss(d["logits"][r0:r1], d["targets"][r0:r1], d["old_d"][r0:r1], d["R"], d["rewards"],
+                              d["cfg"].eps, first, count, loss, logp_out=logp, clipped_out=clip, scoring_only=True)
+    torch.cuda.synchronize()
+    assert dl is None
+    return float(loss.item()), logp.cpu().numpy(), clip.cpu().numpy().astype(bool)
+
+
+@pytest.mark.parametrize("cfgname,lengths,V", [("tiny_clip", None, None), ("mid", [5, 9, 3], None),
+                                               ("tiny_clip", [4, 6], 1001)])
+def test_loss_scoring_only_matches_full_pass_and_oracle(cfgname, lengths, V):
+    """Scoring without dlogits (an old or reference policy pass): same loss, log-probs and clip flags,
+    bit for bit, as the pass that writes dlogits, and the oracle's log-probs."""
+    d = _setup(inputs.CONFIGS[cfgname], lengths=lengths, V=V)
+    G = d["G"]
+    loss_f, _, logp_f, clip_f = _run(d, 0, G)
+    loss_s, logp_s, clip_s = _run_scoring(d, 0, G)
+    assert loss_s == loss_f
+    assert np.array_equal(logp_s, logp_f) and np.array_equal(clip_s, clip_f)
+    logp_ref = grpo.token_logp(d["x"], d["y"])
+    assert np.max(np.abs(logp_s - logp_ref)) <= 1e-4
