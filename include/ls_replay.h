@@ -120,6 +120,43 @@ int ls_replay_attn_bwd(void* stream, const ls_attn_desc* desc,
                        float* dKp_accum, float* dVp_accum,
                        void* workspace, size_t workspace_bytes);
 
+/* Blockwise replay of one long response (LongStraw study notes §3-2, blockwise suffix replay):
+ * the response's query rows are replayed in blocks; block rows q0 .. q0+nq-1 attend to all P
+ * prompt keys and causally to the response's keys 0 .. q0+nq-1 (their own and every earlier
+ * block's), so the blocks together give exactly the full response's attention and gradients.
+ *  q0, nq   first row of the block within the response (>= 0) and its rows (>= 0).
+ *  Q        device bf16 [nq, Hq, Dqk]: the block's queries.
+ *  Ks, Vs   device bf16 [q0 + nq, Hkv, *] with strides ldk/ldv: the response's keys from its
+ *           first token through the block's last.
+ *  O, lse   device bf16 [nq, Hq, Dv] and fp32 [Hq, nq] for the block's rows, overwritten.
+ * Other arguments as in ls_replay_attn_fwd. nq == 0 returns LS_OK and launches nothing. */
+int ls_replay_attn_block_workspace_bytes(const ls_attn_desc* desc, int32_t q0, int32_t nq, int32_t which,
+                                         size_t* bytes);
+int ls_replay_attn_fwd_block(void* stream, const ls_attn_desc* desc,
+                             const void* Kp, const void* Vp,
+                             int32_t q0, int32_t nq,
+                             const void* Q, const void* Ks, const void* Vs,
+                             void* O, float* lse,
+                             void* workspace, size_t workspace_bytes);
+
+/* Backward of one block (arguments as in ls_replay_attn_fwd_block and ls_replay_attn_bwd):
+ *  O, lse, dO  the block's forward outputs and output gradient: [nq, Hq, Dv], [Hq, nq], [nq, Hq, Dv].
+ *  dQ          device bf16 [nq, Hq, Dqk], overwritten (the block's rows only).
+ *  dKs_accum, dVs_accum  device fp32 [q0 + nq, Hkv, Dqk] / [q0 + nq, Hkv, Dv] contiguous, both
+ *              required: the block's contribution to the gradients of the response's keys
+ *              0 .. q0+nq-1 is ADDED (the caller zeroes them before the response's first block).
+ *  dKp_accum, dVp_accum  prompt accumulators as in ls_replay_attn_bwd (exact mode or both NULL).
+ *  workspace   >= ls_replay_attn_block_workspace_bytes(which = 1 exact, 2 response-only).
+ * Blocks of one response that add into the same accumulators must be ordered. */
+int ls_replay_attn_bwd_block(void* stream, const ls_attn_desc* desc,
+                             const void* Kp, const void* Vp,
+                             int32_t q0, int32_t nq,
+                             const void* Q, const void* Ks, const void* Vs,
+                             const void* O, const float* lse, const void* dO,
+                             void* dQ, float* dKs_accum, float* dVs_accum,
+                             float* dKp_accum, float* dVp_accum,
+                             void* workspace, size_t workspace_bytes);
+
 /* Workspace bytes for ls_grpo_token_loss over T rows of vocabulary V (written to *bytes). */
 int ls_grpo_workspace_bytes(int64_t T, int32_t V, size_t* bytes);
 

@@ -37,23 +37,27 @@ int check_cu(int32_t n_resp, const int32_t* cu) {
   return LS_OK;
 }
 
-int plan_for(const ls_attn_desc* d, int32_t n_resp, const int32_t* cu, int which, lsr::AttnPlan* pl) {
+// cu: query-row offsets; kcu: response-key offsets (kcu == cu, or one response whose keys start
+// before its first query row)
+int plan_for(const ls_attn_desc* d, int32_t n_resp, const int32_t* cu, const int32_t* kcu, int which,
+             lsr::AttnPlan* pl) {
   int st = check_desc(d);
   if (st != LS_OK) return st;
   st = check_cu(n_resp, cu);
   if (st != LS_OK) return st;
   // sizes must fit the kernels' 32-bit row arithmetic
   const int64_t T = cu[n_resp];
+  const int64_t Tk = kcu[n_resp];
   const int64_t g = d->Hq / d->Hkv;
-  if (T * d->Hq > INT32_MAX || T * g > INT32_MAX / 2 || (int64_t)d->P + T > INT32_MAX / 2) return LS_ERR_UNSUPPORTED;
+  if (T * d->Hq > INT32_MAX || T * g > INT32_MAX / 2 || (int64_t)d->P + Tk > INT32_MAX / 2) return LS_ERR_UNSUPPORTED;
   // the backward's packed query-row tiles use 32-bit per-lane offsets: Dqk rows of T * g slots
   if ((T * g + 64) * (int64_t)(d->Dqk > d->Dv ? d->Dqk : d->Dv) * 2 > INT32_MAX) return LS_ERR_UNSUPPORTED;
-  if (!lsr::plan_attn(which, d->P, d->Hq, d->Hkv, d->Dqk, d->Dv, n_resp, cu, pl)) return LS_ERR_UNSUPPORTED;
+  if (!lsr::plan_attn(which, d->P, d->Hq, d->Hkv, d->Dqk, d->Dv, n_resp, cu, kcu, pl)) return LS_ERR_UNSUPPORTED;
   return LS_OK;
 }
 
 void fill_geom(lsr::AttnGeom* g, const ls_attn_desc* d, const void* Kp, const void* Vp, int32_t n_resp,
-               const int32_t* cu, const void* Q, const void* Ks, const void* Vs) {
+               const int32_t* cu, const int32_t* kcu, const void* Q, const void* Ks, const void* Vs) {
   g->Kp = static_cast<const uint16_t*>(Kp);
   g->Vp = static_cast<const uint16_t*>(Vp);
   g->Q = static_cast<const uint16_t*>(Q);
@@ -70,7 +74,17 @@ void fill_geom(lsr::AttnGeom* g, const ls_attn_desc* d, const void* Kp, const vo
   g->scale_log2 = d->softmax_scale * 1.4426950408889634f;
   g->n_resp = n_resp;
   for (int i = 0; i <= kMaxResp; ++i) g->tok0[i] = cu[i <= n_resp ? i : n_resp];
+  g->Tk = kcu[n_resp];
+  for (int i = 0; i <= kMaxResp; ++i) g->ktok0[i] = kcu[i <= n_resp ? i : n_resp];
 }
+
+int fwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
+             const int32_t* cu_seqlens, const int32_t* kcu, const void* Q, const void* Ks, const void* Vs, void* O,
+             float* lse, void* workspace, size_t workspace_bytes);
+int bwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
+             const int32_t* cu_seqlens, const int32_t* kcu, const void* Q, const void* Ks, const void* Vs,
+             const void* O, const float* lse, const void* dO, void* dQ, void* dKs, void* dVs, float* dKs_acc,
+             float* dVs_acc, float* dKp_accum, float* dVp_accum, void* workspace, size_t workspace_bytes);
 
 }  // namespace
 
@@ -91,7 +105,7 @@ int ls_replay_attn_workspace_bytes(const ls_attn_desc* desc, int32_t n_resp, con
                                    int32_t which, size_t* bytes) {
   if (!bytes || which < 0 || which > 2) return LS_ERR_INVALID_ARG;
   lsr::AttnPlan pl;
-  const int st = plan_for(desc, n_resp, cu_seqlens, which, &pl);
+  const int st = plan_for(desc, n_resp, cu_seqlens, cu_seqlens, which, &pl);
   if (st != LS_OK) return st;
   *bytes = pl.ws_bytes;
   return LS_OK;
@@ -100,8 +114,58 @@ int ls_replay_attn_workspace_bytes(const ls_attn_desc* desc, int32_t n_resp, con
 int ls_replay_attn_fwd(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
                        const int32_t* cu_seqlens, const void* Q, const void* Ks, const void* Vs, void* O, float* lse,
                        void* workspace, size_t workspace_bytes) {
+  return fwd_impl(stream, desc, Kp, Vp, n_resp, cu_seqlens, cu_seqlens, Q, Ks, Vs, O, lse, workspace,
+                  workspace_bytes);
+}
+
+int ls_replay_attn_bwd(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
+                       const int32_t* cu_seqlens, const void* Q, const void* Ks, const void* Vs, const void* O,
+                       const float* lse, const void* dO, void* dQ, void* dKs, void* dVs, float* dKp_accum,
+                       float* dVp_accum, void* workspace, size_t workspace_bytes) {
+  if (!dKs || !dVs) return LS_ERR_INVALID_ARG;
+  return bwd_impl(stream, desc, Kp, Vp, n_resp, cu_seqlens, cu_seqlens, Q, Ks, Vs, O, lse, dO, dQ, dKs, dVs, nullptr,
+                  nullptr, dKp_accum, dVp_accum, workspace, workspace_bytes);
+}
+
+int ls_replay_attn_block_workspace_bytes(const ls_attn_desc* desc, int32_t q0, int32_t nq, int32_t which,
+                                         size_t* bytes) {
+  if (!bytes || which < 0 || which > 2 || q0 < 0 || nq < 0 || (int64_t)q0 + nq > INT32_MAX) return LS_ERR_INVALID_ARG;
+  const int32_t cu[2] = {0, nq}, kcu[2] = {0, q0 + nq};
   lsr::AttnPlan pl;
-  int st = plan_for(desc, n_resp, cu_seqlens, 0, &pl);
+  const int st = plan_for(desc, 1, cu, kcu, which, &pl);
+  if (st != LS_OK) return st;
+  *bytes = pl.ws_bytes;
+  return LS_OK;
+}
+
+int ls_replay_attn_fwd_block(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t q0,
+                             int32_t nq, const void* Q, const void* Ks, const void* Vs, void* O, float* lse,
+                             void* workspace, size_t workspace_bytes) {
+  if (q0 < 0 || nq < 0 || (int64_t)q0 + nq > INT32_MAX) return LS_ERR_INVALID_ARG;
+  const int32_t cu[2] = {0, nq}, kcu[2] = {0, q0 + nq};
+  return fwd_impl(stream, desc, Kp, Vp, 1, cu, kcu, Q, Ks, Vs, O, lse, workspace, workspace_bytes);
+}
+
+int ls_replay_attn_bwd_block(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t q0,
+                             int32_t nq, const void* Q, const void* Ks, const void* Vs, const void* O,
+                             const float* lse, const void* dO, void* dQ, float* dKs_accum, float* dVs_accum,
+                             float* dKp_accum, float* dVp_accum, void* workspace, size_t workspace_bytes) {
+  if (q0 < 0 || nq < 0 || (int64_t)q0 + nq > INT32_MAX) return LS_ERR_INVALID_ARG;
+  if (!dKs_accum || !dVs_accum) return LS_ERR_INVALID_ARG;
+  const int32_t cu[2] = {0, nq}, kcu[2] = {0, q0 + nq};
+  return bwd_impl(stream, desc, Kp, Vp, 1, cu, kcu, Q, Ks, Vs, O, lse, dO, dQ, nullptr, nullptr, dKs_accum, dVs_accum,
+                  dKp_accum, dVp_accum, workspace, workspace_bytes);
+}
+
+}  // extern "C"
+
+namespace {
+
+int fwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
+             const int32_t* cu_seqlens, const int32_t* kcu, const void* Q, const void* Ks, const void* Vs, void* O,
+             float* lse, void* workspace, size_t workspace_bytes) {
+  lsr::AttnPlan pl;
+  int st = plan_for(desc, n_resp, cu_seqlens, kcu, 0, &pl);
   if (st != LS_OK) return st;
   const int64_t T = cu_seqlens[n_resp];
   if (desc->P > 0 && (!Kp || !Vp || !aligned(Kp, 16) || !aligned(Vp, 16))) return LS_ERR_INVALID_ARG;
@@ -114,7 +178,7 @@ int ls_replay_attn_fwd(void* stream, const ls_attn_desc* desc, const void* Kp, c
 
   lsr::FwdArgs a;
   std::memset(&a, 0, sizeof(a));
-  fill_geom(&a.geo, desc, Kp, Vp, n_resp, cu_seqlens, Q, Ks, Vs);
+  fill_geom(&a.geo, desc, Kp, Vp, n_resp, cu_seqlens, kcu, Q, Ks, Vs);
   a.O = static_cast<uint16_t*>(O);
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);
@@ -134,20 +198,20 @@ int ls_replay_attn_fwd(void* stream, const ls_attn_desc* desc, const void* Kp, c
   return e == hipSuccess ? LS_OK : LS_ERR_HIP;
 }
 
-int ls_replay_attn_bwd(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
-                       const int32_t* cu_seqlens, const void* Q, const void* Ks, const void* Vs, const void* O,
-                       const float* lse, const void* dO, void* dQ, void* dKs, void* dVs, float* dKp_accum,
-                       float* dVp_accum, void* workspace, size_t workspace_bytes) {
+int bwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
+             const int32_t* cu_seqlens, const int32_t* kcu, const void* Q, const void* Ks, const void* Vs,
+             const void* O, const float* lse, const void* dO, void* dQ, void* dKs, void* dVs, float* dKs_acc,
+             float* dVs_acc, float* dKp_accum, float* dVp_accum, void* workspace, size_t workspace_bytes) {
   if ((dKp_accum == nullptr) != (dVp_accum == nullptr)) return LS_ERR_INVALID_ARG;
   const bool exact = dKp_accum != nullptr;
   lsr::AttnPlan pl;
-  int st = plan_for(desc, n_resp, cu_seqlens, exact ? 1 : 2, &pl);
+  int st = plan_for(desc, n_resp, cu_seqlens, kcu, exact ? 1 : 2, &pl);
   if (st != LS_OK) return st;
   const int64_t T = cu_seqlens[n_resp];
   if (desc->P > 0 && (!Kp || !Vp || !aligned(Kp, 16) || !aligned(Vp, 16))) return LS_ERR_INVALID_ARG;
   if (exact && desc->P > 0 && (!aligned(dKp_accum, 16) || !aligned(dVp_accum, 16))) return LS_ERR_INVALID_ARG;
   if (T == 0) return LS_OK;
-  const void* dev[] = {Q, Ks, Vs, O, lse, dO, dQ, dKs, dVs};
+  const void* dev[] = {Q, Ks, Vs, O, lse, dO, dQ, dKs_acc ? dKs_acc : dKs, dVs_acc ? dVs_acc : dVs};
   for (const void* p : dev)
     if (!p || !aligned(p, 16)) return LS_ERR_INVALID_ARG;
   if (pl.ws_bytes > 0 && (!workspace || !aligned(workspace, 256))) return LS_ERR_WORKSPACE;
@@ -155,13 +219,15 @@ int ls_replay_attn_bwd(void* stream, const ls_attn_desc* desc, const void* Kp, c
 
   lsr::BwdArgs a;
   std::memset(&a, 0, sizeof(a));
-  fill_geom(&a.geo, desc, Kp, Vp, n_resp, cu_seqlens, Q, Ks, Vs);
+  fill_geom(&a.geo, desc, Kp, Vp, n_resp, cu_seqlens, kcu, Q, Ks, Vs);
   a.O = static_cast<const uint16_t*>(O);
   a.lse = lse;
   a.dO = static_cast<const uint16_t*>(dO);
   a.dQ = static_cast<uint16_t*>(dQ);
   a.dKs = static_cast<uint16_t*>(dKs);
   a.dVs = static_cast<uint16_t*>(dVs);
+  a.dKs_acc = dKs_acc;
+  a.dVs_acc = dVs_acc;
   a.dKp = exact && desc->P > 0 ? dKp_accum : nullptr;
   a.dVp = exact && desc->P > 0 ? dVp_accum : nullptr;
   char* ws = static_cast<char*>(workspace);
@@ -190,6 +256,10 @@ int ls_replay_attn_bwd(void* stream, const ls_attn_desc* desc, const void* Kp, c
   const hipError_t e = lsr::launch_attn_bwd(a, desc->Dqk, desc->Dv, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LS_OK : LS_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" {
 
 int ls_grpo_workspace_bytes(int64_t T, int32_t V, size_t* bytes) {
   if (!bytes || T < 0 || V < 1) return LS_ERR_INVALID_ARG;

@@ -27,7 +27,8 @@ constexpr int kMaxSplits = 64;
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
-bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, const int32_t* cu, AttnPlan* pl) {
+bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, const int32_t* cu, const int32_t* kcu,
+               AttnPlan* pl) {
   const bool ok = (Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128);
   if (!ok) return false;
   std::memset(pl, 0, sizeof(*pl));
@@ -39,10 +40,11 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
     pl->tile0[i] = qt;
     pl->ktile0[i] = kt;
     pl->spos[i] = sp;
-    const long long R = cu[i + 1] - cu[i];
+    const long long R = cu[i + 1] - cu[i];     // query rows
+    const long long Rk = kcu[i + 1] - kcu[i];  // response keys (>= R: a block's keys start earlier)
     qt += (int)((R * g + kQTile - 1) / kQTile);
-    kt += (int)((R + kDKTile - 1) / kDKTile);
-    sp += (int)((R + kKTile - 1) / kKTile * kKTile);
+    kt += (int)((Rk + kDKTile - 1) / kDKTile);
+    sp += (int)((Rk + kKTile - 1) / kKTile * kKTile);
   }
   for (int i = n_resp; i <= kMaxResp; ++i) {
     pl->tile0[i] = qt;

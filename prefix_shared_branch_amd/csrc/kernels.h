@@ -50,7 +50,12 @@ struct AttnGeom {
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
   int32_t n_resp;
-  int32_t tok0[kMaxResp + 1];   // cu_seqlens
+  int32_t tok0[kMaxResp + 1];   // cu_seqlens: query rows of response i are tok0[i] .. tok0[i+1]-1
+  // Response keys: rows ktok0[i] .. ktok0[i+1]-1 of Ks / Vs (Tk rows in all). A response has at
+  // least as many keys as query rows; query row t sits at key position t + (keys - rows), so a
+  // block of a response (its later rows) sees the keys of the earlier rows too.
+  int32_t Tk;
+  int32_t ktok0[kMaxResp + 1];
 };
 
 // Repacking of per-token rows (pack.hip). Logical row r of head h, dim d is read from
@@ -99,6 +104,7 @@ struct ScaleArgs {
   const uint16_t* Vs;    // response V rows (stride ldv)
   int64_t ldv;
   int64_t T, P;
+  int64_t Tk;            // response V rows
   int32_t Hq, Hkv, Dqk, Dv;
   float* partial;        // [kScaleBlocks, 4]
   float* scales;         // [4]
@@ -128,8 +134,10 @@ struct BwdArgs {
   const float* lse;
   const uint16_t* dO;
   uint16_t* dQ;
-  uint16_t* dKs;
+  uint16_t* dKs;         // bf16 response-key gradients (overwritten), or null with dKs_acc
   uint16_t* dVs;
+  float* dKs_acc;       // or fp32 [Tk, Hkv, Dqk] / [Tk, Hkv, Dv] accumulators the response-key
+  float* dVs_acc;       //   gradients are added into (blocks of one response)
   float* dKp;           // [P, Hkv, Dqk] fp32 accumulators or null
   float* dVp;
   float* delta;         // workspace [Hq, T]: rowsum(dO * O)
@@ -169,7 +177,10 @@ struct AttnPlan {
 };
 
 // which: 0 fwd, 1 bwd exact, 2 bwd response-only. Returns false if (Dqk, Dv) has no kernel.
-bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, const int32_t* cu, AttnPlan* plan);
+// cu: query-row offsets per response; kcu: response-key offsets (kcu = cu except for a block of a
+// response, whose keys start before its first query)
+bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, const int32_t* cu, const int32_t* kcu,
+               AttnPlan* plan);
 hipError_t launch_attn_fwd(FwdArgs& a, int Dqk, int Dv, hipStream_t st);
 hipError_t launch_attn_bwd(BwdArgs& a, int Dqk, int Dv, hipStream_t st);
 // dQ part of the backward (replay_attn_dq.hip): K packing, dQ kernel, split reduction

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void bwd_scale_partials(ScaleArgs a) {
   rows_max<DV>(a.dO, a.T, (int64_t)a.Hq * DV, a.Hq, start, stride, v[0], v[1]);
   rows_max<D>(a.Q, a.T, (int64_t)a.Hq * D, a.Hq, start, stride, v[2], dummy);
   if (a.P > 0) rows_max<DV>(a.Vp, a.P, a.ldv, a.Hkv, start, stride, dummy, v[3]);
-  rows_max<DV>(a.Vs, a.T, a.ldv, a.Hkv, start, stride, dummy, v[3]);
+  rows_max<DV>(a.Vs, a.Tk, a.ldv, a.Hkv, start, stride, dummy, v[3]);
   __shared__ float red[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

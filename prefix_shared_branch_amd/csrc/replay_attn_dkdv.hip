@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
   const int kt = w - kvh * nk;
   const int g = G.g;
 
-  int key0, nkeys, tokb = 0, R = 0, row_begin, row_end;
+  int key0, nkeys, tokb = 0, R = 0, ktokb = 0, qo = 0, row_begin, row_end;
   if (PROMPT) {
     key0 = kt * C::BN;
     nkeys = min(C::BN, G.P - key0);
@@ -84,11 +84,15 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
     while (kt >= a.ktile0[ri + 1]) ++ri;
     tokb = G.tok0[ri];
     R = G.tok0[ri + 1] - tokb;
-    key0 = (kt - a.ktile0[ri]) * C::BN;  // within the response
-    nkeys = min(C::BN, R - key0);
-    // steps start on 32-row boundaries of the packed rows (the slot permutation of the packed
-    // Q^T / dO^T repeats every 16 rows); rows of other responses are masked below
-    row_begin = ((tokb + key0) * g) & ~(C::BR - 1);
+    ktokb = G.ktok0[ri];
+    const int Rk = G.ktok0[ri + 1] - ktokb;  // response keys; query row t sits at key position t + qo
+    qo = Rk - R;
+    key0 = (kt - a.ktile0[ri]) * C::BN;  // within the response's keys
+    nkeys = min(C::BN, Rk - key0);
+    // the first row that sees key key0 sits at key position key0; steps start on 32-row
+    // boundaries of the packed rows (the slot permutation of the packed Q^T / dO^T repeats every
+    // 16 rows); rows of other responses are masked below
+    row_begin = ((tokb + max(0, key0 - qo)) * g) & ~(C::BR - 1);
     row_end = (tokb + R) * g;
   }
 
@@ -103,9 +107,9 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
   bf16x8 kf[C::KS], vf[C::VS];
   {
     const uint16_t* kr = PROMPT ? G.Kp + (int64_t)(key0 + mykey) * G.ldk + kvh * D
-                                : G.Ks + (int64_t)(tokb + key0 + mykey) * G.ldk + kvh * D;
+                                : G.Ks + (int64_t)(ktokb + key0 + mykey) * G.ldk + kvh * D;
     const uint16_t* vr = PROMPT ? G.Vp + (int64_t)(key0 + mykey) * G.ldv + kvh * DV
-                                : G.Vs + (int64_t)(tokb + key0 + mykey) * G.ldv + kvh * DV;
+                                : G.Vs + (int64_t)(ktokb + key0 + mykey) * G.ldv + kvh * DV;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       kf[ks] = kvalid ? ld_bf16x8(kr + ks * 16 + hl * 8) : zero_bf16x8();
@@ -244,9 +248,10 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
       const int q = r >> 2, e = r & 3;
       float pv = fast_exp2(__builtin_fmaf(s[r], c2, -st[q][e >> 1][2 * (e & 1)]));
       if (!PROMPT) {
-        // causal within the response; rows of other responses see none of these keys
+        // causal within the response (row t at key position t + qo); rows of other responses see
+        // none of these keys
         const int t = (m0 + 8 * q + 4 * hl + e) / g - tokb;
-        pv = (key0 + mykey <= t && t < R) ? pv : 0.0f;
+        pv = (t >= 0 && t < R && key0 + mykey <= t + qo) ? pv : 0.0f;
       }
       s[r] = pv;
     }
@@ -335,8 +340,29 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
         const f32x4 add = {dk[b][4 * q] * sc, dk[b][4 * q + 1] * sc, dk[b][4 * q + 2] * sc, dk[b][4 * q + 3] * sc};
         *ptr = *ptr + add;
       }
+  } else if (a.dKs_acc) {
+    // blocks of one response: fp32 sums added into the response-key accumulators
+    const int64_t tok = ktokb + key0 + mykey;
+    float* dvr = a.dVs_acc + (tok * G.Hkv + kvh) * DV + 4 * hl;
+    float* dkr = a.dKs_acc + (tok * G.Hkv + kvh) * D + 4 * hl;
+#pragma unroll
+    for (int b = 0; b < C::VB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4* ptr = reinterpret_cast<f32x4*>(dvr + b * 32 + 8 * q);
+        const f32x4 add = {dv[b][4 * q] * fv, dv[b][4 * q + 1] * fv, dv[b][4 * q + 2] * fv, dv[b][4 * q + 3] * fv};
+        *ptr = *ptr + add;
+      }
+#pragma unroll
+    for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4* ptr = reinterpret_cast<f32x4*>(dkr + b * 32 + 8 * q);
+        const f32x4 add = {dk[b][4 * q] * sc, dk[b][4 * q + 1] * sc, dk[b][4 * q + 2] * sc, dk[b][4 * q + 3] * sc};
+        *ptr = *ptr + add;
+      }
   } else {
-    const int64_t tok = tokb + key0 + mykey;
+    const int64_t tok = ktokb + key0 + mykey;
     uint16_t* dvr = a.dVs + (tok * G.Hkv + kvh) * DV + 4 * hl;
     uint16_t* dkr = a.dKs + (tok * G.Hkv + kvh) * D + 4 * hl;
 #pragma unroll
@@ -370,6 +396,7 @@ hipError_t dkdv_go(BwdArgs& a, hipStream_t st) {
   sa.Vs = G.Vs;
   sa.ldv = G.ldv;
   sa.T = G.T;
+  sa.Tk = G.Tk;
   sa.P = G.P;
   sa.Hq = G.Hq;
   sa.Hkv = G.Hkv;

@@ -69,6 +69,9 @@ __global__ __launch_bounds__(64 * 8, 1) void replay_bwd_dq(BwdArgs a) {
   while (qt >= a.tile0[ri + 1]) ++ri;
   const int tokb = G.tok0[ri];
   const int R = G.tok0[ri + 1] - tokb;
+  const int ktokb = G.ktok0[ri];
+  const int Rk = G.ktok0[ri + 1] - ktokb;  // response keys; query row t sits at key position t + qo
+  const int qo = Rk - R;
   const int g = G.g;
   const int M = R * g;
   const int m0 = (qt - a.tile0[ri]) * C::BM;
@@ -112,8 +115,8 @@ __global__ __launch_bounds__(64 * 8, 1) void replay_bwd_dq(BwdArgs a) {
 
   const int pt0 = sp * a.ptiles_per_split;
   const int np = max(0, min(a.ptiles, pt0 + a.ptiles_per_split) - pt0);
-  const int t_lo = m0 / g;
-  const int t_hi = (min(M, m0 + C::BM) - 1) / g;
+  const int t_lo = m0 / g + qo;                         // key positions of the tile's first and
+  const int t_hi = (min(M, m0 + C::BM) - 1) / g + qo;   // last query rows
   const int ns = (sp == a.splits - 1) ? (t_hi / C::BN + 1) : 0;
   const int nit = np + ns;
 
@@ -138,15 +141,15 @@ __global__ __launch_bounds__(64 * 8, 1) void replay_bwd_dq(BwdArgs a) {
     }
   }
   const char* const kp0 = reinterpret_cast<const char*>(G.Kp + kvh * D);
-  const char* const ks0 = reinterpret_cast<const char*>(G.Ks + (int64_t)tokb * G.ldk + kvh * D);
+  const char* const ks0 = reinterpret_cast<const char*>(G.Ks + (int64_t)ktokb * G.ldk + kvh * D);
   const char* const vp0 = reinterpret_cast<const char*>(G.Vp + kvh * DV);
-  const char* const vs0 = reinterpret_cast<const char*>(G.Vs + (int64_t)tokb * G.ldv + kvh * DV);
+  const char* const vs0 = reinterpret_cast<const char*>(G.Vs + (int64_t)ktokb * G.ldv + kvh * DV);
   const char* const tp0 = reinterpret_cast<const char*>(a.KTp + (int64_t)kvh * D * a.ppad);
   const char* const ts0 = reinterpret_cast<const char*>(a.KTs + (int64_t)kvh * D * a.tpad + a.spos[ri]);
   const int64_t kp_end = ((int64_t)(G.P - 1) * G.ldk + (int64_t)(G.Hkv - kvh) * D) * 2;
-  const int64_t ks_end = ((int64_t)(G.T - 1 - tokb) * G.ldk + (int64_t)(G.Hkv - kvh) * D) * 2;
+  const int64_t ks_end = ((int64_t)(G.Tk - 1 - ktokb) * G.ldk + (int64_t)(G.Hkv - kvh) * D) * 2;
   const int64_t vp_end = ((int64_t)(G.P - 1) * G.ldv + (int64_t)(G.Hkv - kvh) * DV) * 2;
-  const int64_t vs_end = ((int64_t)(G.T - 1 - tokb) * G.ldv + (int64_t)(G.Hkv - kvh) * DV) * 2;
+  const int64_t vs_end = ((int64_t)(G.Tk - 1 - ktokb) * G.ldv + (int64_t)(G.Hkv - kvh) * DV) * 2;
   const int64_t tp_end = (int64_t)(G.Hkv - kvh) * D * a.ppad * 2;
   const int64_t ts_end = ((int64_t)(G.Hkv - kvh) * D * a.tpad - a.spos[ri]) * 2;
   struct TileSrc {
@@ -241,13 +244,13 @@ __global__ __launch_bounds__(64 * 8, 1) void replay_bwd_dq(BwdArgs a) {
   auto softmax = [&](int t, int kb) {
     const bool sfx = t >= np;
     const int key0 = sfx ? (t - np) * C::BN : (pt0 + t) * C::BN;
-    const int nvalid = min(C::BN, (sfx ? R : G.P) - key0);
+    const int nvalid = min(C::BN, (sfx ? Rk : G.P) - key0);
     const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
     if (__builtin_expect(causal || nvalid < C::BN, 0)) {
       asm volatile("");  // a real (wave-uniform) branch, not per-element selects
       // register r holds tile key 32 kb + 8(r/4) + 4hl + r%4: visible iff below nvalid and
-      // (causal tiles) key0 + key <= the row's token. Hidden keys get S = -inf, so P = 0.
-      const int lim = min(nvalid, causal ? trow - key0 + 1 : nvalid) - kb * 32 - 4 * hl;
+      // (causal tiles) key0 + key <= the row's key position. Hidden keys get S = -inf, so P = 0.
+      const int lim = min(nvalid, causal ? trow + qo - key0 + 1 : nvalid) - kb * 32 - 4 * hl;
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[r] = (8 * (r >> 2) + (r & 3)) < lim ? st[r] : -INFINITY;
     }
@@ -378,8 +381,8 @@ hipError_t dq_go(BwdArgs& a, hipStream_t st) {
   p.out = const_cast<uint16_t*>(a.KTs);
   p.nseg = G.n_resp;
   for (int i = 0; i < G.n_resp; ++i) {
-    p.row0[i] = G.tok0[i];
-    p.n[i] = G.tok0[i + 1] - G.tok0[i];
+    p.row0[i] = G.ktok0[i];
+    p.n[i] = G.ktok0[i + 1] - G.ktok0[i];
     p.col0[i] = a.spos[i];
   }
   if ((e = launch_pack_keys_t(p, st)) != hipSuccess) return e;

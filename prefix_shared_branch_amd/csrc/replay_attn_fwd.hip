@@ -93,6 +93,9 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void replay_fwd(FwdArgs a) {
   while (qt >= a.tile0[ri + 1]) ++ri;
   const int tokb = G.tok0[ri];
   const int R = G.tok0[ri + 1] - tokb;
+  const int ktokb = G.ktok0[ri];
+  const int Rk = G.ktok0[ri + 1] - ktokb;  // response keys; query row t sits at key position t + qo
+  const int qo = Rk - R;
   const int g = G.g;
   const int M = R * g;
   const int m0 = (qt - a.tile0[ri]) * C::BM;
@@ -130,8 +133,8 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void replay_fwd(FwdArgs a) {
   // key range: prompt tiles of this split, then (last split) the response's causal tiles
   const int pt0 = sp * a.ptiles_per_split;
   const int np = max(0, min(a.ptiles, pt0 + a.ptiles_per_split) - pt0);
-  const int t_lo = m0 / g;
-  const int t_hi = (min(M, m0 + C::BM) - 1) / g;
+  const int t_lo = m0 / g + qo;                         // key positions of the tile's first and
+  const int t_hi = (min(M, m0 + C::BM) - 1) / g + qo;   // last query rows
   const int ns = (sp == a.splits - 1) ? (t_hi / C::BN + 1) : 0;
   const int nit = np + ns;
 
@@ -157,11 +160,11 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void replay_fwd(FwdArgs a) {
   // the last key read as zeros (those keys are masked out of the softmax); packed V^T slots past the
   // keys hold zeros. Bases and extents are formed once; per tile only the start moves.
   const char* const kp0 = reinterpret_cast<const char*>(G.Kp + kvh * D);
-  const char* const ks0 = reinterpret_cast<const char*>(G.Ks + (int64_t)tokb * G.ldk + kvh * D);
+  const char* const ks0 = reinterpret_cast<const char*>(G.Ks + (int64_t)ktokb * G.ldk + kvh * D);
   const char* const vp0 = reinterpret_cast<const char*>(a.VTp + (int64_t)kvh * DV * a.ppad);
   const char* const vs0 = reinterpret_cast<const char*>(a.VTs + (int64_t)kvh * DV * a.tpad + a.spos[ri]);
   const int64_t kp_end = ((int64_t)(G.P - 1) * G.ldk + (int64_t)(G.Hkv - kvh) * D) * 2;
-  const int64_t ks_end = ((int64_t)(G.T - 1 - tokb) * G.ldk + (int64_t)(G.Hkv - kvh) * D) * 2;
+  const int64_t ks_end = ((int64_t)(G.Tk - 1 - ktokb) * G.ldk + (int64_t)(G.Hkv - kvh) * D) * 2;
   const int64_t vp_end = (int64_t)(G.Hkv - kvh) * DV * a.ppad * 2;
   const int64_t vs_end = ((int64_t)(G.Hkv - kvh) * DV * a.tpad - a.spos[ri]) * 2;
   const int64_t ldk2 = G.ldk * 2;
@@ -247,13 +250,13 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void replay_fwd(FwdArgs a) {
   auto softmax = [&](int t, int kb) {
     const bool sfx = t >= np;
     const int key0 = sfx ? (t - np) * C::BN : (pt0 + t) * C::BN;
-    const int nvalid = min(C::BN, (sfx ? R : G.P) - key0);
+    const int nvalid = min(C::BN, (sfx ? Rk : G.P) - key0);
     const bool causal = sfx && (key0 + C::BN - 1 > t_lo);
     if (__builtin_expect(causal || nvalid < C::BN, 0)) {
       asm volatile("");  // keeps this a real (wave-uniform) branch instead of per-element selects
       // register r holds tile key 32 kb + 8(r/4) + 4hl + r%4; it is visible iff that key is below
-      // nvalid and (causal tiles) key0 + key <= the row's token
-      const int lim = min(nvalid, causal ? trow - key0 + 1 : nvalid) - kb * 32 - 4 * hl;
+      // nvalid and (causal tiles) key0 + key <= the row's key position
+      const int lim = min(nvalid, causal ? trow + qo - key0 + 1 : nvalid) - kb * 32 - 4 * hl;
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[r] = (8 * (r >> 2) + (r & 3)) < lim ? st[r] : -INFINITY;
     }
@@ -449,8 +452,8 @@ hipError_t fwd_go(FwdArgs& a, hipStream_t st) {
     p.hstride = DV;
     p.nseg = G.n_resp;
     for (int i = 0; i < G.n_resp; ++i) {
-      p.row0[i] = G.tok0[i];
-      p.n[i] = G.tok0[i + 1] - G.tok0[i];
+      p.row0[i] = G.ktok0[i];
+      p.n[i] = G.ktok0[i + 1] - G.ktok0[i];
       p.col0[i] = a.spos[i];
     }
     p.out = const_cast<uint16_t*>(a.VTs);

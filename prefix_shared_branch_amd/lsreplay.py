@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "liblsreplay.so")
 LS_OK, LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP = 0, -1, -2, -3, -4
 LS_MAX_RESPONSES_PER_CALL = 64
 EXPORTED = ("ls_replay_attn_workspace_bytes", "ls_replay_attn_fwd", "ls_replay_attn_bwd",
+            "ls_replay_attn_block_workspace_bytes", "ls_replay_attn_fwd_block", "ls_replay_attn_bwd_block",
             "ls_grpo_workspace_bytes", "ls_grpo_token_loss", "ls_status_string", "ls_kernel_timer_start",
             "ls_kernel_timer_stop")
 LS_KERNEL_ATTN_FWD, LS_KERNEL_DKDV_PROMPT, LS_KERNEL_DQ, LS_KERNEL_GRPO_ROWS = 0, 1, 2, 3
@@ -59,6 +60,13 @@ def lib():
         L.ls_replay_attn_bwd.restype = ctypes.c_int
         L.ls_replay_attn_bwd.argtypes = [vp, pdesc, vp, vp, i32, pi32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          vp, sz]
+        L.ls_replay_attn_block_workspace_bytes.restype = ctypes.c_int
+        L.ls_replay_attn_block_workspace_bytes.argtypes = [pdesc, i32, i32, i32, ctypes.POINTER(sz)]
+        L.ls_replay_attn_fwd_block.restype = ctypes.c_int
+        L.ls_replay_attn_fwd_block.argtypes = [vp, pdesc, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz]
+        L.ls_replay_attn_bwd_block.restype = ctypes.c_int
+        L.ls_replay_attn_bwd_block.argtypes = [vp, pdesc, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               vp, vp, sz]
         L.ls_grpo_workspace_bytes.restype = ctypes.c_int
         L.ls_grpo_workspace_bytes.argtypes = [i64, i32, ctypes.POINTER(sz)]
         L.ls_grpo_token_loss.restype = ctypes.c_int
@@ -195,6 +203,69 @@ def ls_replay_attn_bwd(q, ks, vs, kp, vp, cu_seqlens, o, lse, do, dkp_accum=None
         len(cu) - 1, cup, _ptr(q), _ptr(ks), _ptr(vs), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dks), _ptr(dvs),
         _ptr(dkp_accum), _ptr(dvp_accum), _ptr(ws), ws.numel()))
     return dq, dks, dvs
+
+
+def ls_replay_attn_block_workspace_bytes(desc: AttnDesc, q0: int, nq: int, which: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("ls_replay_attn_block_workspace_bytes",
+           lib().ls_replay_attn_block_workspace_bytes(ctypes.byref(desc), int(q0), int(nq), int(which),
+                                                      ctypes.byref(out)))
+    return int(out.value)
+
+
+def ls_replay_attn_fwd_block(q, ks, vs, kp, vp, q0, scale=None, out=None, lse=None, workspace=None):
+    """Forward of rows q0 .. q0+nq-1 of one response (q [nq,Hq,Dqk]; ks/vs hold the response's keys
+    0 .. q0+nq-1). Returns (O [nq,Hq,Dv] bf16, LSE [Hq,nq] fp32)."""
+    import torch
+    desc = make_desc(q, kp, vp, ks, vs, scale)
+    nq, Hq = q.shape[0], q.shape[1]
+    for n, t in (("q", q), ("ks", ks), ("vs", vs), ("kp", kp), ("vp", vp)):
+        _check_tensor(t, n, torch.bfloat16)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if ks.shape[0] != q0 + nq or vs.shape[0] != q0 + nq:
+        raise ValueError(f"ks/vs must hold the response's keys 0 .. q0+nq-1 ({q0 + nq} rows)")
+    out = torch.empty(nq, Hq, desc.Dv, dtype=torch.bfloat16, device=q.device) if out is None else out
+    lse = torch.empty(Hq, nq, dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor(out, "out", torch.bfloat16, (nq, Hq, desc.Dv))
+    _check_tensor(lse, "lse", torch.float32, (Hq, nq))
+    ws = _workspace(ls_replay_attn_block_workspace_bytes(desc, q0, nq, 0), q.device, workspace)
+    _check("ls_replay_attn_fwd_block", lib().ls_replay_attn_fwd_block(
+        _stream(), ctypes.byref(desc), _ptr(kp) if kp.numel() else None, _ptr(vp) if vp.numel() else None,
+        int(q0), int(nq), _ptr(q), _ptr(ks), _ptr(vs), _ptr(out), _ptr(lse), _ptr(ws), ws.numel()))
+    return out, lse
+
+
+def ls_replay_attn_bwd_block(q, ks, vs, kp, vp, q0, o, lse, do, dks_accum, dvs_accum, dkp_accum=None,
+                             dvp_accum=None, scale=None, dq=None, workspace=None):
+    """Backward of one block: returns dQ [nq,Hq,Dqk] bf16 and ADDS the block's key gradients into
+    dks_accum/dvs_accum (fp32 [q0+nq,Hkv,*]) and, in exact mode, into dkp_accum/dvp_accum."""
+    import torch
+    desc = make_desc(q, kp, vp, ks, vs, scale)
+    nq, Hq = q.shape[0], q.shape[1]
+    for n, t in (("q", q), ("ks", ks), ("vs", vs), ("kp", kp), ("vp", vp), ("o", o), ("do", do)):
+        _check_tensor(t, n, torch.bfloat16)
+    _check_tensor(lse, "lse", torch.float32, (Hq, nq))
+    if ks.shape[0] != q0 + nq or vs.shape[0] != q0 + nq:
+        raise ValueError(f"ks/vs must hold the response's keys 0 .. q0+nq-1 ({q0 + nq} rows)")
+    _check_tensor(dks_accum, "dks_accum", torch.float32, (q0 + nq, desc.Hkv, desc.Dqk))
+    _check_tensor(dvs_accum, "dvs_accum", torch.float32, (q0 + nq, desc.Hkv, desc.Dv))
+    if (dkp_accum is None) != (dvp_accum is None):
+        raise ValueError("dkp_accum and dvp_accum must both be given or both be None")
+    if dkp_accum is not None:
+        _check_tensor(dkp_accum, "dkp_accum", torch.float32, (desc.P, desc.Hkv, desc.Dqk))
+        _check_tensor(dvp_accum, "dvp_accum", torch.float32, (desc.P, desc.Hkv, desc.Dv))
+    for n, t in (("q", q), ("o", o), ("do", do), ("dks_accum", dks_accum), ("dvs_accum", dvs_accum)):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    dq = torch.empty(nq, Hq, desc.Dqk, dtype=torch.bfloat16, device=q.device) if dq is None else dq
+    ws = _workspace(ls_replay_attn_block_workspace_bytes(desc, q0, nq, 1 if dkp_accum is not None else 2),
+                    q.device, workspace)
+    _check("ls_replay_attn_bwd_block", lib().ls_replay_attn_bwd_block(
+        _stream(), ctypes.byref(desc), _ptr(kp) if kp.numel() else None, _ptr(vp) if vp.numel() else None,
+        int(q0), int(nq), _ptr(q), _ptr(ks), _ptr(vs), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dks_accum),
+        _ptr(dvs_accum), _ptr(dkp_accum), _ptr(dvp_accum), _ptr(ws), ws.numel()))
+    return dq
 
 
 def ls_grpo_workspace_bytes(T: int, V: int) -> int:

@@ -110,6 +110,39 @@ def test_fwd_bwd_pointer_and_workspace_validation():
     assert _bwd(d, [0, 10], nbytes=0) == L.LS_ERR_WORKSPACE
 
 
+def _block_ws(d, q0, nq, which=0):
+    n = ctypes.c_size_t(0)
+    return L.lib().ls_replay_attn_block_workspace_bytes(ctypes.byref(d), q0, nq, which, ctypes.byref(n)), n.value
+
+
+def _fwd_block(d, q0, nq, Q=BAD, Ks=BAD, ws=BAD, nbytes=1 << 40):
+    return L.lib().ls_replay_attn_fwd_block(None, ctypes.byref(d), BAD, BAD, q0, nq, Q, Ks, BAD, BAD, BAD, ws, nbytes)
+
+
+def _bwd_block(d, q0, nq, dKs=BAD, dVs=BAD, dKp=BAD, dVp=BAD, ws=BAD, nbytes=1 << 40):
+    return L.lib().ls_replay_attn_bwd_block(None, ctypes.byref(d), BAD, BAD, q0, nq, BAD, BAD, BAD, BAD, BAD, BAD,
+                                            BAD, dKs, dVs, dKp, dVp, ws, nbytes)
+
+
+def test_block_validation():
+    d = desc()
+    assert _block_ws(d, -1, 10)[0] == L.LS_ERR_INVALID_ARG
+    assert _block_ws(d, 0, -1)[0] == L.LS_ERR_INVALID_ARG
+    assert _block_ws(d, 0, 10, which=3)[0] == L.LS_ERR_INVALID_ARG
+    rc0, n0 = _block_ws(d, 0, 100)
+    rc1, n1 = _block_ws(d, 900, 100)
+    assert rc0 == L.LS_OK and rc1 == L.LS_OK and n1 > n0    # the block's earlier keys are packed too
+    assert _block_ws(desc(Dqk=96, Dv=96, ldk=192, ldv=192), 0, 10)[0] == L.LS_ERR_UNSUPPORTED
+    assert _fwd_block(d, -5, 10) == L.LS_ERR_INVALID_ARG
+    assert _fwd_block(d, 5, 10, Q=None) == L.LS_ERR_INVALID_ARG
+    assert _fwd_block(d, 5, 10, Ks=ctypes.c_void_p(0x1008)) == L.LS_ERR_INVALID_ARG  # misaligned
+    assert _fwd_block(d, 5, 0) == L.LS_OK                                           # nothing to do
+    assert _bwd_block(d, 5, 10, dKs=None) == L.LS_ERR_INVALID_ARG                   # key accumulators required
+    assert _bwd_block(d, 5, 10, dVs=None) == L.LS_ERR_INVALID_ARG
+    assert _bwd_block(d, 5, 10, dKp=None) == L.LS_ERR_INVALID_ARG                   # exactly one prompt accumulator
+    assert _bwd_block(d, 5, 10, nbytes=0) == L.LS_ERR_WORKSPACE
+
+
 def _loss(V=4096, G=2, R=(3, 4), rewards=(0.0, 1.0), eps=0.2, first=0, count=2, logits=BAD, dl=ctypes.c_void_p(0x90000),
           ws=BAD, nbytes=1 << 30, targets=BAD):
     Ra = np.asarray(R, dtype=np.int32)
