@@ -13,7 +13,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblsreplay.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-HIP_SOURCES = ["grpo_loss.hip", "replay_attn_fwd.hip", "replay_attn_bwd.hip", "replay_attn_dq.hip", "replay_attn_dkdv.hip", "pack.hip"]
+HIP_SOURCES = ["grpo_loss.hip", "replay_attn_fwd.hip", "replay_attn_bwd.hip", "replay_attn_dq.hip", "replay_attn_dkdv.hip", "pack.hip",
+               "replay_attn_wide_fwd.hip", "replay_attn_wide_bwd.hip"]
 CXX_SOURCES = ["api.cpp", "attn_plan.cpp", "timer.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 # the packed-fp32 feature stays off: every v_pk_*_f32 is left out of the kernels
@@ -23,7 +24,8 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "
 # ops, which cannot address AGPRs, and the default AGPR form copies them back and forth.
 SOURCE_FLAGS = {"replay_attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                 "replay_attn_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "replay_attn_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+                "replay_attn_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "replay_attn_wide_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):

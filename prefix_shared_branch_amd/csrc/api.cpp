@@ -23,8 +23,18 @@ int check_desc(const ls_attn_desc* d) {
   if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.0f)) return LS_ERR_INVALID_ARG;
   if (d->ldk < (int64_t)d->Hkv * d->Dqk || d->ldv < (int64_t)d->Hkv * d->Dv) return LS_ERR_INVALID_ARG;
   if ((d->ldk % 8) != 0 || (d->ldv % 8) != 0) return LS_ERR_INVALID_ARG;
-  const bool ok_shape = (d->Dqk == 64 && d->Dv == 64) || (d->Dqk == 128 && d->Dv == 128);
+  const bool wide = d->Dqk == lsr::kWideDqk && d->Dv == lsr::kWideDv;
+  const bool ok_shape = (d->Dqk == 64 && d->Dv == 64) || (d->Dqk == 128 && d->Dv == 128) || wide;
   if (!ok_shape) return LS_ERR_UNSUPPORTED;
+  // latent KV: one kv head whose V rows are the leading Dv dims of the K rows (same row stride)
+  if (wide && (d->Hkv != 1 || d->ldv != d->ldk)) return LS_ERR_UNSUPPORTED;
+  return LS_OK;
+}
+
+// latent-KV heads: V must alias K (the wide kernels read both from the K rows)
+int check_alias(const ls_attn_desc* d, const void* Kp, const void* Vp, const void* Ks, const void* Vs) {
+  if (d->Dqk != lsr::kWideDqk) return LS_OK;
+  if (Vs != Ks || (d->P > 0 && Vp != Kp)) return LS_ERR_UNSUPPORTED;
   return LS_OK;
 }
 
@@ -169,6 +179,7 @@ int fwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void*
   if (st != LS_OK) return st;
   const int64_t T = cu_seqlens[n_resp];
   if (desc->P > 0 && (!Kp || !Vp || !aligned(Kp, 16) || !aligned(Vp, 16))) return LS_ERR_INVALID_ARG;
+  if ((st = check_alias(desc, Kp, Vp, Ks, Vs)) != LS_OK) return st;
   if (T == 0) return LS_OK;
   const void* dev[] = {Q, Ks, Vs, O, lse};
   for (const void* p : dev)
@@ -210,6 +221,7 @@ int bwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void*
   const int64_t T = cu_seqlens[n_resp];
   if (desc->P > 0 && (!Kp || !Vp || !aligned(Kp, 16) || !aligned(Vp, 16))) return LS_ERR_INVALID_ARG;
   if (exact && desc->P > 0 && (!aligned(dKp_accum, 16) || !aligned(dVp_accum, 16))) return LS_ERR_INVALID_ARG;
+  if ((st = check_alias(desc, Kp, Vp, Ks, Vs)) != LS_OK) return st;
   if (T == 0) return LS_OK;
   const void* dev[] = {Q, Ks, Vs, O, lse, dO, dQ, dKs_acc ? dKs_acc : dKs, dVs_acc ? dVs_acc : dVs};
   for (const void* p : dev)
@@ -245,7 +257,7 @@ int bwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void*
   a.rowstat = reinterpret_cast<float*>(ws + pl.off_rs);
   a.mpad = pl.mpad;
   a.scale_part = reinterpret_cast<float*>(ws + pl.off_sc);
-  a.scales = a.scale_part + lsr::kScaleBlocks * 4;
+  a.scales = a.scale_part + lsr::kScaleBlocks * 8;
   a.KTp = reinterpret_cast<const uint16_t*>(ws + pl.off_c);
   a.KTs = reinterpret_cast<const uint16_t*>(ws + pl.off_d);
   a.ppad = pl.ppad;

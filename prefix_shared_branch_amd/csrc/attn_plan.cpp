@@ -19,7 +19,7 @@ namespace lsr {
 
 namespace {
 constexpr int kKTile = 64;    // keys per forward / dQ tile
-constexpr int kDKTile = 128;  // keys per dK/dV workgroup
+constexpr int kDKTileStd = 128;  // keys per dK/dV workgroup (latent-KV heads: kDKTileWide)
 constexpr int kTargetBlocks = 2048;
 constexpr int kMinTilesPerSplit = 8;
 constexpr int kMaxSplits = 64;
@@ -29,12 +29,14 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, const int32_t* cu, const int32_t* kcu,
                AttnPlan* pl) {
-  const bool ok = (Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128);
+  const bool wide = Dqk == kWideDqk && Dv == kWideDv && Hkv == 1;
+  const bool ok = (Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128) || wide;
   if (!ok) return false;
   std::memset(pl, 0, sizeof(*pl));
   const int g = Hq / Hkv;
   const long long T = cu[n_resp];
-  const int kQTile = which == 0 ? kQTileFwd : kQTileDq;
+  const int kQTile = wide ? (which == 0 ? kQTileFwdWide : kQTileDqWide) : (which == 0 ? kQTileFwd : kQTileDq);
+  const int kDKTile = wide ? kDKTileWide : kDKTileStd;
   int qt = 0, kt = 0, sp = 0;
   for (int i = 0; i < n_resp; ++i) {
     pl->tile0[i] = qt;
@@ -76,11 +78,13 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
       pl->off_b = off;
       off = align256(off + (size_t)S * Hq * T * 4);
     }
-    // dimension-major packed V of the prompt and of the responses
-    pl->off_c = off;
-    off = align256(off + (size_t)Hkv * Dv * pl->ppad * 2);
-    pl->off_d = off;
-    off = align256(off + (size_t)Hkv * Dv * pl->tpad * 2);
+    // dimension-major packed V of the prompt and of the responses (latent KV: read from the K tiles)
+    if (!wide) {
+      pl->off_c = off;
+      off = align256(off + (size_t)Hkv * Dv * pl->ppad * 2);
+      pl->off_d = off;
+      off = align256(off + (size_t)Hkv * Dv * pl->tpad * 2);
+    }
   } else {
     pl->off_a = off;  // delta [Hq, T]
     off = align256(off + (size_t)Hq * T * 4);
@@ -88,25 +92,30 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
       pl->off_b = off;
       off = align256(off + (size_t)S * T * Hq * Dqk * 4);
     }
-    // dimension-major packed K of the prompt and of the responses (dQ kernel)
-    pl->off_c = off;
-    off = align256(off + (size_t)Hkv * Dqk * pl->ppad * 2);
-    pl->off_d = off;
-    off = align256(off + (size_t)Hkv * Dqk * pl->tpad * 2);
-    // packed query rows of every kv head (dK/dV kernels)
+    // dimension-major packed K of the prompt and of the responses (dQ kernel; latent KV: read from
+    // the K tiles by transposed LDS reads)
+    if (!wide) {
+      pl->off_c = off;
+      off = align256(off + (size_t)Hkv * Dqk * pl->ppad * 2);
+      pl->off_d = off;
+      off = align256(off + (size_t)Hkv * Dqk * pl->tpad * 2);
+    }
+    // packed query rows of every kv head (dK/dV kernels); latent KV: row-major only
     pl->mpad = (T * g + 63) / 64 * 64;
     pl->off_qr = off;
     off = align256(off + (size_t)Hkv * pl->mpad * Dqk * 2);
     pl->off_or = off;
     off = align256(off + (size_t)Hkv * pl->mpad * Dv * 2);
-    pl->off_qt = off;
-    off = align256(off + (size_t)Hkv * pl->mpad * Dqk * 2);
-    pl->off_ot = off;
-    off = align256(off + (size_t)Hkv * pl->mpad * Dv * 2);
+    if (!wide) {
+      pl->off_qt = off;
+      off = align256(off + (size_t)Hkv * pl->mpad * Dqk * 2);
+      pl->off_ot = off;
+      off = align256(off + (size_t)Hkv * pl->mpad * Dv * 2);
+    }
     pl->off_rs = off;
     off = align256(off + (size_t)Hkv * pl->mpad * 8);
-    pl->off_sc = off;  // fp16 operand scales: partial maxima, then the 4 scales
-    off = align256(off + (size_t)(kScaleBlocks + 1) * 4 * 4);
+    pl->off_sc = off;  // fp16 operand scales: partial maxima (8 per block), then the scales
+    off = align256(off + (size_t)(kScaleBlocks + 1) * 8 * 4);
   }
   pl->ws_bytes = off;
   return true;

@@ -13,6 +13,12 @@ constexpr int kMaxResp = 64;
 // packed query rows per workgroup of the forward and dQ kernels (the plan's query tiles)
 constexpr int kQTileFwd = 256;
 constexpr int kQTileDq = 256;
+// latent-KV heads (V = the leading kWideDv dims of each K row, one kv head): wide kernels
+constexpr int kWideDqk = 576;
+constexpr int kWideDv = 512;
+constexpr int kQTileFwdWide = 128;
+constexpr int kQTileDqWide = 64;
+constexpr int kDKTileWide = 64;   // keys per dK/dV workgroup
 
 // ---------------------------------------------------------------- GRPO token loss
 struct GrpoArgs {
@@ -63,7 +69,7 @@ struct AttnGeom {
 // (K or V rows: grp = 1, hstride = dim; GQA-packed query rows r = t * g + j of kv head h:
 // grp = g, ld = Hq * dim, gstride = dim, hstride = g * dim).
 struct PackArgs {
-  const float* f16_scale;  // null: bf16 copy; else fp16 output of value * (*f16_scale) (pack_keys_t)
+  const float* f16_scale;  // null: bf16 copy; else fp16 output of value * (*f16_scale)
   const uint16_t* src;   // bf16
   int64_t ld;
   int32_t grp;
@@ -96,6 +102,8 @@ hipError_t launch_pack_rowstats(const RowStatArgs& a, hipStream_t st);
 //   [0] s_dO: dO * s_dO has |values| <= 2^15      [1] s_Q: Q * s_Q has |values| <= 2^15
 //   [2] s_dS: 2^15 P (dP - Delta) * s_dS has |values| <= 2^15, from the bound
 //       |dP - Delta| <= 2 max_r |dO_r| max_j |V_j|  (Euclidean row norms)
+//   [3] s_K (latent-KV heads only): K * s_K has |values| <= 2^15
+// Partial maxima are kept as [kScaleBlocks, 8] floats, the scales right after them.
 constexpr int kScaleBlocks = 512;
 struct ScaleArgs {
   const uint16_t* dO;    // [T, Hq, Dv]
@@ -106,7 +114,7 @@ struct ScaleArgs {
   int64_t T, P;
   int64_t Tk;            // response V rows
   int32_t Hq, Hkv, Dqk, Dv;
-  float* partial;        // [kScaleBlocks, 4]
+  float* partial;        // [kScaleBlocks, 8] (the first 4 of each block used here)
   float* scales;         // [4]
 };
 hipError_t launch_bwd_scales(const ScaleArgs& a, hipStream_t st);
@@ -147,7 +155,7 @@ struct BwdArgs {
   uint16_t* QT;         // dimension-major, slot-permuted: [Hkv * Dqk, mpad]
   uint16_t* dOT;        // [Hkv * Dv, mpad]
   float* rowstat;       // [Hkv, mpad, 2]: {LSE log2 e - 15, Delta * s_dS}
-  float* scale_part;    // [kScaleBlocks, 4] partial maxima
+  float* scale_part;    // [kScaleBlocks, 8] partial maxima
   float* scales;        // [4] fp16 operand scales (see ScaleArgs)
   int64_t mpad;         // packed query rows per kv head (T * g) rounded up to 64
   const uint16_t* KTp;  // packed prompt K: [Hkv * Dqk, ppad] (pack.hip layout)
@@ -182,9 +190,15 @@ struct AttnPlan {
 bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, const int32_t* cu, const int32_t* kcu,
                AttnPlan* plan);
 hipError_t launch_attn_fwd(FwdArgs& a, int Dqk, int Dv, hipStream_t st);
+// latent-KV forward main kernel (replay_attn_wide_fwd.hip); the caller merges split partials
+hipError_t launch_attn_fwd_wide(FwdArgs& a, hipStream_t st);
 hipError_t launch_attn_bwd(BwdArgs& a, int Dqk, int Dv, hipStream_t st);
 // dQ part of the backward (replay_attn_dq.hip): K packing, dQ kernel, split reduction
 hipError_t launch_bwd_dq(BwdArgs& a, int Dqk, int Dv, hipStream_t st);
+// latent-KV dQ and dK/dV parts (replay_attn_wide_bwd.hip). The dQ launcher leaves split partials
+// unreduced (the caller reduces); the dK/dV launcher runs its own scales and packing.
+hipError_t launch_bwd_dq_wide(BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dkdv_wide(BwdArgs& a, hipStream_t st);
 // dK/dV part (replay_attn_dkdv.hip): query-row packing, prompt and response dK/dV kernels
 hipError_t launch_bwd_dkdv(BwdArgs& a, int Dqk, int Dv, hipStream_t st);
 

@@ -79,6 +79,7 @@ __global__ __launch_bounds__(256) void pack_keys_t(PackArgs a) {
 }
 
 // row-major copy, 16 bytes per thread: out row (h, col0_s + r) <- logical row row0_s + r of head h
+// (bf16, or fp16 of value * (*f16_scale))
 __global__ __launch_bounds__(256) void pack_rows(PackArgs a) {
   const int cpr = a.dim / 8;                         // 16-byte chunks per row
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -91,6 +92,17 @@ __global__ __launch_bounds__(256) void pack_rows(PackArgs a) {
   const int64_t r = slot - a.col0[s];
   u32x4 v = {0u, 0u, 0u, 0u};
   if (r < a.n[s]) v = *reinterpret_cast<const u32x4*>(a.src + src_row(a, a.row0[s] + r, h) + ch * 8);
+  if (a.f16_scale) {
+    // fp16 rows of value * scale (power of two: exact up to the fp16 rounding, to nearest even)
+    const float f = *a.f16_scale;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f16x2 x;
+      x[0] = (_Float16)(bf16_lo(v[q]) * f);
+      x[1] = (_Float16)(bf16_hi(v[q]) * f);
+      v[q] = __builtin_bit_cast(uint32_t, x);
+    }
+  }
   *reinterpret_cast<u32x4*>(a.out + ((int64_t)h * a.out_ld + slot) * a.dim + ch * 8) = v;
 }
 

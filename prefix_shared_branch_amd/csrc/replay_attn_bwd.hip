@@ -51,6 +51,7 @@ hipError_t bwd_go(BwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_attn_bwd(BwdArgs& a, int Dqk, int Dv, hipStream_t st) {
+  if (Dqk == kWideDqk && Dv == kWideDv) return bwd_go<kWideDqk, kWideDv>(a, st);
   if (Dqk == 64 && Dv == 64) return bwd_go<64, 64>(a, st);
   if (Dqk == 128 && Dv == 128) return bwd_go<128, 128>(a, st);
   return hipErrorInvalidValue;

@@ -470,6 +470,7 @@ hipError_t dkdv_go(BwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_bwd_dkdv(BwdArgs& a, int Dqk, int Dv, hipStream_t st) {
+  if (Dqk == kWideDqk && Dv == kWideDv) return launch_bwd_dkdv_wide(a, st);
   if (Dqk == 64 && Dv == 64) return dkdv_go<64, 64>(a, st);
   if (Dqk == 128 && Dv == 128) return dkdv_go<128, 128>(a, st);
   return hipErrorInvalidValue;

@@ -401,6 +401,13 @@ hipError_t dq_go(BwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_bwd_dq(BwdArgs& a, int Dqk, int Dv, hipStream_t st) {
+  if (Dqk == kWideDqk && Dv == kWideDv) {
+    hipError_t e = launch_bwd_dq_wide(a, st);
+    if (e != hipSuccess || a.splits == 1 || a.qtiles == 0) return e;
+    const long long n4 = (long long)a.geo.T * a.geo.Hq * kWideDqk / 4;
+    hipLaunchKernelGGL((replay_bwd_dq_reduce<kWideDqk>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   if (Dqk == 64 && Dv == 64) return dq_go<64, 64>(a, st);
   if (Dqk == 128 && Dv == 128) return dq_go<128, 128>(a, st);
   return hipErrorInvalidValue;

@@ -476,6 +476,14 @@ hipError_t fwd_go(FwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_attn_fwd(FwdArgs& a, int Dqk, int Dv, hipStream_t st) {
+  if (Dqk == kWideDqk && Dv == kWideDv) {
+    // latent KV: V^T fragments come from the K tiles themselves (no packing pass)
+    const hipError_t e = launch_attn_fwd_wide(a, st);
+    if (e != hipSuccess || a.splits == 1 || a.qtiles == 0) return e;
+    const long long total = (long long)a.geo.T * a.geo.Hq * (kWideDv / 4);
+    hipLaunchKernelGGL((replay_fwd_merge<kWideDv>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   if (Dqk == 64 && Dv == 64) return fwd_go<64, 64>(a, st);
   if (Dqk == 128 && Dv == 128) return fwd_go<128, 128>(a, st);
   return hipErrorInvalidValue;
