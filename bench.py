@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="million", choices=["tiny", "mid", "long", "million"])
+    ap.add_argument("--workload", default="million", choices=["tiny", "mid", "long", "million", "mla"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = automatic)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -69,11 +69,13 @@ class Workload:
         T = int(self.cu[-1])
         t0 = time.time()
         self.kp = to_dev(inputs.prompt_k(cfg))
-        self.vp = to_dev(inputs.prompt_v(cfg))
-        log(f"prompt K/V resident ({2 * self.kp.numel() * 2 / 2**30:.2f} GiB) in {time.time() - t0:.1f}s")
+        # latent KV: V is the leading Dv dims of the K rows (a strided view, no copy)
+        self.vp = self.kp[:, :, :cfg.Dv] if cfg.mla else to_dev(inputs.prompt_v(cfg))
+        log(f"prompt K/V resident ({(self.kp.numel() + (0 if cfg.mla else self.vp.numel())) * 2 / 2**30:.2f} GiB) "
+            f"in {time.time() - t0:.1f}s")
         self.q = to_dev(inputs.suffix_q(cfg, 0, T))
         self.ks = to_dev(inputs.suffix_k(cfg, 0, T))
-        self.vs = to_dev(inputs.suffix_v(cfg, 0, T))
+        self.vs = self.ks[:, :, :cfg.Dv] if cfg.mla else to_dev(inputs.suffix_v(cfg, 0, T))
         self.do = to_dev(inputs.suffix_do(cfg, 0, T))
         self.logits, self.targets, self.old = [], [], []
         t0 = time.time()
@@ -148,9 +150,10 @@ def flops(cfg, R):
     d, dv = cfg.Dqk, cfg.Dv
     prompt_pairs = R * cfg.P
     alg = 6 * (d + dv) * pairs * cfg.Hq
+    hilo = 1 if cfg.mla else 2   # the latent-KV dK/dV kernel runs its fp16 products once
     executed = (2 * (d + dv) * pairs             # forward: S, PV
                 + (2 * d + 2 * dv) * pairs       # dK/dV kernel: S, dP recomputed
-                + 2 * (2 * dv + 2 * d) * prompt_pairs + (2 * dv + 2 * d) * (pairs - prompt_pairs)  # dV, dK (hi/lo on prompt)
+                + hilo * (2 * dv + 2 * d) * prompt_pairs + (2 * dv + 2 * d) * (pairs - prompt_pairs)  # dV, dK
                 + (4 * d + 2 * dv) * pairs) * cfg.Hq   # dQ kernel: S, dP, dQ
     return alg, executed, pairs
 

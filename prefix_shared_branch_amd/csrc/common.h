@@ -193,6 +193,22 @@ __device__ __forceinline__ s16x4 lds_tr_at(const char* base, int byte_off) {
       reinterpret_cast<LSR_LDS s16x4*>(reinterpret_cast<uintptr_t>(base + byte_off)));
 }
 
+// LDS reads through LDS-typed pointers derived from a __shared__ array (rather than from an integer
+// address): the compiler keeps the array's identity, so a kernel whose ring stages are separate
+// arrays does not wait, before reading one stage, for direct loads in flight into another.
+__device__ __forceinline__ bf16x8 lds_b128_as(const char* base, int off) {
+  return *(const LSR_LDS bf16x8*)((const LSR_LDS char*)base + off);
+}
+__device__ __forceinline__ f16x8 lds_h128_as(const char* base, int off) {
+  return *(const LSR_LDS f16x8*)((const LSR_LDS char*)base + off);
+}
+__device__ __forceinline__ f32x4 lds_f32x4_as(const char* base, int off) {
+  return *(const LSR_LDS f32x4*)((const LSR_LDS char*)base + off);
+}
+__device__ __forceinline__ s16x4 lds_tr_as(const char* base, int off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LSR_LDS s16x4*)((LSR_LDS char*)base + off));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

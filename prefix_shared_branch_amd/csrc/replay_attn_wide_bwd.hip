@@ -150,7 +150,13 @@ struct WideDqCfg {
 
 __global__ __launch_bounds__(64 * WideDqCfg::NW, 1) void replay_bwd_dq_wide(BwdArgs a) {
   using C = WideDqCfg;
-  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE];
+  // one LDS array per ring stage (reads of one stage never wait for loads into another)
+  __shared__ __attribute__((aligned(1024))) char sm0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm3[C::STAGE];
+  static_assert(C::NSTAGE == 4, "one array per stage");
+  char* const stg[4] = {sm0, sm1, sm2, sm3};
 
   const AttnGeom& G = a.geo;
   const int W = a.qtiles * a.splits;
@@ -219,13 +225,13 @@ __global__ __launch_bounds__(64 * WideDqCfg::NW, 1) void replay_bwd_dq_wide(BwdA
   const int64_t kp_end = ((int64_t)(G.P - 1) * G.ldk + kD) * 2;
   const int64_t ks_end = ((int64_t)(G.Tk - 1 - ktokb) * G.ldk + kD) * 2;
   const int64_t ldk2 = G.ldk * 2;
-  auto issue = [&](int u) {
+  auto issue = [&](int u, auto jc) {
     const int uu = min(u, nit - 1);
     const bool pr = uu < nps;
     const int key0 = pr ? pkey0 + uu * C::BN : (uu - nps) * C::BN;
     const int64_t ko = key0 * ldk2;
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc((pr ? kp0 : ks0) + ko, (pr ? kp_end : ks_end) - ko);
-    char* dst = smem + (u % C::NSTAGE) * C::STAGE;
+    char* dst = stg[decltype(jc)::value];
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
@@ -243,38 +249,70 @@ __global__ __launch_bounds__(64 * WideDqCfg::NW, 1) void replay_bwd_dq_wide(BwdA
   for (int d = 0; d < C::KT; ++d) dq[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float c2 = G.scale_log2;
 
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+  using J2 = std::integral_constant<int, 2>;
+  using J3 = std::integral_constant<int, 3>;
   if (nit > 0) {
-    issue(0);
-    issue(1);
-    issue(2);
+    issue(0, J0{});
+    issue(1, J1{});
+    issue(2, J2{});
   }
-  for (int u = 0; u < nit; ++u) {
+  // One tile (the ring runs in whole rounds of four; tiles past the last are fully masked).
+  auto tile = [&](int u, auto jc) {
+    constexpr int J = decltype(jc)::value;
     wait_vmem_le<2 * C::PPW>();
     wait_lds();
     bare_barrier();
-    issue(u + 3);
-    const int sb = (u % C::NSTAGE) * C::STAGE;
+    issue(u + 3, std::integral_constant<int, (J + 3) % 4>{});
+    const char* sb = stg[J];
+    // Run A: S^T and dP^T. Every fragment read is written out first; the schedule below issues the
+    // reads of k-step s + 2 right after the MFMAs of step s, so LDS latency hides under the MFMAs.
+    bf16x8 k0[C::KS], k1[C::KS];
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const int off = kb[s & 1] + 128 * (s >> 1);
+      k0[s] = lds_b128_as(sb, off);
+      k1[s] = lds_b128_as(sb, off + 4 * kRow72);
+    }
     f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     f32x4 dp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
-      const int off = sb + kb[s & 1] + 128 * (s >> 1);
-      const bf16x8 k0 = lds_b128_at(smem, off);
-      const bf16x8 k1 = lds_b128_at(smem, off + 4 * kRow72);
-      st[0] = mfma16(k0, qf[s], st[0]);
-      st[1] = mfma16(k1, qf[s], st[1]);
+      st[0] = mfma16(k0[s], qf[s], st[0]);
+      st[1] = mfma16(k1[s], qf[s], st[1]);
       if (s < C::VS) {
-        dp[0] = mfma16(k0, of[s], dp[0]);
-        dp[1] = mfma16(k1, of[s], dp[1]);
+        dp[0] = mfma16(k0[s], of[s], dp[0]);
+        dp[1] = mfma16(k1[s], of[s], dp[1]);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      if (s < C::VS) __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (s + 2 < C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // first K^T fragments of run B, in flight during the dS arithmetic
+    constexpr int LB = 4;
+    s16x4 t0[C::KT], t1[C::KT];
+    auto rd_t = [&](int d) {
+      const int off = tb[d & 3] + 128 * (d >> 2);
+      t0[d] = lds_tr_as(sb, off);
+      t1[d] = lds_tr_as(sb, off + 4 * kRow72);
+    };
+#pragma unroll
+    for (int d = 0; d < LB; ++d) rd_t(d);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool live = u < nit;
     const bool pr = u < nps;
     const int key0 = pr ? pkey0 + u * C::BN : (u - nps) * C::BN;
     const int nvalid = min(C::BN, (pr ? G.P : Rk) - key0);
     const bool causal = !pr && (key0 + C::BN - 1 > t_lo);
-    if (__builtin_expect(causal || nvalid < C::BN, 0)) {
+    if (__builtin_expect(!live || causal || nvalid < C::BN, 0)) {
       asm volatile("");
-      const int lim = min(nvalid, causal ? trow + qo - key0 + 1 : nvalid) - 8 * q4;
+      const int lim = (live ? min(nvalid, causal ? trow + qo - key0 + 1 : nvalid) : 0) - 8 * q4;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -288,13 +326,24 @@ __global__ __launch_bounds__(64 * WideDqCfg::NW, 1) void replay_bwd_dq_wide(BwdA
         const float p = fast_exp2(__builtin_fmaf(st[h][r], c2, -lrow));
         ds[4 * h + r] = (__bf16)(p * (dp[h][r] - drow));
       }
+    __builtin_amdgcn_sched_barrier(0);
+    // Run B: dQ^T += K^T dS^T, the reads of fragment d + LB following the MFMA of fragment d
+#pragma unroll
+    for (int d = LB; d < C::KT; ++d) rd_t(d);
+#pragma unroll
+    for (int d = 0; d < C::KT; ++d) dq[d] = mfma16(join_tr(t0[d], t1[d]), ds, dq[d]);
 #pragma unroll
     for (int d = 0; d < C::KT; ++d) {
-      const int off = sb + tb[d & 3] + 128 * (d >> 2);
-      const s16x4 t0 = lds_tr_at(smem, off);
-      const s16x4 t1 = lds_tr_at(smem, off + 4 * kRow72);
-      dq[d] = mfma16(join_tr(t0, t1), ds, dq[d]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (d + LB < C::KT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int u0 = 0; u0 < nit; u0 += 4) {
+    tile(u0, J0{});
+    tile(u0 + 1, J1{});
+    tile(u0 + 2, J2{});
+    tile(u0 + 3, J3{});
   }
   wait_vmem();
   if (!rvalid) return;
@@ -335,7 +384,11 @@ struct WideKvCfg {
 template <bool PROMPT>
 __global__ __launch_bounds__(64 * WideKvCfg::NW, 1) void replay_bwd_dkdv_wide(BwdArgs a) {
   using C = WideKvCfg;
-  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE];
+  // one LDS array per ring stage (reads of one stage never wait for loads into the other)
+  __shared__ __attribute__((aligned(1024))) char sm0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm1[C::STAGE];
+  static_assert(C::NSTAGE == 2, "one array per stage");
+  char* const stg[2] = {sm0, sm1};
 
   const AttnGeom& G = a.geo;
   const int nk = PROMPT ? a.ktiles_prompt : a.ktile0[G.n_resp];
@@ -431,13 +484,13 @@ __global__ __launch_bounds__(64 * WideKvCfg::NW, 1) void replay_bwd_dkdv_wide(Bw
   const char* const osrc = reinterpret_cast<const char*>(a.dOr);
   const char* const rsrc = reinterpret_cast<const char*>(a.rowstat);
   const int64_t mpad = a.mpad;
-  auto issue = [&](int n) {
+  auto issue = [&](int n, auto jc) {
     const int nn = min(n, nsteps - 1);
     const int64_t m0 = row_begin + (int64_t)nn * C::BR;
     const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qsrc + m0 * kRow72, (mpad - m0) * kRow72);
     const __amdgpu_buffer_rsrc_t ro = buf_rsrc(osrc + m0 * kRow64, (mpad - m0) * kRow64);
     const __amdgpu_buffer_rsrc_t rr = buf_rsrc(rsrc + m0 * 8, (mpad - m0) * 8);
-    char* dst = smem + (n % C::NSTAGE) * C::STAGE;
+    char* dst = stg[decltype(jc)::value];
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
@@ -460,31 +513,68 @@ __global__ __launch_bounds__(64 * WideKvCfg::NW, 1) void replay_bwd_dkdv_wide(Bw
   };
 
   const int key_local = key0 + mykey;  // (response keys: position within the response)
-  if (nsteps > 0) issue(0);
-  for (int n = 0; n < nsteps; ++n) {
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+  if (nsteps > 0) issue(0, J0{});
+  // One 32-row step (the ring runs in whole rounds of two; a step past the last adds nothing).
+  // Fragment reads are written out first and scheduled a fixed distance ahead of their MFMAs.
+  constexpr int LB = 4;  // read-ahead (fragments) of the dV / dK run
+  auto step = [&](int n, auto jc) {
+    constexpr int J = decltype(jc)::value;
     wait_vmem_le<0>();
     wait_lds();
     bare_barrier();  // step n landed for all waves; step n - 1 is no longer read
-    issue(n + 1);
-    const int sb = (n % C::NSTAGE) * C::STAGE;
+    issue(n + 1, std::integral_constant<int, (J + 1) % 2>{});
+    const char* sb = stg[J];
+    // Run A: S = Q K^T and dP = dO V^T; the reads of k-step s + 1 follow the MFMAs of step s
+    f16x8 qa[C::KS], qz[C::KS], oa[C::VS], oz[C::VS];
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const int off = qb[s & 1] + 128 * (s >> 1);
+      qa[s] = lds_h128_as(sb, off);
+      qz[s] = lds_h128_as(sb, off + 4 * kRow72);
+      if (s < C::VS) {
+        const int oo = ob[s & 3] + 256 * (s >> 2);
+        oa[s] = lds_h128_as(sb, oo);
+        oz[s] = lds_h128_as(sb, oo + 4 * kRow64);
+      }
+    }
     f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     f32x4 dp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
-      const int off = sb + qb[s & 1] + 128 * (s >> 1);
-      st[0] = mfma16h(lds_h128(smem, off), kf[s], st[0]);
-      st[1] = mfma16h(lds_h128(smem, off + 4 * kRow72), kf[s], st[1]);
+      st[0] = mfma16h(qa[s], kf[s], st[0]);
+      st[1] = mfma16h(qz[s], kf[s], st[1]);
       if (s < C::VS) {
-        const int oo = sb + ob[s & 3] + 256 * (s >> 2);
-        dp[0] = mfma16h(lds_h128(smem, oo), kf[s], dp[0]);
-        dp[1] = mfma16h(lds_h128(smem, oo + 4 * kRow64), kf[s], dp[1]);
+        dp[0] = mfma16h(oa[s], kf[s], dp[0]);
+        dp[1] = mfma16h(oz[s], kf[s], dp[1]);
       }
     }
-    // this lane: key mykey, step rows 8 q4 + e (e = 4 h + r); statistics {LSE log2 e - 15, Delta s_dS}
-    const char* rs = smem + sb + C::OFF_RS + wv * 1024 + q4 * 64;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      if (s < C::VS) __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (s + 1 < C::VS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      else if (s + 1 < C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // row statistics of this lane's rows 8 q4 .. 8 q4 + 7, and the first fragments of run B
     f32x4 sv[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sv[k] = *reinterpret_cast<const LSR_LDS f32x4*>(reinterpret_cast<uintptr_t>(rs + 16 * k));
+    for (int k = 0; k < 4; ++k) sv[k] = lds_f32x4_as(sb, C::OFF_RS + wv * 1024 + q4 * 64 + 16 * k);
+    s16x4 ta[C::VT + C::KT], tz[C::VT + C::KT];  // dO^T fragments, then Q^T fragments
+    auto rd_t = [&](int i) {
+      const int off = i < C::VT ? (otb ^ (i << 5)) : qtb[(i - C::VT) & 3] + 128 * ((i - C::VT) >> 2);
+      const int du = i < C::VT ? 4 * kRow64 : 4 * kRow72;
+      ta[i] = lds_tr_as(sb, off);
+      tz[i] = lds_tr_as(sb, off + du);
+    };
+#pragma unroll
+    for (int i = 0; i < LB; ++i) rd_t(i);
+    __builtin_amdgcn_sched_barrier(0);
+    // this lane: key mykey, step rows 8 q4 + e (e = 4 h + r); statistics {LSE log2 e - 15, Delta s_dS}
+    const bool live = n < nsteps;
     float pe[8], de[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -509,20 +599,28 @@ __global__ __launch_bounds__(64 * WideKvCfg::NW, 1) void replay_bwd_dkdv_wide(Bw
     f16x8 pb, db;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pb[e] = (_Float16)pe[e];
-      db[e] = (_Float16)de[e];
+      pb[e] = (_Float16)(live ? pe[e] : 0.0f);
+      db[e] = (_Float16)(live ? de[e] : 0.0f);
     }
-    // dV^T += dO^T P, dK^T += Q^T dS (transposed fragments of the staged rows)
+    __builtin_amdgcn_sched_barrier(0);
+    // Run B: dV^T += dO^T P, then dK^T += Q^T dS (transposed fragments of the staged rows); the
+    // reads of fragment i + LB follow the MFMA of fragment i
 #pragma unroll
-    for (int d = 0; d < C::VT; ++d) {
-      const int off = sb + (otb ^ (d << 5));
-      dv[d] = mfma16h(join_tr_h(lds_tr_at(smem, off), lds_tr_at(smem, off + 4 * kRow64)), pb, dv[d]);
-    }
+    for (int i = LB; i < C::VT + C::KT; ++i) rd_t(i);
 #pragma unroll
-    for (int d = 0; d < C::KT; ++d) {
-      const int off = sb + qtb[d & 3] + 128 * (d >> 2);
-      dk[d] = mfma16h(join_tr_h(lds_tr_at(smem, off), lds_tr_at(smem, off + 4 * kRow72)), db, dk[d]);
+    for (int d = 0; d < C::VT; ++d) dv[d] = mfma16h(join_tr_h(ta[d], tz[d]), pb, dv[d]);
+#pragma unroll
+    for (int d = 0; d < C::KT; ++d) dk[d] = mfma16h(join_tr_h(ta[C::VT + d], tz[C::VT + d]), db, dk[d]);
+#pragma unroll
+    for (int i = 0; i < C::VT + C::KT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + LB < C::VT + C::KT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int n0 = 0; n0 < nsteps; n0 += 2) {
+    step(n0, J0{});
+    step(n0 + 1, J1{});
   }
   wait_vmem();
   if (!kvalid) return;

@@ -51,9 +51,8 @@ struct WideFwdCfg {
   static constexpr int STAGE = BN * KROW;      // 36 KB
   static constexpr int NSTAGE = 4;
   static constexpr int NP = STAGE / 1024;      // 1 KB direct-load pieces per tile
-  static constexpr int LW = 4;                 // waves 0-3 move the tiles, PPW pieces each
-  static constexpr int PPW = NP / LW;
-  static_assert(NP % LW == 0, "pieces split evenly over the loading waves");
+  static constexpr int PPW = 5;                // direct loads per wave per tile (see issue)
+  static_assert(NP == 4 * NW + 4, "four pieces per wave, then one more for waves 0-3");
   static constexpr int KS = D / 32;            // k-steps of the score product
   static constexpr int DT = DV / 16;           // 16-dim tiles of O^T
   static constexpr float kStale = 8.0f;        // stabiliser slack (exp2 units)
@@ -67,7 +66,15 @@ __device__ __forceinline__ int wide_swz(int r) { return ((r >> 1) & 1) | ((r >> 
 
 __global__ __launch_bounds__(64 * WideFwdCfg::NW, 1) void replay_fwd_wide(FwdArgs a) {
   using C = WideFwdCfg;
-  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE];
+  // one LDS array per ring stage: the compiler then tells a stage's transposed reads apart from the
+  // direct loads in flight into the other stages (and waits for none of them)
+  __shared__ __attribute__((aligned(1024))) char sm0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm3[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sdummy[4 * 1024];
+  static_assert(C::NSTAGE == 4, "one array per stage");
+  char* const stg[4] = {sm0, sm1, sm2, sm3};
 
   const AttnGeom& G = a.geo;
   const int W = a.qtiles * a.splits;  // one kv head
@@ -140,23 +147,25 @@ __global__ __launch_bounds__(64 * WideFwdCfg::NW, 1) void replay_fwd_wide(FwdArg
   const int64_t kp_end = ((int64_t)(G.P - 1) * G.ldk + C::D) * 2;
   const int64_t ks_end = ((int64_t)(G.Tk - 1 - ktokb) * G.ldk + C::D) * 2;
   const int64_t ldk2 = G.ldk * 2;
-  auto issue = [&](int u) {
-    if (wv >= C::LW) return;
+  auto issue = [&](int u, auto jc) {
     const int uu = min(u, nit - 1);  // past the last tile: reload it (keeps the wait counts fixed)
     const bool pr = uu < nps;
     const int key0 = pr ? pkey0 + uu * C::BN : (uu - nps) * C::BN;
     const int64_t ko = key0 * ldk2;
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc((pr ? kp0 : ks0) + ko, (pr ? kp_end : ks_end) - ko);
-    char* dst = smem + (u % C::NSTAGE) * C::STAGE;
+    char* dst = stg[decltype(jc)::value];
     int ln = lane;
     asm volatile("" : "+v"(ln));  // per-lane offsets recomputed per tile rather than pinned
 #pragma unroll
     for (int k = 0; k < C::PPW; ++k) {
-      const int pc = wv + C::LW * k;
+      // pieces wv, wv + 8, wv + 16, wv + 24, then 32 + wv for waves 0-3; waves 4-7 repeat a piece
+      // into a scratch slot, so that every wave issues the same number of loads per tile
+      const int pc = k < C::PPW - 1 ? wv + C::NW * k : C::NP - 4 + (wv & 3);
       const int unit = pc * 64 + ln;
       const int row = unit / 72;
       const int c = (unit - row * 72) ^ wide_swz(row);
-      lds_dma16_buf(rs, (uint32_t)(row * ldk2 + (c << 4)), dst + pc * 1024);
+      char* d = (k < C::PPW - 1 || wv < 4) ? dst + pc * 1024 : sdummy + (wv - 4) * 1024;
+      lds_dma16_buf(rs, (uint32_t)(row * ldk2 + (c << 4)), d);
     }
   };
 
@@ -167,34 +176,65 @@ __global__ __launch_bounds__(64 * WideFwdCfg::NW, 1) void replay_fwd_wide(FwdArg
   float l_run = 0.0f;    // sum over this lane's keys
   const float c2 = G.scale_log2;
 
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+  using J2 = std::integral_constant<int, 2>;
+  using J3 = std::integral_constant<int, 3>;
   if (nit > 0) {
-    issue(0);
-    issue(1);
-    issue(2);
+    issue(0, J0{});
+    issue(1, J1{});
+    issue(2, J2{});
   }
-  for (int u = 0; u < nit; ++u) {
+  // One tile: wait for its pieces, hand the stage of tile u - 1 to the loads of tile u + 3, then
+  // S^T (run A), softmax, O^T += V^T P^T (run B). The reads of each run are written out first; the
+  // schedule issues them a fixed distance ahead of the MFMAs that use them. Tiles past the last
+  // (the ring runs in whole rounds of four) are fully masked and change nothing.
+  constexpr int LA = 1, LB = 2;  // read-ahead distance in k-steps / dim tiles
+  auto tile = [&](int u, auto jc) {
+    constexpr int J = decltype(jc)::value;
     wait_vmem_le<2 * C::PPW>();  // this wave's pieces of tile u have landed
     wait_lds();
     bare_barrier();              // all pieces of tile u landed; tile u - 1 is no longer read
-    issue(u + 3);
-    const int sb = (u % C::NSTAGE) * C::STAGE;
+    issue(u + 3, std::integral_constant<int, (J + 3) % 4>{});
+    const char* sb = stg[J];
+    bf16x8 k0[C::KS], k1[C::KS];
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const int off = kb[s & 1] + 128 * (s >> 1);
+      k0[s] = lds_b128_as(sb, off);
+      k1[s] = lds_b128_as(sb, off + 4 * C::KROW);
+    }
     f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
-      const int off = sb + kb[s & 1] + 128 * (s >> 1);
-      const bf16x8 k0 = lds_b128_at(smem, off);
-      const bf16x8 k1 = lds_b128_at(smem, off + 4 * C::KROW);
-      st[0] = mfma16(k0, qf[s], st[0]);
-      st[1] = mfma16(k1, qf[s], st[1]);
+      st[0] = mfma16(k0[s], qf[s], st[0]);
+      st[1] = mfma16(k1[s], qf[s], st[1]);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (s + LA < C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s16x4 t0[C::DT], t1[C::DT];
+    auto rd_t = [&](int d) {
+      const int off = vb[d & 3] + 128 * (d >> 2);
+      t0[d] = lds_tr_as(sb, off);
+      t1[d] = lds_tr_as(sb, off + 4 * C::KROW);
+    };
+#pragma unroll
+    for (int d = 0; d < LB; ++d) rd_t(d);
+    __builtin_amdgcn_sched_barrier(0);
     // softmax: this lane holds keys 8 q4 + 4 h + r (h = tile, r = register) of its row
+    const bool live = u < nit;
     const bool pr = u < nps;
     const int key0 = pr ? pkey0 + u * C::BN : (u - nps) * C::BN;
     const int nvalid = min(C::BN, (pr ? G.P : Rk) - key0);
     const bool causal = !pr && (key0 + C::BN - 1 > t_lo);
-    if (__builtin_expect(causal || nvalid < C::BN, 0)) {
+    if (__builtin_expect(!live || causal || nvalid < C::BN, 0)) {
       asm volatile("");
-      const int lim = min(nvalid, causal ? trow + qo - key0 + 1 : nvalid) - 8 * q4;
+      const int lim = (live ? min(nvalid, causal ? trow + qo - key0 + 1 : nvalid) : 0) - 8 * q4;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -227,14 +267,24 @@ __global__ __launch_bounds__(64 * WideFwdCfg::NW, 1) void replay_fwd_wide(FwdArg
         p[4 * h + r] = (__bf16)e;
       }
     l_run += ls;
+    __builtin_amdgcn_sched_barrier(0);
     // O^T += V^T P^T over the tile's 32 keys
 #pragma unroll
+    for (int d = LB; d < C::DT; ++d) rd_t(d);
+#pragma unroll
+    for (int d = 0; d < C::DT; ++d) o[d] = mfma16(join_tr(t0[d], t1[d]), p, o[d]);
+#pragma unroll
     for (int d = 0; d < C::DT; ++d) {
-      const int off = sb + vb[d & 3] + 128 * (d >> 2);
-      const s16x4 t0 = lds_tr_at(smem, off);
-      const s16x4 t1 = lds_tr_at(smem, off + 4 * C::KROW);
-      o[d] = mfma16(join_tr(t0, t1), p, o[d]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (d + LB < C::DT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int u0 = 0; u0 < nit; u0 += 4) {
+    tile(u0, J0{});
+    tile(u0 + 1, J1{});
+    tile(u0 + 2, J2{});
+    tile(u0 + 3, J3{});
   }
 
   wait_vmem();  // the reloads issued past the last tile land before the workgroup's LDS is released

@@ -90,3 +90,46 @@ def test_mla_blockwise_replay():
     from tests.test_gpu_block import _blockwise, _check
     case = Case(inputs.replace(MLA, P=2000, seed=60), [150])
     _check(_blockwise(case, [0, 1, 70, 150]), case.oracle())
+
+
+def test_mla_full_prompt_sampled_rows_and_column_sums():
+    """P = 2,097,152 latent rows and the first response at its full length, in the launch
+    configuration the benchmark times (one call per response, exact prompt gradients). O, LSE and
+    dQ on sampled rows and heads (each row and head depends on that row and head alone); the
+    value-gradient column sums sum_j dV_P[j] + sum_s dVs[s] = sum_t sum_h dO[t, h] (softmax weights
+    sum to one) over all heads."""
+    import torch
+    from oracle import attn
+    from prefix_shared_branch_amd import lsreplay as L
+    from tests.helpers import dev_bf16
+    cfg = MLA
+    f64 = inputs.bf16_bits_to_f64
+    r = int(inputs.response_lengths(cfg)[0])
+    kp_bits = inputs.prompt_k(cfg)
+    kp = dev_bf16(kp_bits)
+    q_b, ks_b, do_b = inputs.suffix_q(cfg, 0, r), inputs.suffix_k(cfg, 0, r), inputs.suffix_do(cfg, 0, r)
+    q, ks, do = dev_bf16(q_b), dev_bf16(ks_b), dev_bf16(do_b)
+    vp, vs = kp[:, :, :cfg.Dv], ks[:, :, :cfg.Dv]
+    dkp = torch.zeros(cfg.P, 1, cfg.Dqk, dtype=torch.float32, device="cuda")
+    dvp = torch.zeros(cfg.P, 1, cfg.Dv, dtype=torch.float32, device="cuda")
+    o, lse = L.ls_replay_attn_fwd(q, ks, vs, kp, vp, [0, r], cfg.scale)
+    dq, dks, dvs = L.ls_replay_attn_bwd(q, ks, vs, kp, vp, [0, r], o, lse, do, dkp, dvp, cfg.scale)
+    torch.cuda.synchronize()
+    # the oracle at full P for two of the 16 query heads (heads share the one latent kv head)
+    hs = [0, cfg.Hq - 1]
+    Kp = f64(kp_bits)
+    del kp_bits
+    Ks, Q, dO = f64(ks_b), f64(q_b)[:, hs, :], f64(do_b)
+    rows = np.array([0, r - 1])
+    O, LSE = attn.replay_attn_fwd(Kp, Kp[:, :, :cfg.Dv], Q, Ks, Ks[:, :, :cfg.Dv], [0, r], cfg.scale, rows=rows)
+    check_bf16_out(host_f64(o[rows][:, hs]), O[rows], "O rows")
+    d = host_f64(lse)[hs][:, rows] - LSE[:, rows]
+    assert np.max(np.abs(d)) <= 1e-4, d
+    dQ = attn.replay_attn_bwd_rows(Kp, Kp[:, :, :cfg.Dv], Q, Ks, Ks[:, :, :cfg.Dv], dO[:, hs, :], [0, r], cfg.scale,
+                                   rows)
+    check_bf16_out(host_f64(dq[rows][:, hs]), dQ, "dQ rows")
+    # every head: value-gradient column sums
+    want = dO.sum(axis=(0, 1))
+    have = (dvp.double().sum(dim=(0, 1)) + dvs.double().sum(dim=(0, 1))).cpu().numpy()
+    rel = np.linalg.norm(have - want) / np.linalg.norm(want)
+    assert rel <= 1e-3, rel
