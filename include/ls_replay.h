@@ -46,11 +46,16 @@ typedef enum {
 /* Shape of one attention layer in replay.
  *  P        prompt length (>= 0; 0 gives plain causal attention over the response).
  *  Hq, Hkv  query / key-value heads, Hq % Hkv == 0; query head h reads kv head h / (Hq/Hkv).
- *  Dqk, Dv  head dims; supported pairs: (64,64), (128,128). Other pairs: LS_ERR_UNSUPPORTED.
+ *  Dqk, Dv  head dims; supported pairs: (64,64), (128,128), and (576,512) for latent KV (the
+ *           absorbed-latent attention of the GLM run's latent pages, LongStraw study notes §3-3).
+ *           Other pairs: LS_ERR_UNSUPPORTED.
  *  ldk, ldv elements between consecutive tokens of K and of V, for prompt and suffix alike;
  *           element (token j, kv head k, dim d) sits at K[j*ldk + k*Dqk + d] and
  *           V[j*ldv + k*Dv + d]. ldk >= Hkv*Dqk, ldv >= Hkv*Dv, both multiples of 8.
- *           Latent KV (Hkv == 1, V = first Dv dims of K) passes V = K and ldv = ldk.
+ *           Latent KV (Hkv == 1, V = first Dv dims of K) passes V = K and ldv = ldk. For
+ *           (576,512) this aliasing is required: Hkv must be 1, ldv == ldk, and every call must
+ *           pass Vp == Kp (when P > 0) and Vs == Ks; otherwise LS_ERR_UNSUPPORTED (the latent
+ *           kernels read V from the K rows and never touch a separate V buffer).
  *  softmax_scale  finite and > 0 (the usual choice is 1/sqrt(Dqk)).
  */
 typedef struct ls_attn_desc {

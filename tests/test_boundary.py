@@ -184,3 +184,30 @@ def test_kernel_timer_validation():
     assert lib.ls_kernel_timer_start(L.LS_KERNEL_DQ) == L.LS_OK
     assert lib.ls_kernel_timer_stop(ctypes.byref(ms), ctypes.byref(n)) == L.LS_OK
     assert ms.value == 0.0 and n.value == 0
+
+
+def _latent(**kw):
+    base = dict(P=4096, Hq=16, Hkv=1, Dqk=576, Dv=512, ldk=576, ldv=576, softmax_scale=1.0 / 24.0)
+    base.update(kw)
+    return desc(**base)
+
+
+def test_latent_kv_shape_validation():
+    """(576, 512) heads are served only as latent KV: one kv head, V rows = the K rows' leading dims."""
+    for which in (0, 1, 2):
+        rc, n = ws_bytes(_latent(), [0, 100, 300], which)
+        assert rc == L.LS_OK and n > 0
+    assert ws_bytes(_latent(Hq=32, Hkv=2, ldk=1152, ldv=1152), [0, 10])[0] == L.LS_ERR_UNSUPPORTED
+    assert ws_bytes(_latent(ldv=512), [0, 10])[0] == L.LS_ERR_UNSUPPORTED
+    assert ws_bytes(_latent(Dv=448, ldv=576), [0, 10])[0] == L.LS_ERR_UNSUPPORTED
+    assert _block_ws(_latent(), 100, 50, 1)[0] == L.LS_OK
+
+
+def test_latent_kv_requires_aliased_v():
+    d = _latent()
+    K, V = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    # checked before any device work: a separate V buffer is refused, the aliased form passes
+    assert _fwd(d, [0, 0], Kp=K, Vp=V, Ks=K, Vs=K) == L.LS_ERR_UNSUPPORTED
+    assert _fwd(d, [0, 0], Kp=K, Vp=K, Ks=K, Vs=V) == L.LS_ERR_UNSUPPORTED
+    assert _fwd(d, [0, 0], Kp=K, Vp=K, Ks=V, Vs=V) == L.LS_OK
+    assert _fwd(_latent(P=0), [0, 0], Kp=None, Vp=None, Ks=V, Vs=V) == L.LS_OK
