@@ -271,6 +271,63 @@ int bwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void*
 
 }  // namespace
 
+namespace lsr {
+
+int grpo_rows(hipStream_t st, int32_t V, int32_t G, const int32_t* R, const float* rewards, float eps, int32_t first,
+              int32_t count, int64_t lo, int64_t hi, const uint16_t* logits, const int32_t* targets,
+              const float* old_logp, uint16_t* dlogits, float* loss_accum, float* logp_out, uint8_t* clipped_out,
+              float* row_loss, bool vec) {
+  // group advantage in float64 on the host: A_i = (r_i - mean) / (std_pop + 1e-6)
+  double mean = 0.0;
+  for (int i = 0; i < G; ++i) mean += rewards[i];
+  mean /= G;
+  double var = 0.0;
+  for (int i = 0; i < G; ++i) var += (rewards[i] - mean) * (rewards[i] - mean);
+  const double sd = std::sqrt(var / G);
+
+  // the rows of each response that fall in [lo, hi), launched in batches of at most kMaxResp
+  GrpoArgs a;
+  int nb = 0;
+  int64_t brow0 = 0, rows = 0;
+  auto flush = [&]() -> bool {
+    if (nb == 0) return true;
+    a.n = nb;
+    a.T = rows;
+    a.V = V;
+    a.eps = eps;
+    a.logits = logits + (brow0 - lo) * V;
+    a.dlogits = dlogits ? dlogits + (brow0 - lo) * V : nullptr;
+    a.targets = targets + brow0;
+    a.old_logp = old_logp + brow0;
+    a.row_loss = row_loss + (brow0 - lo);
+    a.logp_out = logp_out ? logp_out + brow0 : nullptr;
+    a.clipped_out = clipped_out ? clipped_out + brow0 : nullptr;
+    a.loss_accum = loss_accum;
+    nb = 0;
+    rows = 0;
+    return launch_grpo(a, vec, st) == hipSuccess;
+  };
+  int64_t start = 0;
+  for (int i = first; i < first + count; ++i) {
+    const int64_t s = start > lo ? start : lo;
+    const int64_t e = (start + R[i]) < hi ? (start + R[i]) : hi;
+    start += R[i];
+    if (s >= e) continue;
+    if (nb == 0) {
+      std::memset(&a, 0, sizeof(a));
+      brow0 = s;
+    }
+    rows += e - s;
+    a.row_end[nb] = (int32_t)rows;
+    a.A[nb] = (float)((rewards[i] - mean) / (sd + 1e-6));
+    a.w[nb] = (float)(1.0 / ((double)G * (double)R[i]));
+    if (++nb == kMaxResp && !flush()) return LS_ERR_HIP;
+  }
+  return flush() ? LS_OK : LS_ERR_HIP;
+}
+
+}  // namespace lsr
+
 extern "C" {
 
 int ls_grpo_workspace_bytes(int64_t T, int32_t V, size_t* bytes) {
@@ -306,46 +363,10 @@ int ls_grpo_token_loss(void* stream, int32_t V, int32_t G, const int32_t* R, con
   if (!workspace || !aligned(workspace, 16)) return LS_ERR_WORKSPACE;
   if (workspace_bytes < need) return LS_ERR_WORKSPACE;
 
-  // group advantage in float64 on the host: A_i = (r_i - mean) / (std_pop + 1e-6)
-  double mean = 0.0;
-  for (int i = 0; i < G; ++i) mean += rewards[i];
-  mean /= G;
-  double var = 0.0;
-  for (int i = 0; i < G; ++i) var += (rewards[i] - mean) * (rewards[i] - mean);
-  const double sd = std::sqrt(var / G);
-
   const bool vec = (V % 8) == 0 && aligned(logits, 16) && (!dlogits || aligned(dlogits, 16));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  // responses are launched in batches of at most kMaxResp
-  int64_t row0 = 0;
-  for (int b0 = first; b0 < first + count; b0 += kMaxResp) {
-    const int nb = (first + count - b0) < kMaxResp ? (first + count - b0) : kMaxResp;
-    lsr::GrpoArgs a;
-    std::memset(&a, 0, sizeof(a));
-    int64_t rows = 0;
-    for (int k = 0; k < nb; ++k) {
-      const int i = b0 + k;
-      rows += R[i];
-      a.row_end[k] = (int32_t)rows;
-      a.A[k] = (float)((rewards[i] - mean) / (sd + 1e-6));
-      a.w[k] = (float)(1.0 / ((double)G * (double)R[i]));
-    }
-    a.n = nb;
-    a.T = rows;
-    a.V = V;
-    a.eps = eps;
-    a.logits = static_cast<const uint16_t*>(logits) + row0 * V;
-    a.dlogits = static_cast<uint16_t*>(dlogits) + row0 * V;
-    a.targets = targets + row0;
-    a.old_logp = old_logp + row0;
-    a.row_loss = static_cast<float*>(workspace) + row0;
-    a.logp_out = logp_out ? logp_out + row0 : nullptr;
-    a.clipped_out = clipped_out ? clipped_out + row0 : nullptr;
-    a.loss_accum = loss_accum;
-    if (lsr::launch_grpo(a, vec, st) != hipSuccess) return LS_ERR_HIP;
-    row0 += rows;
-  }
-  return LS_OK;
+  return lsr::grpo_rows(static_cast<hipStream_t>(stream), V, G, R, rewards, eps, first, count, 0, T,
+                        static_cast<const uint16_t*>(logits), targets, old_logp, static_cast<uint16_t*>(dlogits),
+                        loss_accum, logp_out, clipped_out, static_cast<float*>(workspace), vec);
 }
 
 }  // extern "C"

@@ -41,6 +41,13 @@ struct GrpoArgs {
 // vec: rows are 16-byte aligned and V % 8 == 0
 hipError_t launch_grpo(const GrpoArgs& a, bool vec, hipStream_t st);
 size_t grpo_workspace_bytes(int64_t T);
+// Loss over the packed rows [lo, hi) of responses first .. first+count-1 (host side, api.cpp): the
+// advantages come from all G rewards; `logits`, `dlogits` (or null) and `row_loss` point at row lo,
+// targets / old_logp / logp_out / clipped_out at row 0. Returns an ls_status code.
+int grpo_rows(hipStream_t st, int32_t V, int32_t G, const int32_t* R, const float* rewards, float eps, int32_t first,
+              int32_t count, int64_t lo, int64_t hi, const uint16_t* logits, const int32_t* targets,
+              const float* old_logp, uint16_t* dlogits, float* loss_accum, float* logp_out, uint8_t* clipped_out,
+              float* row_loss, bool vec);
 
 // ---------------------------------------------------------------- replay attention
 // Query rows are GQA-packed per kv head: within response i, packed row m = t * g + j is

@@ -25,6 +25,7 @@ import numpy as np
 # tensor ids (part of the seed derivation; never renumber)
 TID_Q, TID_KP, TID_VP, TID_KS, TID_VS, TID_DO = 1, 2, 3, 4, 5, 6
 TID_LOGITS, TID_TARGETS, TID_OLD_NOISE, TID_REWARDS, TID_LENGTHS = 7, 8, 9, 10, 11
+TID_HIDDEN, TID_PROJ = 12, 13
 
 CHUNK_ELEMS = 1 << 22  # elements per generator chunk (rows are never split)
 
@@ -207,3 +208,14 @@ def targets(cfg: Config, i: int, n: int) -> np.ndarray:
 def old_logp_noise(cfg: Config, i: int, n: int) -> np.ndarray:
     """N(0, old_sigma^2) noise; old-policy log-probs are the current log-probs plus this noise."""
     return (_rng(cfg.seed, TID_OLD_NOISE, i).standard_normal(n) * cfg.old_sigma).astype(np.float32)
+
+
+# ---- LM-head tensors (LM head fused with the loss): hidden states H [R_i, d] ~ N(0, 1) per response i,
+# and the vocabulary projection W [V, d] ~ N(0, (logit_sigma / sqrt(d))^2), so that the logits H W^T
+# have about the loss configs' spread (standard deviation logit_sigma).
+def hidden(cfg: Config, i: int, r0: int, r1: int, d: int) -> np.ndarray:
+    return normal_bf16_rows(cfg.seed, TID_HIDDEN, i, r0, r1, d, 1.0)
+
+
+def projection(cfg: Config, d: int) -> np.ndarray:
+    return normal_bf16_rows(cfg.seed, TID_PROJ, 0, 0, cfg.V, d, cfg.logit_sigma / float(np.sqrt(d)))

@@ -19,8 +19,8 @@ LS_OK, LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP = 0,
 LS_MAX_RESPONSES_PER_CALL = 64
 EXPORTED = ("ls_replay_attn_workspace_bytes", "ls_replay_attn_fwd", "ls_replay_attn_bwd",
             "ls_replay_attn_block_workspace_bytes", "ls_replay_attn_fwd_block", "ls_replay_attn_bwd_block",
-            "ls_grpo_workspace_bytes", "ls_grpo_token_loss", "ls_status_string", "ls_kernel_timer_start",
-            "ls_kernel_timer_stop")
+            "ls_grpo_workspace_bytes", "ls_grpo_token_loss", "ls_grpo_lmhead_workspace_bytes",
+            "ls_grpo_lmhead_loss", "ls_status_string", "ls_kernel_timer_start", "ls_kernel_timer_stop")
 LS_KERNEL_ATTN_FWD, LS_KERNEL_DKDV_PROMPT, LS_KERNEL_DQ, LS_KERNEL_GRPO_ROWS = 0, 1, 2, 3
 
 
@@ -71,6 +71,11 @@ def lib():
         L.ls_grpo_workspace_bytes.argtypes = [i64, i32, ctypes.POINTER(sz)]
         L.ls_grpo_token_loss.restype = ctypes.c_int
         L.ls_grpo_token_loss.argtypes = [vp, i32, i32, pi32, pf32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz]
+        L.ls_grpo_lmhead_workspace_bytes.restype = ctypes.c_int
+        L.ls_grpo_lmhead_workspace_bytes.argtypes = [i64, i32, i32, ctypes.POINTER(sz)]
+        L.ls_grpo_lmhead_loss.restype = ctypes.c_int
+        L.ls_grpo_lmhead_loss.argtypes = [vp, i32, i32, i32, pi32, pf32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, sz]
         L.ls_kernel_timer_start.restype = ctypes.c_int
         L.ls_kernel_timer_start.argtypes = [i32]
         L.ls_kernel_timer_stop.restype = ctypes.c_int
@@ -304,6 +309,51 @@ def ls_grpo_token_loss(logits, targets, old_logp, R, rewards, eps, first, count,
         _stream(), V, len(Ra), Rp, rp, float(eps), int(first), int(count), _ptr(logits), _ptr(targets),
         _ptr(old_logp), _ptr(dlogits), _ptr(loss_accum), _ptr(logp_out), _ptr(clipped_out), _ptr(ws), ws.numel()))
     return dlogits
+
+
+def ls_grpo_lmhead_workspace_bytes(T: int, V: int, d: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("ls_grpo_lmhead_workspace_bytes", lib().ls_grpo_lmhead_workspace_bytes(int(T), int(V), int(d),
+                                                                                  ctypes.byref(out)))
+    return int(out.value)
+
+
+def ls_grpo_lmhead_loss(H, W, targets, old_logp, R, rewards, eps, first, count, loss_accum, dW_accum=None,
+                        dH=None, logp_out=None, clipped_out=None, workspace=None, scoring_only=False):
+    """LM head (logits = H W^T, chunked) fused with the clipped-GRPO loss of responses [first, first+count):
+    adds the loss share into loss_accum and dL/dW into dW_accum (fp32 [V, d]); returns dH (bf16 [T, d]),
+    or None with scoring_only."""
+    import torch
+    T, d = H.shape
+    V = W.shape[0]
+    _check_tensor(H, "H", torch.bfloat16)
+    _check_tensor(W, "W", torch.bfloat16, (V, d))
+    _check_tensor(targets, "targets", torch.int32, (T,))
+    _check_tensor(old_logp, "old_logp", torch.float32, (T,))
+    _check_tensor(loss_accum, "loss_accum", torch.float32)
+    if not (H.is_contiguous() and W.is_contiguous()):
+        raise ValueError("H and W must be contiguous")
+    if scoring_only:
+        if dH is not None or dW_accum is not None:
+            raise ValueError("scoring_only takes no gradient buffers")
+    else:
+        if dW_accum is None:
+            raise ValueError("dW_accum (fp32 [V, d], zeroed by the caller) is required")
+        _check_tensor(dW_accum, "dW_accum", torch.float32, (V, d))
+        dH = torch.empty_like(H) if dH is None else dH
+        _check_tensor(dH, "dH", torch.bfloat16, (T, d))
+    if logp_out is not None:
+        _check_tensor(logp_out, "logp_out", torch.float32, (T,))
+    if clipped_out is not None:
+        _check_tensor(clipped_out, "clipped_out", torch.uint8, (T,))
+    Ra, Rp = _i32_array(R)
+    ra, rp = _f32_array(rewards)
+    ws = _workspace(ls_grpo_lmhead_workspace_bytes(T, V, d), H.device, workspace)
+    _check("ls_grpo_lmhead_loss", lib().ls_grpo_lmhead_loss(
+        _stream(), V, d, len(Ra), Rp, rp, float(eps), int(first), int(count), _ptr(H), _ptr(W), _ptr(targets),
+        _ptr(old_logp), _ptr(loss_accum), _ptr(dH), _ptr(dW_accum), _ptr(logp_out), _ptr(clipped_out), _ptr(ws),
+        ws.numel()))
+    return dH
 
 
 def ls_kernel_timer_start(kernel: int) -> None:

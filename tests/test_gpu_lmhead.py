@@ -1,0 +1,102 @@
+"""GPU parity of ls_grpo_lmhead_loss (LM head, logits = H W^T chunk by chunk, fused with the clipped
+GRPO objective of the LongStraw study notes §1-1) against the fp64 oracle in oracle/lmhead.py.
+
+The oracle rounds the logits to bf16 as the device does (one fp32 accumulation, then bf16). Its
+fp64 product and the device's fp32 one can round to neighbouring bf16 values where the product sits
+next to a rounding midpoint; tokens whose target logit is such a case, or whose ratio sits at a clip
+boundary, are compared with one bf16 step of slack (log-probs) or not at all (clip flags)."""
+import numpy as np
+import pytest
+
+from oracle import grpo, lmhead
+from prefix_shared_branch_amd import inputs
+from tests.helpers import check_bf16_out, dev_bf16, host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(cfg, lengths, d):
+    import torch
+    R = np.asarray(lengths, dtype=np.int32)
+    G = len(R)
+    rewards = inputs.rewards(inputs.replace(cfg, G=G))
+    if rewards.min() == rewards.max():
+        rewards[0] = 1.0 - rewards[0]
+    hb = np.concatenate([inputs.hidden(cfg, i, 0, int(R[i]), d) for i in range(G)])
+    wb = inputs.projection(cfg, d)
+    Hf, Wf = inputs.bf16_bits_to_f64(hb), inputs.bf16_bits_to_f64(wb)
+    y = np.concatenate([inputs.targets(cfg, i, int(R[i])) for i in range(G)])
+    x64 = Hf @ Wf.T
+    old = (grpo.token_logp(lmhead.round_bf16(x64), y)
+           + np.concatenate([inputs.old_logp_noise(cfg, i, int(R[i])) for i in range(G)])).astype(np.float32)
+    return dict(R=R, G=G, rewards=rewards, Hf=Hf, Wf=Wf, y=y, old=old, x64=x64, H=dev_bf16(hb), W=dev_bf16(wb),
+                targets=torch.from_numpy(y).cuda(), old_d=torch.from_numpy(old).cuda(), eps=cfg.eps, V=cfg.V, d=d)
+
+
+def _run(s, scoring_only=False):
+    import torch
+    from prefix_shared_branch_amd import lsreplay as L
+    T = int(s["R"].sum())
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    logp = torch.empty(T, dtype=torch.float32, device="cuda")
+    clip = torch.empty(T, dtype=torch.uint8, device="cuda")
+    dW = None if scoring_only else torch.zeros(s["V"], s["d"], dtype=torch.float32, device="cuda")
+    dH = L.ls_grpo_lmhead_loss(s["H"], s["W"], s["targets"], s["old_d"], s["R"], s["rewards"], s["eps"], 0, s["G"],
+                               loss, dW_accum=dW, logp_out=logp, clipped_out=clip, scoring_only=scoring_only)
+    torch.cuda.synchronize()
+    return loss, dH, dW, logp, clip
+
+
+def _ambiguous(x64):
+    """Products whose fp64 and fp32 forms may round to different bf16 neighbours."""
+    return lmhead.round_bf16(x64 * (1 + 2.0 ** -20)) != lmhead.round_bf16(x64 * (1 - 2.0 ** -20))
+
+
+def _check(s, got):
+    loss, dH, dW, logp, clip = got
+    G, R, eps = s["G"], s["R"], s["eps"]
+    l_ref, dH_ref, dW_ref, logp_ref, clip_ref = lmhead.lmhead_grpo_loss(s["Hf"], s["Wf"], s["y"], s["old"], R,
+                                                                        s["rewards"], G, eps, 0, G)
+    x = lmhead.round_bf16(s["x64"])
+    S_abs = grpo.abs_term_scale(x, s["y"], s["old"], R, s["rewards"], G, eps, 0, G)
+    assert abs(float(loss.item()) - l_ref) <= 1e-3 * S_abs, (float(loss.item()), l_ref, S_abs)
+    T = len(s["y"])
+    xt = s["x64"][np.arange(T), s["y"]]
+    step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(xt), 1e-30))) - 7)   # one bf16 step at the target logit
+    slack = np.where(_ambiguous(xt), step, 0.0)
+    dl = np.abs(host_f64(logp) - logp_ref)
+    assert np.all(dl <= 1e-4 + slack), np.max(dl - slack)
+    rho = np.exp(logp_ref - s["old"].astype(np.float64))
+    sure = (np.abs(rho - (1 - eps)) > 1e-3) & (np.abs(rho - (1 + eps)) > 1e-3)
+    np.testing.assert_array_equal(host_f64(clip)[sure].astype(bool), clip_ref[sure])
+    if dH is not None:
+        check_bf16_out(host_f64(dH)[:, None, :], dH_ref[:, None, :], "dH", literal_abs=False)
+        check_bf16_out(host_f64(dW)[:, None, :], dW_ref[:, None, :], "dW", literal_abs=False)
+    return l_ref
+
+
+@pytest.mark.parametrize("cfg_name,lengths,d", [
+    ("tiny", [70, 1500, 900], 256),       # 2,470 tokens: two chunks, a response across the boundary
+    ("tiny_clip", [33, 64], 96),          # clipped tokens in play
+    ("mid", [40, 60], 64),                # the full 151,936-word vocabulary
+])
+def test_lmhead_loss_matches_oracle(cfg_name, lengths, d):
+    s = _setup(inputs.CONFIGS[cfg_name], lengths, d)
+    _check(s, _run(s))
+
+
+def test_lmhead_scoring_only_and_accumulation():
+    """Scoring mode gives the same loss share and log-probs with no gradient work; a second call adds
+    its dW into the same accumulator."""
+    import torch
+    from prefix_shared_branch_amd import lsreplay as L
+    s = _setup(inputs.CONFIGS["tiny"], [300, 200], 128)
+    loss, dH, dW, logp, clip = _run(s)
+    loss2, _, _, logp2, clip2 = _run(s, scoring_only=True)
+    assert torch.equal(loss, loss2) and torch.equal(logp, logp2) and torch.equal(clip, clip2)
+    loss3 = torch.zeros(1, dtype=torch.float32, device="cuda")
+    L.ls_grpo_lmhead_loss(s["H"], s["W"], s["targets"], s["old_d"], s["R"], s["rewards"], s["eps"], 0, s["G"],
+                          loss3, dW_accum=dW)
+    torch.cuda.synchronize()
+    _, _, dW1, _, _ = _run(s)
+    assert torch.allclose(dW, 2 * dW1, rtol=1e-6, atol=0)   # the same sums added twice
