@@ -158,6 +158,38 @@ def flops(cfg, R):
     return alg, executed, pairs
 
 
+def lmhead_measure(cfg, wl):
+    """One call of the fused LM-head loss over response 0 (hidden size Hq * Dqk), timed after a warm-up
+    call; also the scoring-only call (logits GEMM and loss, no gradient GEMMs)."""
+    import torch
+    from prefix_shared_branch_amd import lsreplay as L
+    d = cfg.Hq * cfg.Dqk
+    R0 = int(wl.R[0])
+    H = to_dev(inputs.hidden(cfg, 0, 0, R0, d))
+    W = to_dev(inputs.projection(cfg, d))
+    dW = torch.zeros(cfg.V, d, dtype=torch.float32, device="cuda")
+    dH = torch.empty(R0, d, dtype=torch.bfloat16, device="cuda")
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.ls_grpo_lmhead_workspace_bytes(R0, cfg.V, d), dtype=torch.uint8, device="cuda")
+    args = (H, W, wl.targets[0], wl.old[0], wl.R, wl.rewards, cfg.eps, 0, 1, loss)
+    L.ls_grpo_lmhead_loss(*args, dW_accum=dW, dH=dH, workspace=ws)     # warm-up (library handle, kernels)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    L.ls_grpo_lmhead_loss(*args, dW_accum=dW, dH=dH, workspace=ws)
+    ev[1].record()
+    L.ls_grpo_lmhead_loss(*args, workspace=ws, scoring_only=True)
+    ev[2].record()
+    torch.cuda.synchronize()
+    t, ts = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+    fl = 2.0 * R0 * cfg.V * d
+    out = {"tokens": R0, "d": d, "vocab": cfg.V, "ms": t, "TFLOPs": 3 * fl / (t * 1e-3) / 1e12,
+           "frac_peak": 3 * fl / (t * 1e-3) / PEAK_BF16, "scoring_ms": ts,
+           "scoring_TFLOPs": fl / (ts * 1e-3) / 1e12}
+    del H, W, dW, dH, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, rows):
     """Time the fp64 oracle on a bounded sample: the first `rows` rows of response 0 against the full
     prompt (an exact sub-problem), for the query heads of kv head 0, forward + backward with
@@ -307,6 +339,10 @@ def main():
     t_score = ev_s[0].elapsed_time(ev_s[1])
     score_bytes = tokens * (2 * cfg.V + 12)
 
+    # LM head fused with the loss (the step to the left of the loss) on the first response: hidden
+    # size d = Hq * Dqk, logits = H W^T chunk by chunk; 3 GEMMs of 2 R V d flops each
+    lm = lmhead_measure(cfg, wl)
+
     # dominant kernel: the dK/dV prompt kernel, timed by the library's kernel timer (HIP events on
     # the launch stream around every launch in the timed region)
     dkdv_ms = dk_total / max(1, dk_launches)
@@ -346,6 +382,7 @@ def main():
             "loss_frac_hbm": loss_bytes / (t_loss * 1e-3) / PEAK_HBM,
             "scoring_loss_ms_per_group": t_score,
             "scoring_loss_GBps": score_bytes / (t_score * 1e-3) / 1e9,
+            "lmhead": lm,
             "peak_mem_GiB": torch.cuda.max_memory_allocated() / 2**30,
             "pages_context": "2.1M token positions on eight H20 GPUs (whole model, end to end; not comparable)",
         },

@@ -211,3 +211,32 @@ def test_latent_kv_requires_aliased_v():
     assert _fwd(d, [0, 0], Kp=K, Vp=K, Ks=K, Vs=V) == L.LS_ERR_UNSUPPORTED
     assert _fwd(d, [0, 0], Kp=K, Vp=K, Ks=V, Vs=V) == L.LS_OK
     assert _fwd(_latent(P=0), [0, 0], Kp=None, Vp=None, Ks=V, Vs=V) == L.LS_OK
+
+
+def _lm(V=4096, d=256, G=2, R=(3, 4), first=0, count=2, H=BAD, W=BAD, dH=BAD, dW=BAD, ws=BAD, nbytes=1 << 40,
+        eps=0.2):
+    Ra = np.asarray(R, dtype=np.int32)
+    rw = np.asarray([1.0, 0.0][:len(R)] + [0.0] * max(0, len(R) - 2), dtype=np.float32)
+    return L.lib().ls_grpo_lmhead_loss(None, V, d, G, Ra.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                       rw.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), eps, first, count, H, W,
+                                       BAD, BAD, BAD, dH, dW, None, None, ws, nbytes)
+
+
+def test_lmhead_validation():
+    """Argument checks of the LM-head entry point, all before any device work."""
+    n = ctypes.c_size_t(0)
+    assert L.lib().ls_grpo_lmhead_workspace_bytes(5000, 4096, 256, ctypes.byref(n)) == L.LS_OK
+    assert n.value >= 2 * 2048 * 4096 * 2                       # logits and dlogits of one chunk
+    assert L.lib().ls_grpo_lmhead_workspace_bytes(-1, 4096, 256, ctypes.byref(n)) == L.LS_ERR_INVALID_ARG
+    assert _lm(V=4100) == L.LS_ERR_UNSUPPORTED                   # rows of the loss kernel: V % 8 == 0
+    assert _lm(d=250) == L.LS_ERR_UNSUPPORTED
+    assert _lm(V=200000) == L.LS_ERR_UNSUPPORTED
+    assert _lm(dH=None) == L.LS_ERR_INVALID_ARG                  # gradients come in pairs
+    assert _lm(dW=None) == L.LS_ERR_INVALID_ARG
+    assert _lm(H=None) == L.LS_ERR_INVALID_ARG
+    assert _lm(H=ctypes.c_void_p(0x1008)) == L.LS_ERR_INVALID_ARG   # misaligned
+    assert _lm(first=1, count=2) == L.LS_ERR_INVALID_ARG
+    assert _lm(eps=1.5) == L.LS_ERR_INVALID_ARG
+    assert _lm(R=(3, 0)) == L.LS_ERR_INVALID_ARG
+    assert _lm(nbytes=100) == L.LS_ERR_WORKSPACE
+    assert _lm(ws=None) == L.LS_ERR_WORKSPACE
