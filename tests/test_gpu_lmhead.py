@@ -33,16 +33,20 @@ def _setup(cfg, lengths, d):
                 targets=torch.from_numpy(y).cuda(), old_d=torch.from_numpy(old).cuda(), eps=cfg.eps, V=cfg.V, d=d)
 
 
-def _run(s, scoring_only=False):
+def _run(s, scoring_only=False, first=0, count=None):
     import torch
     from prefix_shared_branch_amd import lsreplay as L
-    T = int(s["R"].sum())
+    count = s["G"] - first if count is None else count
+    T = int(s["R"][first:first + count].sum())
     loss = torch.zeros(1, dtype=torch.float32, device="cuda")
     logp = torch.empty(T, dtype=torch.float32, device="cuda")
     clip = torch.empty(T, dtype=torch.uint8, device="cuda")
     dW = None if scoring_only else torch.zeros(s["V"], s["d"], dtype=torch.float32, device="cuda")
-    dH = L.ls_grpo_lmhead_loss(s["H"], s["W"], s["targets"], s["old_d"], s["R"], s["rewards"], s["eps"], 0, s["G"],
-                               loss, dW_accum=dW, logp_out=logp, clipped_out=clip, scoring_only=scoring_only)
+    cu = np.concatenate([[0], np.cumsum(s["R"])])
+    r0, r1 = int(cu[first]), int(cu[first + count])
+    dH = L.ls_grpo_lmhead_loss(s["H"][r0:r1], s["W"], s["targets"][r0:r1], s["old_d"][r0:r1], s["R"], s["rewards"],
+                               s["eps"], first, count, loss, dW_accum=dW, logp_out=logp, clipped_out=clip,
+                               scoring_only=scoring_only)
     torch.cuda.synchronize()
     return loss, dH, dW, logp, clip
 
@@ -52,21 +56,25 @@ def _ambiguous(x64):
     return lmhead.round_bf16(x64 * (1 + 2.0 ** -20)) != lmhead.round_bf16(x64 * (1 - 2.0 ** -20))
 
 
-def _check(s, got):
+def _check(s, got, first=0, count=None):
     loss, dH, dW, logp, clip = got
     G, R, eps = s["G"], s["R"], s["eps"]
-    l_ref, dH_ref, dW_ref, logp_ref, clip_ref = lmhead.lmhead_grpo_loss(s["Hf"], s["Wf"], s["y"], s["old"], R,
-                                                                        s["rewards"], G, eps, 0, G)
-    x = lmhead.round_bf16(s["x64"])
-    S_abs = grpo.abs_term_scale(x, s["y"], s["old"], R, s["rewards"], G, eps, 0, G)
+    count = G - first if count is None else count
+    cu = np.concatenate([[0], np.cumsum(R)])
+    sl = slice(int(cu[first]), int(cu[first + count]))
+    y, old, x64 = s["y"][sl], s["old"][sl], s["x64"][sl]
+    l_ref, dH_ref, dW_ref, logp_ref, clip_ref = lmhead.lmhead_grpo_loss(s["Hf"][sl], s["Wf"], y, old, R,
+                                                                        s["rewards"], G, eps, first, count)
+    x = lmhead.round_bf16(x64)
+    S_abs = grpo.abs_term_scale(x, y, old, R, s["rewards"], G, eps, first, count)
     assert abs(float(loss.item()) - l_ref) <= 1e-3 * S_abs, (float(loss.item()), l_ref, S_abs)
-    T = len(s["y"])
-    xt = s["x64"][np.arange(T), s["y"]]
+    T = len(y)
+    xt = x64[np.arange(T), y]
     step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(xt), 1e-30))) - 7)   # one bf16 step at the target logit
     slack = np.where(_ambiguous(xt), step, 0.0)
     dl = np.abs(host_f64(logp) - logp_ref)
     assert np.all(dl <= 1e-4 + slack), np.max(dl - slack)
-    rho = np.exp(logp_ref - s["old"].astype(np.float64))
+    rho = np.exp(logp_ref - old.astype(np.float64))
     sure = (np.abs(rho - (1 - eps)) > 1e-3) & (np.abs(rho - (1 + eps)) > 1e-3)
     np.testing.assert_array_equal(host_f64(clip)[sure].astype(bool), clip_ref[sure])
     if dH is not None:
@@ -83,6 +91,12 @@ def _check(s, got):
 def test_lmhead_loss_matches_oracle(cfg_name, lengths, d):
     s = _setup(inputs.CONFIGS[cfg_name], lengths, d)
     _check(s, _run(s))
+
+
+def test_lmhead_middle_response_of_a_group():
+    """A call over response 1 only: the advantages still come from all G rewards."""
+    s = _setup(inputs.CONFIGS["tiny"], [50, 2100, 30], 128)
+    _check(s, _run(s, first=1, count=1), first=1, count=1)
 
 
 def test_lmhead_scoring_only_and_accumulation():

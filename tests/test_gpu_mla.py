@@ -56,7 +56,7 @@ def test_mla_unaliased_v_is_rejected():
     assert e.value.code == L.LS_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("P,lengths,seed", [(3000 + 17, [37, 130], 56), (64, [9, 2], 57)])
+@pytest.mark.parametrize("P,lengths,seed", [(3000 + 17, [37, 130], 56), (64, [9, 2], 57), (500, [5, 0, 20], 61)])
 def test_mla_backward_exact(P, lengths, seed):
     """One call over several responses: dQ, response-key dK/dV, and the prompt accumulators."""
     from tests.test_gpu_attn import _check_all
