@@ -36,11 +36,16 @@ __device__ __forceinline__ f16x8 join_tr_h(const s16x4& a, const s16x4& b) {
   return __builtin_bit_cast(f16x8, join_tr(a, b));
 }
 
-// LDS tiles of 576-dim rows (1152 B, 72 chunks): logical chunk c of row r at c ^ swz72(r); of
-// 512-dim rows (1024 B, 64 chunks): at c ^ swz64(r). Both keep every 16-lane phase of the
-// interleaved-row fragment reads and of the transposed reads on distinct bank groups.
-__device__ __forceinline__ int swz72(int r) { return ((r >> 1) & 1) | ((r >> 2) & 6); }
-__device__ __forceinline__ int swz64(int r) { return (r & 3) | ((r >> 1) & 12); }
+// LDS tiles of 576-dim rows (1152 B, 72 chunks) and of 512-dim rows (1024 B, 64 chunks): logical
+// chunk c of row r sits at c ^ swz72(r) (low three bits) / c ^ swz64(r) (low four bits). Two read
+// patterns hit them: interleaved-row fragment reads (16 bytes per lane, rows 8a + b and 8a + 4 + b,
+// b < 4, one chunk per 16 lanes) and transposed reads (8 bytes per lane, rows 8q + 4u + e, e < 4,
+// 32 bytes per row). Both swizzles were chosen by measuring LDS bank-conflict cycles
+// (SQ_LDS_BANK_CONFLICT) for these patterns over linear swizzles of row bits 0, 1, 3, 4: each is a
+// simplest one with no conflict cycles for either pattern at its pitch. Neither reads bit 2 (the
+// two interleaved tiles, 4 rows apart, and the two halves of a transposed read share the swizzle).
+__device__ __forceinline__ int swz72(int r) { return (((r >> 3) & 1) << 1) | (((r >> 1) & 1) << 2); }
+__device__ __forceinline__ int swz64(int r) { return (((r >> 3) & 1) << 1) | (((r >> 1) & 1) << 2) | ((r & 1) << 3); }
 
 constexpr int kD = kWideDqk, kDV = kWideDv;
 constexpr int kRow72 = kD * 2, kRow64 = kDV * 2;
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(64 * WideDqCfg::NW, 1) void replay_bwd_dq_wide(BwdA
   const int key_t = 8 * q4 + (i16 >> 2);
   int tb[4];
   {
-    const int b0 = key_t * kRow72 + (q4 << 5) + ((((i16 >> 1) ^ (i16 >> 3)) & 1) << 4) + ((i16 & 1) << 3);
+    const int b0 = key_t * kRow72 + ((((i16 >> 1) & 1) ^ swz72(key_t)) << 4) + ((i16 & 1) << 3);
 #pragma unroll
     for (int d0 = 0; d0 < 4; ++d0) tb[d0] = b0 ^ (d0 << 5);
   }
@@ -470,7 +475,7 @@ __global__ __launch_bounds__(64 * WideKvCfg::NW, 1) void replay_bwd_dkdv_wide(Bw
   const int row_t = 8 * q4 + (i16 >> 2);
   int qtb[4];
   {
-    const int b0 = row_t * kRow72 + (q4 << 5) + ((((i16 >> 1) ^ (i16 >> 3)) & 1) << 4) + ((i16 & 1) << 3);
+    const int b0 = row_t * kRow72 + ((((i16 >> 1) & 1) ^ swz72(row_t)) << 4) + ((i16 & 1) << 3);
 #pragma unroll
     for (int d0 = 0; d0 < 4; ++d0) qtb[d0] = b0 ^ (d0 << 5);
   }

@@ -59,10 +59,14 @@ struct WideFwdCfg {
 };
 
 // LDS K tile: row r (key) holds 72 chunks of 16 bytes; logical chunk c sits at c ^ wide_swz(r)
-// (only the low three bits change, so a chunk stays in its group of eight). For the 16 keys of a
-// score tile, or the 8 keys x 2 chunks of a pair of transposed reads, the swizzle and the row pitch
-// (1152 B, odd in 128-byte units) put every 16-byte read of a 16-lane phase in its own bank group.
-__device__ __forceinline__ int wide_swz(int r) { return ((r >> 1) & 1) | ((r >> 2) & 6); }
+// (only the low three bits change, so a chunk stays in its group of eight). Two read patterns hit
+// the tile: score-tile reads (16 bytes per lane, keys 8a + b and 8a + 4 + b, b < 4, one chunk per
+// 16 lanes) and transposed reads (8 bytes per lane, keys 8q + 4u + e, e < 4, 32 bytes per key).
+// With the 1152-byte pitch, this swizzle (bits 3 and 1 of the key into chunk bits 1 and 2) is the
+// simplest one that measured zero LDS bank-conflict cycles for both patterns among all linear
+// 3-bit swizzles of key bits 0, 1, 3, 4 (SQ_LDS_BANK_CONFLICT on gfx950). It ignores bit 2, so the
+// two score tiles (keys 4 apart) and both halves of a transposed read share it.
+__device__ __forceinline__ int wide_swz(int r) { return (((r >> 3) & 1) << 1) | (((r >> 1) & 1) << 2); }
 
 __global__ __launch_bounds__(64 * WideFwdCfg::NW, 1) void replay_fwd_wide(FwdArgs a) {
   using C = WideFwdCfg;
@@ -119,13 +123,13 @@ __global__ __launch_bounds__(64 * WideFwdCfg::NW, 1) void replay_fwd_wide(FwdArg
 #pragma unroll
   for (int s0 = 0; s0 < 2; ++s0) kb[s0] = key_a * C::KROW + (((4 * s0 + q4) ^ wide_swz(key_a)) << 4);
   // Transposed V^T reads: lane j of group q addresses key 8q + 4u + j / 4, dims 16 d + 4 (j % 4) .. +3
-  // and receives dims 16 d + j of keys 8q + 4u .. +3. Chunk 2d + (j/2)%2 XOR the row swizzle
-  // ((j >> 3) & 1 | 2 q) gives 32 (d ^ q) + 16 (((j >> 1) ^ (j >> 3)) & 1) + 8 (j & 1) bytes, so
-  // for d = 4 d' + d0 the offset is vb[d0] + 128 d' (+ 4 rows for u = 1).
+  // and receives dims 16 d + j of keys 8q + 4u .. +3. Its chunk 2d + (j / 2) % 2 sits at
+  // (2d) ^ X with X = ((j / 2) % 2) ^ wide_swz(row) (the swizzle does not depend on u), i.e. at byte
+  // (32 d) ^ 16 X of the row: for d = 4 d' + d0 the offset is vb[d0] + 128 d' (+ 4 rows for u = 1).
   const int key_t = 8 * q4 + (i16 >> 2);
   int vb[4];
   {
-    const int b0 = key_t * C::KROW + ((q4 & 3) << 5) + ((((i16 >> 1) ^ (i16 >> 3)) & 1) << 4) + ((i16 & 1) << 3);
+    const int b0 = key_t * C::KROW + ((((i16 >> 1) & 1) ^ wide_swz(key_t)) << 4) + ((i16 & 1) << 3);
 #pragma unroll
     for (int d0 = 0; d0 < 4; ++d0) vb[d0] = b0 ^ (d0 << 5);
   }
@@ -158,14 +162,16 @@ __global__ __launch_bounds__(64 * WideFwdCfg::NW, 1) void replay_fwd_wide(FwdArg
     asm volatile("" : "+v"(ln));  // per-lane offsets recomputed per tile rather than pinned
 #pragma unroll
     for (int k = 0; k < C::PPW; ++k) {
-      // pieces wv, wv + 8, wv + 16, wv + 24, then 32 + wv for waves 0-3; waves 4-7 repeat a piece
-      // into a scratch slot, so that every wave issues the same number of loads per tile
+      // pieces wv, wv + 8, wv + 16, wv + 24, then 32 + wv for waves 0-3; waves 4-7 load the tile's
+      // first kilobyte (just fetched by wave 0) into a scratch slot, so that every wave issues the
+      // same number of loads per tile
+      const bool real = k < C::PPW - 1 || wv < 4;
       const int pc = k < C::PPW - 1 ? wv + C::NW * k : C::NP - 4 + (wv & 3);
       const int unit = pc * 64 + ln;
       const int row = unit / 72;
       const int c = (unit - row * 72) ^ wide_swz(row);
-      char* d = (k < C::PPW - 1 || wv < 4) ? dst + pc * 1024 : sdummy + (wv - 4) * 1024;
-      lds_dma16_buf(rs, (uint32_t)(row * ldk2 + (c << 4)), d);
+      const uint32_t voff = real ? (uint32_t)(row * ldk2 + (c << 4)) : (uint32_t)(ln << 4);
+      lds_dma16_buf(rs, voff, real ? dst + pc * 1024 : sdummy + (wv - 4) * 1024);
     }
   };
 
