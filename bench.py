@@ -99,6 +99,7 @@ class Workload:
         self.dkp = torch.zeros(cfg.P, cfg.Hkv, cfg.Dqk, dtype=torch.float32, device=dev)
         self.dvp = torch.zeros(cfg.P, cfg.Hkv, cfg.Dv, dtype=torch.float32, device=dev)
         self.o = torch.empty(Rmax, cfg.Hq, cfg.Dv, dtype=torch.bfloat16, device=dev)
+        self.o_lo = torch.empty(Rmax, cfg.Hq, cfg.Dv, dtype=torch.bfloat16, device=dev)  # O's rounding residual
         self.dq = torch.empty(Rmax, cfg.Hq, cfg.Dqk, dtype=torch.bfloat16, device=dev)
         self.dks = torch.empty(Rmax, cfg.Hkv, cfg.Dqk, dtype=torch.bfloat16, device=dev)
         self.dvs = torch.empty(Rmax, cfg.Hkv, cfg.Dv, dtype=torch.bfloat16, device=dev)
@@ -122,7 +123,7 @@ class Workload:
         if ev:
             ev[0].record()
         o, lse = L.ls_replay_attn_fwd(self.q[sl], self.ks[sl], self.vs[sl], self.kp, self.vp, [0, R], cfg.scale,
-                                      out=self.o[:R], lse=self.lse[i], workspace=self.ws)
+                                      out=self.o[:R], lse=self.lse[i], workspace=self.ws, o_lo=self.o_lo[:R])
         if ev:
             ev[1].record()
         L.ls_grpo_token_loss(self.logits[i], self.targets[i], self.old[i], self.R, self.rewards, cfg.eps, i, 1,
@@ -131,7 +132,7 @@ class Workload:
             ev[2].record()
         L.ls_replay_attn_bwd(self.q[sl], self.ks[sl], self.vs[sl], self.kp, self.vp, [0, R], o, lse, self.do[sl],
                              self.dkp if exact else None, self.dvp if exact else None, cfg.scale,
-                             dq=self.dq[:R], dks=self.dks[:R], dvs=self.dvs[:R], workspace=self.ws)
+                             dq=self.dq[:R], dks=self.dks[:R], dvs=self.dvs[:R], workspace=self.ws, o_lo=self.o_lo[:R])
         if ev:
             ev[3].record()
             times.append(ev)

@@ -90,6 +90,12 @@ int ls_replay_attn_workspace_bytes(const ls_attn_desc* desc, int32_t n_resp, con
  *  Ks, Vs  device bf16 [T, Hkv, *] with strides ldk/ldv (latent KV: Vs = Ks).
  *  O       device bf16 [T, Hq, Dv] contiguous, overwritten.
  *  lse     device fp32 [Hq, T], overwritten: natural-log sum of exp of the visible scores.
+ *  O_lo    optional device bf16 [T, Hq, Dv] contiguous, or NULL. When given it is overwritten with
+ *          the bf16 of O32 - O, where O32 is the fp32 output before rounding: O + O_lo carries
+ *          the output to about 16 significant bits. The backward uses it for the row term
+ *          Delta = rowsum(dO * O) of dS = P (dP - Delta); without it Delta sees O's bf16 rounding,
+ *          which matters only where a handful of prompt keys carry whole softmax rows (very
+ *          short prompts: the prompt accumulators then drift by ~2e-3 relative instead of <1e-3).
  *  workspace  device, >= ls_replay_attn_workspace_bytes(which = 0), 256-byte aligned; may be
  *          NULL when that size is 0.
  * All device pointers 16-byte aligned. T == 0 returns LS_OK and launches nothing. */
@@ -97,12 +103,13 @@ int ls_replay_attn_fwd(void* stream, const ls_attn_desc* desc,
                        const void* Kp, const void* Vp,
                        int32_t n_resp, const int32_t* cu_seqlens,
                        const void* Q, const void* Ks, const void* Vs,
-                       void* O, float* lse,
+                       void* O, float* lse, void* O_lo,
                        void* workspace, size_t workspace_bytes);
 
 /* Replay attention backward (same section; the prompt-side term is the dl/dz_P part of the
  * gradient decomposition of §2-2). Arguments as in ls_replay_attn_fwd, plus:
  *  O, lse  the forward's outputs for these inputs.
+ *  O_lo    the forward's O_lo for these inputs, or NULL (Delta from the bf16 O alone).
  *  dO      device bf16 [T, Hq, Dv] contiguous.
  *  dQ      device bf16 [T, Hq, Dqk] contiguous, overwritten.
  *  dKs     device bf16 [T, Hkv, Dqk] contiguous, overwritten.
@@ -120,7 +127,7 @@ int ls_replay_attn_bwd(void* stream, const ls_attn_desc* desc,
                        const void* Kp, const void* Vp,
                        int32_t n_resp, const int32_t* cu_seqlens,
                        const void* Q, const void* Ks, const void* Vs,
-                       const void* O, const float* lse, const void* dO,
+                       const void* O, const float* lse, const void* O_lo, const void* dO,
                        void* dQ, void* dKs, void* dVs,
                        float* dKp_accum, float* dVp_accum,
                        void* workspace, size_t workspace_bytes);
@@ -134,6 +141,7 @@ int ls_replay_attn_bwd(void* stream, const ls_attn_desc* desc,
  *  Ks, Vs   device bf16 [q0 + nq, Hkv, *] with strides ldk/ldv: the response's keys from its
  *           first token through the block's last.
  *  O, lse   device bf16 [nq, Hq, Dv] and fp32 [Hq, nq] for the block's rows, overwritten.
+ *  O_lo     optional bf16 [nq, Hq, Dv] rounding residual of O, as in ls_replay_attn_fwd.
  * Other arguments as in ls_replay_attn_fwd. nq == 0 returns LS_OK and launches nothing. */
 int ls_replay_attn_block_workspace_bytes(const ls_attn_desc* desc, int32_t q0, int32_t nq, int32_t which,
                                          size_t* bytes);
@@ -141,11 +149,12 @@ int ls_replay_attn_fwd_block(void* stream, const ls_attn_desc* desc,
                              const void* Kp, const void* Vp,
                              int32_t q0, int32_t nq,
                              const void* Q, const void* Ks, const void* Vs,
-                             void* O, float* lse,
+                             void* O, float* lse, void* O_lo,
                              void* workspace, size_t workspace_bytes);
 
 /* Backward of one block (arguments as in ls_replay_attn_fwd_block and ls_replay_attn_bwd):
  *  O, lse, dO  the block's forward outputs and output gradient: [nq, Hq, Dv], [Hq, nq], [nq, Hq, Dv].
+ *  O_lo        the block forward's O_lo, or NULL.
  *  dQ          device bf16 [nq, Hq, Dqk], overwritten (the block's rows only).
  *  dKs_accum, dVs_accum  device fp32 [q0 + nq, Hkv, Dqk] / [q0 + nq, Hkv, Dv] contiguous, both
  *              required: the block's contribution to the gradients of the response's keys
@@ -157,7 +166,7 @@ int ls_replay_attn_bwd_block(void* stream, const ls_attn_desc* desc,
                              const void* Kp, const void* Vp,
                              int32_t q0, int32_t nq,
                              const void* Q, const void* Ks, const void* Vs,
-                             const void* O, const float* lse, const void* dO,
+                             const void* O, const float* lse, const void* O_lo, const void* dO,
                              void* dQ, float* dKs_accum, float* dVs_accum,
                              float* dKp_accum, float* dVp_accum,
                              void* workspace, size_t workspace_bytes);

@@ -90,11 +90,12 @@ void fill_geom(lsr::AttnGeom* g, const ls_attn_desc* d, const void* Kp, const vo
 
 int fwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
              const int32_t* cu_seqlens, const int32_t* kcu, const void* Q, const void* Ks, const void* Vs, void* O,
-             float* lse, void* workspace, size_t workspace_bytes);
+             float* lse, void* O_lo, void* workspace, size_t workspace_bytes);
 int bwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
              const int32_t* cu_seqlens, const int32_t* kcu, const void* Q, const void* Ks, const void* Vs,
-             const void* O, const float* lse, const void* dO, void* dQ, void* dKs, void* dVs, float* dKs_acc,
-             float* dVs_acc, float* dKp_accum, float* dVp_accum, void* workspace, size_t workspace_bytes);
+             const void* O, const float* lse, const void* O_lo, const void* dO, void* dQ, void* dKs, void* dVs,
+             float* dKs_acc, float* dVs_acc, float* dKp_accum, float* dVp_accum, void* workspace,
+             size_t workspace_bytes);
 
 }  // namespace
 
@@ -123,18 +124,18 @@ int ls_replay_attn_workspace_bytes(const ls_attn_desc* desc, int32_t n_resp, con
 
 int ls_replay_attn_fwd(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
                        const int32_t* cu_seqlens, const void* Q, const void* Ks, const void* Vs, void* O, float* lse,
-                       void* workspace, size_t workspace_bytes) {
-  return fwd_impl(stream, desc, Kp, Vp, n_resp, cu_seqlens, cu_seqlens, Q, Ks, Vs, O, lse, workspace,
+                       void* O_lo, void* workspace, size_t workspace_bytes) {
+  return fwd_impl(stream, desc, Kp, Vp, n_resp, cu_seqlens, cu_seqlens, Q, Ks, Vs, O, lse, O_lo, workspace,
                   workspace_bytes);
 }
 
 int ls_replay_attn_bwd(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
                        const int32_t* cu_seqlens, const void* Q, const void* Ks, const void* Vs, const void* O,
-                       const float* lse, const void* dO, void* dQ, void* dKs, void* dVs, float* dKp_accum,
-                       float* dVp_accum, void* workspace, size_t workspace_bytes) {
+                       const float* lse, const void* O_lo, const void* dO, void* dQ, void* dKs, void* dVs,
+                       float* dKp_accum, float* dVp_accum, void* workspace, size_t workspace_bytes) {
   if (!dKs || !dVs) return LS_ERR_INVALID_ARG;
-  return bwd_impl(stream, desc, Kp, Vp, n_resp, cu_seqlens, cu_seqlens, Q, Ks, Vs, O, lse, dO, dQ, dKs, dVs, nullptr,
-                  nullptr, dKp_accum, dVp_accum, workspace, workspace_bytes);
+  return bwd_impl(stream, desc, Kp, Vp, n_resp, cu_seqlens, cu_seqlens, Q, Ks, Vs, O, lse, O_lo, dO, dQ, dKs, dVs,
+                  nullptr, nullptr, dKp_accum, dVp_accum, workspace, workspace_bytes);
 }
 
 int ls_replay_attn_block_workspace_bytes(const ls_attn_desc* desc, int32_t q0, int32_t nq, int32_t which,
@@ -149,22 +150,23 @@ int ls_replay_attn_block_workspace_bytes(const ls_attn_desc* desc, int32_t q0, i
 }
 
 int ls_replay_attn_fwd_block(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t q0,
-                             int32_t nq, const void* Q, const void* Ks, const void* Vs, void* O, float* lse,
+                             int32_t nq, const void* Q, const void* Ks, const void* Vs, void* O, float* lse, void* O_lo,
                              void* workspace, size_t workspace_bytes) {
   if (q0 < 0 || nq < 0 || (int64_t)q0 + nq > INT32_MAX) return LS_ERR_INVALID_ARG;
   const int32_t cu[2] = {0, nq}, kcu[2] = {0, q0 + nq};
-  return fwd_impl(stream, desc, Kp, Vp, 1, cu, kcu, Q, Ks, Vs, O, lse, workspace, workspace_bytes);
+  return fwd_impl(stream, desc, Kp, Vp, 1, cu, kcu, Q, Ks, Vs, O, lse, O_lo, workspace, workspace_bytes);
 }
 
 int ls_replay_attn_bwd_block(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t q0,
                              int32_t nq, const void* Q, const void* Ks, const void* Vs, const void* O,
-                             const float* lse, const void* dO, void* dQ, float* dKs_accum, float* dVs_accum,
-                             float* dKp_accum, float* dVp_accum, void* workspace, size_t workspace_bytes) {
+                             const float* lse, const void* O_lo, const void* dO, void* dQ, float* dKs_accum,
+                             float* dVs_accum, float* dKp_accum, float* dVp_accum, void* workspace,
+                             size_t workspace_bytes) {
   if (q0 < 0 || nq < 0 || (int64_t)q0 + nq > INT32_MAX) return LS_ERR_INVALID_ARG;
   if (!dKs_accum || !dVs_accum) return LS_ERR_INVALID_ARG;
   const int32_t cu[2] = {0, nq}, kcu[2] = {0, q0 + nq};
-  return bwd_impl(stream, desc, Kp, Vp, 1, cu, kcu, Q, Ks, Vs, O, lse, dO, dQ, nullptr, nullptr, dKs_accum, dVs_accum,
-                  dKp_accum, dVp_accum, workspace, workspace_bytes);
+  return bwd_impl(stream, desc, Kp, Vp, 1, cu, kcu, Q, Ks, Vs, O, lse, O_lo, dO, dQ, nullptr, nullptr, dKs_accum,
+                  dVs_accum, dKp_accum, dVp_accum, workspace, workspace_bytes);
 }
 
 }  // extern "C"
@@ -173,7 +175,7 @@ namespace {
 
 int fwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
              const int32_t* cu_seqlens, const int32_t* kcu, const void* Q, const void* Ks, const void* Vs, void* O,
-             float* lse, void* workspace, size_t workspace_bytes) {
+             float* lse, void* O_lo, void* workspace, size_t workspace_bytes) {
   lsr::AttnPlan pl;
   int st = plan_for(desc, n_resp, cu_seqlens, kcu, 0, &pl);
   if (st != LS_OK) return st;
@@ -184,6 +186,7 @@ int fwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void*
   const void* dev[] = {Q, Ks, Vs, O, lse};
   for (const void* p : dev)
     if (!p || !aligned(p, 16)) return LS_ERR_INVALID_ARG;
+  if (O_lo && !aligned(O_lo, 16)) return LS_ERR_INVALID_ARG;
   if (pl.ws_bytes > 0 && (!workspace || !aligned(workspace, 256))) return LS_ERR_WORKSPACE;
   if (workspace_bytes < pl.ws_bytes) return LS_ERR_WORKSPACE;
 
@@ -191,6 +194,7 @@ int fwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void*
   std::memset(&a, 0, sizeof(a));
   fill_geom(&a.geo, desc, Kp, Vp, n_resp, cu_seqlens, kcu, Q, Ks, Vs);
   a.O = static_cast<uint16_t*>(O);
+  a.O_lo = static_cast<uint16_t*>(O_lo);
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);
   a.o_part = pl.splits > 1 ? reinterpret_cast<float*>(ws + pl.off_a) : nullptr;
@@ -202,6 +206,10 @@ int fwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void*
   for (int i = 0; i <= kMaxResp; ++i) a.tile0[i] = pl.tile0[i];
   a.VTp = reinterpret_cast<const uint16_t*>(ws + pl.off_c);
   a.VTs = reinterpret_cast<const uint16_t*>(ws + pl.off_d);
+  if (desc->Dqk != lsr::kWideDqk) {  // latent KV reads V from the K tiles as bf16 (no V scale)
+    a.vscale_part = reinterpret_cast<float*>(ws + pl.off_sc);
+    a.vscale = a.vscale_part + lsr::kScaleBlocks * 8;
+  }
   a.ppad = pl.ppad;
   a.tpad = pl.tpad;
   for (int i = 0; i <= kMaxResp; ++i) a.spos[i] = pl.spos[i];
@@ -211,8 +219,9 @@ int fwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void*
 
 int bwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void* Vp, int32_t n_resp,
              const int32_t* cu_seqlens, const int32_t* kcu, const void* Q, const void* Ks, const void* Vs,
-             const void* O, const float* lse, const void* dO, void* dQ, void* dKs, void* dVs, float* dKs_acc,
-             float* dVs_acc, float* dKp_accum, float* dVp_accum, void* workspace, size_t workspace_bytes) {
+             const void* O, const float* lse, const void* O_lo, const void* dO, void* dQ, void* dKs, void* dVs,
+             float* dKs_acc, float* dVs_acc, float* dKp_accum, float* dVp_accum, void* workspace,
+             size_t workspace_bytes) {
   if ((dKp_accum == nullptr) != (dVp_accum == nullptr)) return LS_ERR_INVALID_ARG;
   const bool exact = dKp_accum != nullptr;
   lsr::AttnPlan pl;
@@ -226,6 +235,7 @@ int bwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void*
   const void* dev[] = {Q, Ks, Vs, O, lse, dO, dQ, dKs_acc ? dKs_acc : dKs, dVs_acc ? dVs_acc : dVs};
   for (const void* p : dev)
     if (!p || !aligned(p, 16)) return LS_ERR_INVALID_ARG;
+  if (O_lo && !aligned(O_lo, 16)) return LS_ERR_INVALID_ARG;
   if (pl.ws_bytes > 0 && (!workspace || !aligned(workspace, 256))) return LS_ERR_WORKSPACE;
   if (workspace_bytes < pl.ws_bytes) return LS_ERR_WORKSPACE;
 
@@ -233,6 +243,7 @@ int bwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void*
   std::memset(&a, 0, sizeof(a));
   fill_geom(&a.geo, desc, Kp, Vp, n_resp, cu_seqlens, kcu, Q, Ks, Vs);
   a.O = static_cast<const uint16_t*>(O);
+  a.O_lo = static_cast<const uint16_t*>(O_lo);
   a.lse = lse;
   a.dO = static_cast<const uint16_t*>(dO);
   a.dQ = static_cast<uint16_t*>(dQ);

@@ -84,6 +84,8 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
       off = align256(off + (size_t)Hkv * Dv * pl->ppad * 2);
       pl->off_d = off;
       off = align256(off + (size_t)Hkv * Dv * pl->tpad * 2);
+      pl->off_sc = off;  // fp16 scale of V: partial maxima (8 per block), then the scale
+      off = align256(off + (size_t)(kScaleBlocks + 1) * 8 * 4);
     }
   } else {
     pl->off_a = off;  // delta [Hq, T]

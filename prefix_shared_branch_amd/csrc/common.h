@@ -64,6 +64,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// bf16 of the rounding residuals x0 - bf16(x0), x1 - bf16(x1), given rounded = pack_bf16x2(x0, x1):
+// the pair (rounded, residual) carries x to about 16 significant bits.
+__device__ __forceinline__ uint32_t pack_bf16x2_residual(float x0, float x1, uint32_t rounded) {
+  return pack_bf16x2(x0 - bf16_lo(rounded), x1 - bf16_hi(rounded));
+}
+
 // 8 consecutive registers of a C tile (r0..r0+7) -> bf16 B/A operand.
 __device__ __forceinline__ bf16x8 c_regs_to_bf16x8(const f32x16& c, int r0) {
   bf16x8 v;

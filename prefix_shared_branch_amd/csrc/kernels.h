@@ -125,15 +125,23 @@ struct ScaleArgs {
   float* scales;         // [4]
 };
 hipError_t launch_bwd_scales(const ScaleArgs& a, hipStream_t st);
+// Forward V scale (head dims 64 / 128): scales[0] = s_V, a power of two with max |V| s_V <= 2^15 over
+// the prompt and response V rows, scales[1] = 1 / s_V. Only Vp, Vs, ldv, P, Tk, Hkv, Dv, partial and
+// scales are read.
+hipError_t launch_fwd_vscale(const ScaleArgs& a, hipStream_t st);
 
 struct FwdArgs {
   AttnGeom geo;
   uint16_t* O;          // bf16 [T, Hq, Dv]
+  uint16_t* O_lo;       // optional bf16 [T, Hq, Dv]: bf16 of O - bf16(O), the fp32 output's rounding residual
   float* lse;           // [Hq, T]
   float* o_part;        // [S, T, Hq, Dv] fp32 (S > 1)
   float* lse_part;      // [S, Hq, T] (S > 1)
   const uint16_t* VTp;  // packed prompt V: [Hkv * Dv, ppad] (pack.hip layout)
   const uint16_t* VTs;  // packed response V: [Hkv * Dv, tpad], response i from slot spos[i]
+                        // (head dims 64 / 128: fp16 of V s_V, see vscale)
+  float* vscale_part;   // [kScaleBlocks, 8] partial maxima of |V|
+  float* vscale;        // {s_V, 1 / s_V}
   int64_t ppad, tpad;
   int32_t spos[kMaxResp + 1];
   int32_t splits;       // S
@@ -146,6 +154,7 @@ struct FwdArgs {
 struct BwdArgs {
   AttnGeom geo;
   const uint16_t* O;
+  const uint16_t* O_lo;  // optional: the forward's rounding residual of O (Delta from O + O_lo)
   const float* lse;
   const uint16_t* dO;
   uint16_t* dQ;

@@ -212,7 +212,54 @@ __global__ __launch_bounds__(256) void bwd_scale_final(ScaleArgs a) {
   }
 }
 
+// Forward: partial maxima of |V| over the prompt and response V rows (one per block).
+template <int DV>
+__global__ __launch_bounds__(256) void fwd_vscale_partials(ScaleArgs a) {
+  const int64_t start = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  float amax = 0.0f, nmax = 0.0f;
+  if (a.P > 0) rows_max<DV>(a.Vp, a.P, a.ldv, a.Hkv, start, stride, amax, nmax);
+  rows_max<DV>(a.Vs, a.Tk, a.ldv, a.Hkv, start, stride, amax, nmax);
+  __shared__ float red[4];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = __builtin_elementwise_maximum(amax, __shfl_xor(amax, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    a.partial[blockIdx.x * 8] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(red[0], red[1]),
+                                                              __builtin_elementwise_maximum(red[2], red[3]));
+}
+
+// s_V = 2^k with max |V| s_V <= 2^15 (fp16 holds V s_V exactly where its exponent fits; products
+// with probabilities <= 2^8 accumulate in fp32), and its exact inverse
+__global__ __launch_bounds__(256) void fwd_vscale_final(ScaleArgs a) {
+  __shared__ float red[4];
+  float v = 0.0f;
+  for (int b = threadIdx.x; b < kScaleBlocks; b += 256) v = __builtin_elementwise_maximum(v, a.partial[b * 8]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = __builtin_elementwise_maximum(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(red[0], red[1]),
+                                                  __builtin_elementwise_maximum(red[2], red[3]));
+    const float s = pow2_fit(m);
+    a.scales[0] = s;
+    a.scales[1] = 1.0f / s;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_fwd_vscale(const ScaleArgs& a, hipStream_t st) {
+  if (a.Dv == 64) hipLaunchKernelGGL((fwd_vscale_partials<64>), dim3(kScaleBlocks), dim3(256), 0, st, a);
+  else if (a.Dv == 128) hipLaunchKernelGGL((fwd_vscale_partials<128>), dim3(kScaleBlocks), dim3(256), 0, st, a);
+  else return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fwd_vscale_final, dim3(1), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd_scales(const ScaleArgs& a, hipStream_t st) {
   if (a.Dqk == 64 && a.Dv == 64) hipLaunchKernelGGL((bwd_scale_partials<64, 64>), dim3(kScaleBlocks), dim3(256), 0, st, a);

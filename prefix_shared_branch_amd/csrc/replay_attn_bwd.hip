@@ -2,6 +2,7 @@
 // P = exp(S scale - LSE), dP = dO V^T, Delta = rowsum(dO * O) and dS = P (dP - Delta),
 //   dV_j += sum_rows P_rj dO_r,  dK_j += scale sum_rows dS_rj Q_r,  dQ_r = scale sum_j dS_rj K_j.
 //
+// Delta is taken from O + O_lo when the forward's rounding residual O_lo is given (O alone otherwise).
 // This file holds the Delta pass (replay_bwd_pre) and the launch sequence of one backward call:
 // Delta, then the dK/dV kernels (replay_attn_dkdv.hip: key-tile owners, prompt keys accumulated in
 // place), then dQ (replay_attn_dq.hip: query-tile owners, split-K over the prompt).
@@ -25,8 +26,11 @@ __global__ __launch_bounds__(256) void replay_bwd_pre(BwdArgs a) {
   if (ok) {
     const u32x4 x = *reinterpret_cast<const u32x4*>(a.dO + pair * DV + c * 8);
     const u32x4 y = *reinterpret_cast<const u32x4*>(a.O + pair * DV + c * 8);
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (a.O_lo) z = *reinterpret_cast<const u32x4*>(a.O_lo + pair * DV + c * 8);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s += bf16_lo(x[q]) * bf16_lo(y[q]) + bf16_hi(x[q]) * bf16_hi(y[q]);
+    for (int q = 0; q < 4; ++q)
+      s += bf16_lo(x[q]) * (bf16_lo(y[q]) + bf16_lo(z[q])) + bf16_hi(x[q]) * (bf16_hi(y[q]) + bf16_hi(z[q]));
   }
 #pragma unroll
   for (int o = TPP / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);

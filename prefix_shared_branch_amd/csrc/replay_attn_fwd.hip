@@ -11,6 +11,11 @@
 // where P^T comes straight from the score accumulators and every V^T fragment is one 16-byte LDS
 // read. Two waves share each SIMD and run half a step apart, so one wave's softmax (VALU) overlaps
 // the other's MFMAs.
+// The PV product runs in fp16 (MFMA 32x32x16 f16, the same rate as bf16): the packed V^T holds
+// fp16 of V s_V, s_V a power of two with max |V| s_V <= 2^15 (fwd_vscale in pack.hip), so the
+// conversion is exact wherever the exponent fits, and P keeps 11 significant bits instead of 8.
+// The backward's row term Delta = rowsum(dO O) is formed from this output, and a single heavy
+// prompt key (very short prompts) passes the weight rounding straight into the prompt gradient.
 // The softmax stabiliser is only moved when a row maximum exceeds it by more than 2^8 (in exp2
 // units), so the O rescale is rare; probabilities stay <= 256, far inside fp32/bf16 range.
 // Workgroup ids are mapped so that each XCD owns a contiguous run of (kv head, split) streams:
@@ -19,6 +24,8 @@
 //
 // replay_fwd_merge: log-sum-exp merge of the split partials,
 //   lse = log sum_s exp(lse_s),  O = sum_s exp(lse_s - lse) O_s.
+#include <cstring>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void replay_fwd(FwdArgs a) {
   float mu = -INFINITY;  // stabiliser (score * scale * log2 e)
   float l_run = 0.0f;    // row sum of this lane's keys
   f32x16 st;             // S^T of the 32-key block whose softmax comes next
-  bf16x8 p0, p1;         // P^T of the block whose PV product comes next (two 16-key B operands)
+  f16x8 p0, p1;          // P^T of the block whose PV product comes next (two 16-key B operands)
   const float c2 = G.scale_log2;
 
   // MFMA phase of 32-key block j = 2t + h: S^T = K Q^T for block j (tile t, half h) and
@@ -227,9 +234,9 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void replay_fwd(FwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) st = mfma32(kf[ks], qf[ks], st);
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) o[nb] = mfma32(vf[0][nb], p0, o[nb]);
+    for (int nb = 0; nb < C::NB; ++nb) o[nb] = mfma32h(__builtin_bit_cast(f16x8, vf[0][nb]), p0, o[nb]);
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) o[nb] = mfma32(vf[1][nb], p1, o[nb]);
+    for (int nb = 0; nb < C::NB; ++nb) o[nb] = mfma32h(__builtin_bit_cast(f16x8, vf[1][nb]), p1, o[nb]);
     // Issue order: the K fragment reads, then the score MFMAs each followed by V^T fragment reads
     // (a direct load after the second and the sixth), then the PV MFMAs; LDS latency hides under
     // the MFMA chain.
@@ -285,8 +292,8 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void replay_fwd(FwdArgs a) {
       ls1 += st[r + 1];
     }
     l_run += ls0 + ls1;
-    p0 = c_regs_to_bf16x8(st, 0);
-    p1 = c_regs_to_bf16x8(st, 8);
+    p0 = c_regs_to_f16x8(st, 0);
+    p1 = c_regs_to_f16x8(st, 8);
   };
 
   // Both groups run the same program: per 32-key block j, an MFMA phase then a softmax phase, each
@@ -331,7 +338,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void replay_fwd(FwdArgs a) {
       *reinterpret_cast<LSR_LDS u32x4*>(reinterpret_cast<uintptr_t>(z + (i * 64 * C::NW + threadIdx.x) * 16)) =
           u32x4{0u, 0u, 0u, 0u};
   }
-  p0 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  p0 = __builtin_bit_cast(f16x8, u32x4{0u, 0u, 0u, 0u});
   p1 = p0;
   wait_lds();
   wait_vmem_le<2 * C::PPW>();  // tile 0 before barrier 0: tiles 1 and 2 may be in flight
@@ -360,17 +367,23 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void replay_fwd(FwdArgs a) {
   const float l = pair_sum(l_run);
   if (!rvalid) return;
   const int64_t tok = tokb + trow;
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const float inv = l > 0.0f ? a.vscale[1] / l : 0.0f;   // O = (V s_V)^T P^T / (l s_V)
   const float lse = l > 0.0f ? (mu + fast_log2(l)) * kLn2 : -INFINITY;
   if (a.splits == 1) {
-    uint16_t* orow = a.O + (tok * G.Hq + hq) * DV + 4 * hl;
+    const int64_t off = (tok * G.Hq + hq) * DV + 4 * hl;
+    uint16_t* orow = a.O + off;
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const u32x2 v = {pack_bf16x2(o[nb][4 * q] * inv, o[nb][4 * q + 1] * inv),
-                         pack_bf16x2(o[nb][4 * q + 2] * inv, o[nb][4 * q + 3] * inv)};
+        const float x0 = o[nb][4 * q] * inv, x1 = o[nb][4 * q + 1] * inv;
+        const float x2 = o[nb][4 * q + 2] * inv, x3 = o[nb][4 * q + 3] * inv;
+        const u32x2 v = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
         *reinterpret_cast<u32x2*>(orow + nb * 32 + 8 * q) = v;
+        if (a.O_lo) {
+          const u32x2 r = {pack_bf16x2_residual(x0, x1, v[0]), pack_bf16x2_residual(x2, x3, v[1])};
+          *reinterpret_cast<u32x2*>(a.O_lo + off + nb * 32 + 8 * q) = r;
+        }
       }
     if (hl == 0) a.lse[(int64_t)hq * G.T + tok] = lse;
   } else {
@@ -411,6 +424,10 @@ __global__ __launch_bounds__(256) void replay_fwd_merge(FwdArgs a) {
   }
   const u32x2 ov = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
   *reinterpret_cast<u32x2*>(a.O + (t * G.Hq + h) * DV + 4 * c) = ov;
+  if (a.O_lo) {
+    const u32x2 r = {pack_bf16x2_residual(acc[0], acc[1], ov[0]), pack_bf16x2_residual(acc[2], acc[3], ov[1])};
+    *reinterpret_cast<u32x2*>(a.O_lo + (t * G.Hq + h) * DV + 4 * c) = r;
+  }
   if (c == 0) a.lse[(int64_t)h * G.T + t] = lse;
 }
 
@@ -418,11 +435,27 @@ template <int D, int DV>
 hipError_t fwd_go(FwdArgs& a, hipStream_t st) {
   const long long W = (long long)a.qtiles * a.geo.Hkv * a.splits;
   if (W == 0) return hipSuccess;
-  // dimension-major packed V of the prompt and of every response
+  // V scale, then dimension-major packed fp16 V s_V of the prompt and of every response
   const AttnGeom& G = a.geo;
+  {
+    ScaleArgs sa;
+    std::memset(&sa, 0, sizeof(sa));
+    sa.Vp = G.Vp;
+    sa.Vs = G.Vs;
+    sa.ldv = G.ldv;
+    sa.P = G.P;
+    sa.Tk = G.Tk;
+    sa.Hkv = G.Hkv;
+    sa.Dqk = D;
+    sa.Dv = DV;
+    sa.partial = a.vscale_part;
+    sa.scales = a.vscale;
+    hipError_t e = launch_fwd_vscale(sa, st);
+    if (e != hipSuccess) return e;
+  }
   if (G.P > 0) {
     PackArgs p;
-    p.f16_scale = nullptr;
+    p.f16_scale = a.vscale;
     p.src = G.Vp;
     p.ld = G.ldv;
     p.dim = DV;
@@ -442,7 +475,7 @@ hipError_t fwd_go(FwdArgs& a, hipStream_t st) {
   }
   {
     PackArgs p;
-    p.f16_scale = nullptr;
+    p.f16_scale = a.vscale;
     p.src = G.Vs;
     p.ld = G.ldv;
     p.dim = DV;

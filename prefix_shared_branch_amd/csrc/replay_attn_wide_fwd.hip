@@ -301,11 +301,17 @@ __global__ __launch_bounds__(64 * WideFwdCfg::NW, 1) void replay_fwd_wide(FwdArg
   const float lse = l > 0.0f ? (mu + fast_log2(l)) * kLn2 : -INFINITY;
   // lane holds dims 16 d + 4 q4 .. +3 of its row
   if (a.splits == 1) {
-    uint16_t* orow = a.O + (tok * G.Hq + hq) * C::DV + 4 * q4;
+    const int64_t off = (tok * G.Hq + hq) * C::DV + 4 * q4;
+    uint16_t* orow = a.O + off;
 #pragma unroll
     for (int d = 0; d < C::DT; ++d) {
-      const u32x2 v = {pack_bf16x2(o[d][0] * inv, o[d][1] * inv), pack_bf16x2(o[d][2] * inv, o[d][3] * inv)};
+      const f32x4 x = o[d] * inv;
+      const u32x2 v = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
       *reinterpret_cast<u32x2*>(orow + 16 * d) = v;
+      if (a.O_lo) {
+        const u32x2 r = {pack_bf16x2_residual(x[0], x[1], v[0]), pack_bf16x2_residual(x[2], x[3], v[1])};
+        *reinterpret_cast<u32x2*>(a.O_lo + off + 16 * d) = r;
+      }
     }
     if (q4 == 0) a.lse[(int64_t)hq * G.T + tok] = lse;
   } else {

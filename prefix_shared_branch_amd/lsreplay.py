@@ -56,17 +56,17 @@ def lib():
         L.ls_replay_attn_workspace_bytes.restype = ctypes.c_int
         L.ls_replay_attn_workspace_bytes.argtypes = [pdesc, i32, pi32, i32, ctypes.POINTER(sz)]
         L.ls_replay_attn_fwd.restype = ctypes.c_int
-        L.ls_replay_attn_fwd.argtypes = [vp, pdesc, vp, vp, i32, pi32, vp, vp, vp, vp, vp, vp, sz]
+        L.ls_replay_attn_fwd.argtypes = [vp, pdesc, vp, vp, i32, pi32, vp, vp, vp, vp, vp, vp, vp, sz]
         L.ls_replay_attn_bwd.restype = ctypes.c_int
         L.ls_replay_attn_bwd.argtypes = [vp, pdesc, vp, vp, i32, pi32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                         vp, sz]
+                                         vp, vp, sz]
         L.ls_replay_attn_block_workspace_bytes.restype = ctypes.c_int
         L.ls_replay_attn_block_workspace_bytes.argtypes = [pdesc, i32, i32, i32, ctypes.POINTER(sz)]
         L.ls_replay_attn_fwd_block.restype = ctypes.c_int
-        L.ls_replay_attn_fwd_block.argtypes = [vp, pdesc, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz]
+        L.ls_replay_attn_fwd_block.argtypes = [vp, pdesc, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz]
         L.ls_replay_attn_bwd_block.restype = ctypes.c_int
         L.ls_replay_attn_bwd_block.argtypes = [vp, pdesc, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                               vp, vp, sz]
+                                               vp, vp, vp, sz]
         L.ls_grpo_workspace_bytes.restype = ctypes.c_int
         L.ls_grpo_workspace_bytes.argtypes = [i64, i32, ctypes.POINTER(sz)]
         L.ls_grpo_token_loss.restype = ctypes.c_int
@@ -155,8 +155,17 @@ def _check_tensor(t, name, dtype, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def ls_replay_attn_fwd(q, ks, vs, kp, vp, cu_seqlens, scale=None, out=None, lse=None, workspace=None):
-    """Replay attention forward. Returns (O [T,Hq,Dv] bf16, LSE [Hq,T] fp32)."""
+def _check_o_lo(o_lo, shape):
+    import torch
+    if o_lo is not None:
+        _check_tensor(o_lo, "o_lo", torch.bfloat16, shape)
+        if not o_lo.is_contiguous():
+            raise ValueError("o_lo must be contiguous")
+
+
+def ls_replay_attn_fwd(q, ks, vs, kp, vp, cu_seqlens, scale=None, out=None, lse=None, workspace=None, o_lo=None):
+    """Replay attention forward. Returns (O [T,Hq,Dv] bf16, LSE [Hq,T] fp32); fills o_lo (bf16
+    [T,Hq,Dv], the rounding residual of O for the backward's Delta) when it is given."""
     import torch
     desc = make_desc(q, kp, vp, ks, vs, scale)
     T, Hq = q.shape[0], q.shape[1]
@@ -168,19 +177,21 @@ def ls_replay_attn_fwd(q, ks, vs, kp, vp, cu_seqlens, scale=None, out=None, lse=
     lse = torch.empty(Hq, T, dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensor(out, "out", torch.bfloat16, (T, Hq, desc.Dv))
     _check_tensor(lse, "lse", torch.float32, (Hq, T))
+    _check_o_lo(o_lo, (T, Hq, desc.Dv))
     cu, cup = _i32_array(cu_seqlens)
     nbytes = ls_replay_attn_workspace_bytes(desc, cu, 0)
     ws = _workspace(nbytes, q.device, workspace)
     _check("ls_replay_attn_fwd", lib().ls_replay_attn_fwd(
         _stream(), ctypes.byref(desc), _ptr(kp) if kp.numel() else None, _ptr(vp) if vp.numel() else None,
-        len(cu) - 1, cup, _ptr(q), _ptr(ks), _ptr(vs), _ptr(out), _ptr(lse), _ptr(ws), ws.numel()))
+        len(cu) - 1, cup, _ptr(q), _ptr(ks), _ptr(vs), _ptr(out), _ptr(lse), _ptr(o_lo), _ptr(ws), ws.numel()))
     return out, lse
 
 
 def ls_replay_attn_bwd(q, ks, vs, kp, vp, cu_seqlens, o, lse, do, dkp_accum=None, dvp_accum=None, scale=None,
-                       dq=None, dks=None, dvs=None, workspace=None):
+                       dq=None, dks=None, dvs=None, workspace=None, o_lo=None):
     """Replay attention backward. Adds into dkp_accum/dvp_accum (fp32) when given (exact
-    prompt-gradient mode); both None = response-only closure. Returns (dQ, dKs, dVs) bf16."""
+    prompt-gradient mode); both None = response-only closure. o_lo: the forward's residual of O,
+    or None. Returns (dQ, dKs, dVs) bf16."""
     import torch
     desc = make_desc(q, kp, vp, ks, vs, scale)
     T, Hq = q.shape[0], q.shape[1]
@@ -201,12 +212,13 @@ def ls_replay_attn_bwd(q, ks, vs, kp, vp, cu_seqlens, o, lse, do, dkp_accum=None
     dks = torch.empty(T, desc.Hkv, desc.Dqk, dtype=torch.bfloat16, device=q.device) if dks is None else dks
     dvs = torch.empty(T, desc.Hkv, desc.Dv, dtype=torch.bfloat16, device=q.device) if dvs is None else dvs
     cu, cup = _i32_array(cu_seqlens)
+    _check_o_lo(o_lo, (T, Hq, desc.Dv))
     nbytes = ls_replay_attn_workspace_bytes(desc, cu, 1 if dkp_accum is not None else 2)
     ws = _workspace(nbytes, q.device, workspace)
     _check("ls_replay_attn_bwd", lib().ls_replay_attn_bwd(
         _stream(), ctypes.byref(desc), _ptr(kp) if kp.numel() else None, _ptr(vp) if vp.numel() else None,
-        len(cu) - 1, cup, _ptr(q), _ptr(ks), _ptr(vs), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dks), _ptr(dvs),
-        _ptr(dkp_accum), _ptr(dvp_accum), _ptr(ws), ws.numel()))
+        len(cu) - 1, cup, _ptr(q), _ptr(ks), _ptr(vs), _ptr(o), _ptr(lse), _ptr(o_lo), _ptr(do), _ptr(dq), _ptr(dks),
+        _ptr(dvs), _ptr(dkp_accum), _ptr(dvp_accum), _ptr(ws), ws.numel()))
     return dq, dks, dvs
 
 
@@ -218,7 +230,7 @@ def ls_replay_attn_block_workspace_bytes(desc: AttnDesc, q0: int, nq: int, which
     return int(out.value)
 
 
-def ls_replay_attn_fwd_block(q, ks, vs, kp, vp, q0, scale=None, out=None, lse=None, workspace=None):
+def ls_replay_attn_fwd_block(q, ks, vs, kp, vp, q0, scale=None, out=None, lse=None, workspace=None, o_lo=None):
     """Forward of rows q0 .. q0+nq-1 of one response (q [nq,Hq,Dqk]; ks/vs hold the response's keys
     0 .. q0+nq-1). Returns (O [nq,Hq,Dv] bf16, LSE [Hq,nq] fp32)."""
     import torch
@@ -234,15 +246,16 @@ def ls_replay_attn_fwd_block(q, ks, vs, kp, vp, q0, scale=None, out=None, lse=No
     lse = torch.empty(Hq, nq, dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensor(out, "out", torch.bfloat16, (nq, Hq, desc.Dv))
     _check_tensor(lse, "lse", torch.float32, (Hq, nq))
+    _check_o_lo(o_lo, (nq, Hq, desc.Dv))
     ws = _workspace(ls_replay_attn_block_workspace_bytes(desc, q0, nq, 0), q.device, workspace)
     _check("ls_replay_attn_fwd_block", lib().ls_replay_attn_fwd_block(
         _stream(), ctypes.byref(desc), _ptr(kp) if kp.numel() else None, _ptr(vp) if vp.numel() else None,
-        int(q0), int(nq), _ptr(q), _ptr(ks), _ptr(vs), _ptr(out), _ptr(lse), _ptr(ws), ws.numel()))
+        int(q0), int(nq), _ptr(q), _ptr(ks), _ptr(vs), _ptr(out), _ptr(lse), _ptr(o_lo), _ptr(ws), ws.numel()))
     return out, lse
 
 
 def ls_replay_attn_bwd_block(q, ks, vs, kp, vp, q0, o, lse, do, dks_accum, dvs_accum, dkp_accum=None,
-                             dvp_accum=None, scale=None, dq=None, workspace=None):
+                             dvp_accum=None, scale=None, dq=None, workspace=None, o_lo=None):
     """Backward of one block: returns dQ [nq,Hq,Dqk] bf16 and ADDS the block's key gradients into
     dks_accum/dvs_accum (fp32 [q0+nq,Hkv,*]) and, in exact mode, into dkp_accum/dvp_accum."""
     import torch
@@ -263,13 +276,14 @@ def ls_replay_attn_bwd_block(q, ks, vs, kp, vp, q0, o, lse, do, dks_accum, dvs_a
     for n, t in (("q", q), ("o", o), ("do", do), ("dks_accum", dks_accum), ("dvs_accum", dvs_accum)):
         if not t.is_contiguous():
             raise ValueError(f"{n} must be contiguous")
+    _check_o_lo(o_lo, (nq, Hq, desc.Dv))
     dq = torch.empty(nq, Hq, desc.Dqk, dtype=torch.bfloat16, device=q.device) if dq is None else dq
     ws = _workspace(ls_replay_attn_block_workspace_bytes(desc, q0, nq, 1 if dkp_accum is not None else 2),
                     q.device, workspace)
     _check("ls_replay_attn_bwd_block", lib().ls_replay_attn_bwd_block(
         _stream(), ctypes.byref(desc), _ptr(kp) if kp.numel() else None, _ptr(vp) if vp.numel() else None,
-        int(q0), int(nq), _ptr(q), _ptr(ks), _ptr(vs), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dks_accum),
-        _ptr(dvs_accum), _ptr(dkp_accum), _ptr(dvp_accum), _ptr(ws), ws.numel()))
+        int(q0), int(nq), _ptr(q), _ptr(ks), _ptr(vs), _ptr(o), _ptr(lse), _ptr(o_lo), _ptr(do), _ptr(dq),
+        _ptr(dks_accum), _ptr(dvs_accum), _ptr(dkp_accum), _ptr(dvp_accum), _ptr(ws), ws.numel()))
     return dq
 
 

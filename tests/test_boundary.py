@@ -80,18 +80,18 @@ def test_seqlens_validation():
     assert rc == L.LS_OK and n > 0                                   # delta buffer
 
 
-def _fwd(d, cu, Kp=BAD, Vp=BAD, Q=BAD, Ks=BAD, Vs=BAD, O=BAD, lse=BAD, ws=BAD, nbytes=1 << 40):
+def _fwd(d, cu, Kp=BAD, Vp=BAD, Q=BAD, Ks=BAD, Vs=BAD, O=BAD, lse=BAD, O_lo=None, ws=BAD, nbytes=1 << 40):
     cu = np.asarray(cu, dtype=np.int32)
     return L.lib().ls_replay_attn_fwd(None, ctypes.byref(d), Kp, Vp, len(cu) - 1,
-                                      cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), Q, Ks, Vs, O, lse, ws,
+                                      cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), Q, Ks, Vs, O, lse, O_lo, ws,
                                       nbytes)
 
 
-def _bwd(d, cu, dKp=BAD, dVp=BAD, ws=BAD, nbytes=1 << 40, Q=BAD):
+def _bwd(d, cu, dKp=BAD, dVp=BAD, ws=BAD, nbytes=1 << 40, Q=BAD, O_lo=None):
     cu = np.asarray(cu, dtype=np.int32)
     return L.lib().ls_replay_attn_bwd(None, ctypes.byref(d), BAD, BAD, len(cu) - 1,
                                       cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), Q, BAD, BAD, BAD, BAD,
-                                      BAD, BAD, BAD, BAD, dKp, dVp, ws, nbytes)
+                                      O_lo, BAD, BAD, BAD, BAD, dKp, dVp, ws, nbytes)
 
 
 def test_fwd_bwd_pointer_and_workspace_validation():
@@ -108,6 +108,9 @@ def test_fwd_bwd_pointer_and_workspace_validation():
     assert _bwd(d, [0, 10], dVp=None) == L.LS_ERR_INVALID_ARG
     assert _bwd(d, [0, 10], dKp=None, dVp=None, Q=None) == L.LS_ERR_INVALID_ARG
     assert _bwd(d, [0, 10], nbytes=0) == L.LS_ERR_WORKSPACE
+    # the optional rounding residual of O: NULL is accepted, a misaligned pointer is not
+    assert _fwd(d, [0, 10], O_lo=ctypes.c_void_p(0x1008)) == L.LS_ERR_INVALID_ARG
+    assert _bwd(d, [0, 10], O_lo=ctypes.c_void_p(0x1008)) == L.LS_ERR_INVALID_ARG
 
 
 def _block_ws(d, q0, nq, which=0):
@@ -116,12 +119,13 @@ def _block_ws(d, q0, nq, which=0):
 
 
 def _fwd_block(d, q0, nq, Q=BAD, Ks=BAD, ws=BAD, nbytes=1 << 40):
-    return L.lib().ls_replay_attn_fwd_block(None, ctypes.byref(d), BAD, BAD, q0, nq, Q, Ks, BAD, BAD, BAD, ws, nbytes)
+    return L.lib().ls_replay_attn_fwd_block(None, ctypes.byref(d), BAD, BAD, q0, nq, Q, Ks, BAD, BAD, BAD, None, ws,
+                                            nbytes)
 
 
 def _bwd_block(d, q0, nq, dKs=BAD, dVs=BAD, dKp=BAD, dVp=BAD, ws=BAD, nbytes=1 << 40):
-    return L.lib().ls_replay_attn_bwd_block(None, ctypes.byref(d), BAD, BAD, q0, nq, BAD, BAD, BAD, BAD, BAD, BAD,
-                                            BAD, dKs, dVs, dKp, dVp, ws, nbytes)
+    return L.lib().ls_replay_attn_bwd_block(None, ctypes.byref(d), BAD, BAD, q0, nq, BAD, BAD, BAD, BAD, BAD, None,
+                                            BAD, BAD, dKs, dVs, dKp, dVp, ws, nbytes)
 
 
 def test_block_validation():

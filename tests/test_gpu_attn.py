@@ -18,9 +18,10 @@ pytestmark = pytest.mark.gpu
 class Case:
     """Seeded inputs of one config with explicit response lengths (packed)."""
 
-    def __init__(self, cfg, lengths):
+    def __init__(self, cfg, lengths, residual=True):
         import torch
         self.cfg = cfg
+        self.residual = residual  # pass the forward's rounding residual of O to the backward
         self.lengths = np.asarray(lengths, dtype=np.int32)
         self.cu = inputs.cu_seqlens(self.lengths)
         T = int(self.cu[-1])
@@ -40,15 +41,21 @@ class Case:
         self.torch = torch
 
     def fwd(self, cu=None, sl=slice(None)):
+        """Forward; with residual, O carries its rounding residual as the attribute o_lo."""
         from prefix_shared_branch_amd import lsreplay as L
         cu = self.cu if cu is None else cu
-        return L.ls_replay_attn_fwd(self.q[sl], self.ks[sl], self.vs[sl], self.kp, self.vp, cu, self.cfg.scale)
+        q = self.q[sl]
+        lo = self.torch.empty(q.shape[0], self.cfg.Hq, self.cfg.Dv, dtype=self.torch.bfloat16,
+                              device="cuda") if self.residual else None
+        o, lse = L.ls_replay_attn_fwd(q, self.ks[sl], self.vs[sl], self.kp, self.vp, cu, self.cfg.scale, o_lo=lo)
+        o.o_lo = lo
+        return o, lse
 
     def bwd(self, o, lse, dkp=None, dvp=None, cu=None, sl=slice(None)):
         from prefix_shared_branch_amd import lsreplay as L
         cu = self.cu if cu is None else cu
         return L.ls_replay_attn_bwd(self.q[sl], self.ks[sl], self.vs[sl], self.kp, self.vp, cu, o, lse, self.do[sl],
-                                    dkp, dvp, self.cfg.scale)
+                                    dkp, dvp, self.cfg.scale, o_lo=getattr(o, "o_lo", None))
 
     def accums(self):
         t = self.torch
@@ -234,3 +241,34 @@ def test_backward_operand_scaling(do_scale, q_scale):
             assert not bool(x.any()), "a zero dO must give exactly zero gradients"
         return
     _check_all(dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp), ref, literal_abs=False)
+
+
+def test_output_rounding_residual():
+    """O_lo holds the fp32 output's rounding residual: at most half a bf16 step of O, and O + O_lo
+    is closer to the fp64 output than O alone (long prompt: the fp32 sum is far below a bf16 step)."""
+    cfg = inputs.replace(inputs.CONFIGS["tiny"], Hq=8, Hkv=2, Dqk=128, Dv=128, P=5000, seed=37)
+    case = Case(cfg, [70, 130])
+    o, _ = case.fwd()
+    case.torch.cuda.synchronize()
+    hi, lo = host_f64(o), host_f64(o.o_lo)
+    ref = case.oracle(accumulate=False)["O"]
+    # one bf16 step at |O| in [2^e, 2^(e+1)) is 2^(e - 7)
+    step = np.exp2(np.floor(np.log2(np.maximum(np.abs(hi), 1e-30))) - 7)
+    assert np.all(np.abs(lo) <= step / 2 * (1 + 2 ** -7))
+    for h in range(cfg.Hq):
+        e_hi = np.linalg.norm(hi[:, h] - ref[:, h])
+        e_sum = np.linalg.norm(hi[:, h] + lo[:, h] - ref[:, h])
+        assert e_sum <= 0.5 * e_hi, (h, e_sum, e_hi)
+
+
+def test_backward_without_output_residual():
+    """O_lo is optional: Delta from the bf16 O alone keeps the bars at a prompt of a thousand keys."""
+    cfg = inputs.replace(inputs.CONFIGS["tiny"], P=1000, seed=38)
+    case = Case(cfg, [40, 200], residual=False)
+    t = case.torch
+    dkp, dvp = case.accums()
+    o, lse = case.fwd()
+    assert o.o_lo is None
+    dq, dks, dvs = case.bwd(o, lse, dkp, dvp)
+    t.cuda.synchronize()
+    _check_all(dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp), case.oracle())

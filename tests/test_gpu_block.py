@@ -27,9 +27,10 @@ def _blockwise(case, bounds, exact=True):
     outs = {"O": [], "LSE": [], "dQ": []}
     for q0, q1 in zip(bounds[:-1], bounds[1:]):
         q, ks, vs, do = case.q[q0:q1], case.ks[:q1], case.vs[:q1], case.do[q0:q1]
-        o, lse = L.ls_replay_attn_fwd_block(q, ks, vs, case.kp, case.vp, q0, cfg.scale)
+        lo = t.empty(q1 - q0, cfg.Hq, cfg.Dv, dtype=t.bfloat16, device="cuda")
+        o, lse = L.ls_replay_attn_fwd_block(q, ks, vs, case.kp, case.vp, q0, cfg.scale, o_lo=lo)
         dq = L.ls_replay_attn_bwd_block(q, ks, vs, case.kp, case.vp, q0, o, lse, do, dks[:q1], dvs[:q1], dkp, dvp,
-                                        cfg.scale)
+                                        cfg.scale, o_lo=lo)
         outs["O"].append(o)
         outs["LSE"].append(lse)
         outs["dQ"].append(dq)

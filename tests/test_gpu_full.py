@@ -46,9 +46,10 @@ class Prompt:
         d = {n: dev_bf16(b) for n, b in bits.items()}
         dkp = t.zeros(cfg.P, cfg.Hkv, cfg.Dqk, dtype=t.float32, device="cuda") if exact else None
         dvp = t.zeros(cfg.P, cfg.Hkv, cfg.Dv, dtype=t.float32, device="cuda") if exact else None
-        o, lse = L.ls_replay_attn_fwd(d["q"], d["ks"], d["vs"], self.kp, self.vp, [0, r], cfg.scale)
+        lo = t.empty(r, cfg.Hq, cfg.Dv, dtype=t.bfloat16, device="cuda")
+        o, lse = L.ls_replay_attn_fwd(d["q"], d["ks"], d["vs"], self.kp, self.vp, [0, r], cfg.scale, o_lo=lo)
         dq, dks, dvs = L.ls_replay_attn_bwd(d["q"], d["ks"], d["vs"], self.kp, self.vp, [0, r], o, lse, d["do"],
-                                            dkp, dvp, cfg.scale)
+                                            dkp, dvp, cfg.scale, o_lo=lo)
         t.cuda.synchronize()
         return bits, dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp)
 

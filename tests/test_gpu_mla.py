@@ -112,8 +112,9 @@ def test_mla_full_prompt_sampled_rows_and_column_sums():
     vp, vs = kp[:, :, :cfg.Dv], ks[:, :, :cfg.Dv]
     dkp = torch.zeros(cfg.P, 1, cfg.Dqk, dtype=torch.float32, device="cuda")
     dvp = torch.zeros(cfg.P, 1, cfg.Dv, dtype=torch.float32, device="cuda")
-    o, lse = L.ls_replay_attn_fwd(q, ks, vs, kp, vp, [0, r], cfg.scale)
-    dq, dks, dvs = L.ls_replay_attn_bwd(q, ks, vs, kp, vp, [0, r], o, lse, do, dkp, dvp, cfg.scale)
+    lo = torch.empty(r, cfg.Hq, cfg.Dv, dtype=torch.bfloat16, device="cuda")
+    o, lse = L.ls_replay_attn_fwd(q, ks, vs, kp, vp, [0, r], cfg.scale, o_lo=lo)
+    dq, dks, dvs = L.ls_replay_attn_bwd(q, ks, vs, kp, vp, [0, r], o, lse, do, dkp, dvp, cfg.scale, o_lo=lo)
     torch.cuda.synchronize()
     # the oracle at full P for two of the 16 query heads (heads share the one latent kv head)
     hs = [0, cfg.Hq - 1]

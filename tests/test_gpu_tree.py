@@ -51,9 +51,10 @@ def test_two_level_prefix_tree(D, P, nb, children):
     got = {}
     # the branch, once, against the prompt
     sb = slice(0, nb)
-    ob, lb = L.ls_replay_attn_fwd_block(dev["q"][sb], slot_k[:nb], slot_v[:nb], kp, vp, 0, cfg.scale)
+    lo = torch.empty(max(nb, rmax), cfg.Hq, D, dtype=torch.bfloat16, device="cuda")   # O's rounding residual
+    ob, lb = L.ls_replay_attn_fwd_block(dev["q"][sb], slot_k[:nb], slot_v[:nb], kp, vp, 0, cfg.scale, o_lo=lo[:nb])
     got["dQ_B"] = L.ls_replay_attn_bwd_block(dev["q"][sb], slot_k[:nb], slot_v[:nb], kp, vp, 0, ob, lb, dev["do"][sb],
-                                             acc_k[:nb], acc_v[:nb], dkp, dvp, cfg.scale)
+                                             acc_k[:nb], acc_v[:nb], dkp, dvp, cfg.scale, o_lo=lo[:nb])
     got["O_B"], got["LSE_B"] = ob, lb
     for c, r in enumerate(children):
         s = slice(int(cu[1 + c]), int(cu[2 + c]))
@@ -61,9 +62,11 @@ def test_two_level_prefix_tree(D, P, nb, children):
         slot_v[nb:nb + r] = dev["v"][s]
         acc_k[nb:].zero_()
         acc_v[nb:].zero_()
-        o, lse = L.ls_replay_attn_fwd_block(dev["q"][s], slot_k[:nb + r], slot_v[:nb + r], kp, vp, nb, cfg.scale)
+        o, lse = L.ls_replay_attn_fwd_block(dev["q"][s], slot_k[:nb + r], slot_v[:nb + r], kp, vp, nb, cfg.scale,
+                                            o_lo=lo[:r])
         dq = L.ls_replay_attn_bwd_block(dev["q"][s], slot_k[:nb + r], slot_v[:nb + r], kp, vp, nb, o, lse,
-                                        dev["do"][s], acc_k[:nb + r], acc_v[:nb + r], dkp, dvp, cfg.scale)
+                                        dev["do"][s], acc_k[:nb + r], acc_v[:nb + r], dkp, dvp, cfg.scale,
+                                        o_lo=lo[:r])
         got[f"O_{c}"], got[f"LSE_{c}"], got[f"dQ_{c}"] = o, lse, dq
         got[f"dK_{c}"], got[f"dV_{c}"] = acc_k[nb:nb + r].clone(), acc_v[nb:nb + r].clone()
     torch.cuda.synchronize()
