@@ -262,10 +262,10 @@ def recorded_traffic(kernel, workload):
             + rec["write_kib_per_launch"] * 1024 * rec["write_scale"])
 
 
-def copy_calibration():
-    """A plain device copy of known size, for reading FETCH_SIZE / WRITE_SIZE against known bytes."""
+def device_copy_GBps(n=1 << 30):
+    """Bytes read + written per second by a plain device-to-device copy of n bytes (one warm-up, three
+    timed): the HBM rate a simple streaming kernel reaches on this part, beside the 8 TB/s nameplate."""
     import torch
-    n = 1 << 30
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     e0 = torch.cuda.Event(enable_timing=True)
@@ -276,7 +276,13 @@ def copy_calibration():
         dst.copy_(src)
     e1.record()
     torch.cuda.synchronize()
-    gbps = 3 * 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    return 3 * 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def copy_calibration():
+    """A plain device copy of known size, for reading FETCH_SIZE / WRITE_SIZE against known bytes."""
+    n = 1 << 30
+    gbps = device_copy_GBps(n)
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 4, "copy_GBps": gbps}), flush=True)
 
 
@@ -343,6 +349,7 @@ def main():
     # LM head fused with the loss (the step to the left of the loss) on the first response: hidden
     # size d = Hq * Dqk, logits = H W^T chunk by chunk; 3 GEMMs of 2 R V d flops each
     lm = lmhead_measure(cfg, wl)
+    copy_gbps = device_copy_GBps()
 
     # dominant kernel: the dK/dV prompt kernel, timed by the library's kernel timer (HIP events on
     # the launch stream around every launch in the timed region)
@@ -381,6 +388,8 @@ def main():
             "fwd_alg_TFLOPs": fwd_alg / (t_fwd * 1e-3) / 1e12,
             "loss_GBps": loss_bytes / (t_loss * 1e-3) / 1e9,
             "loss_frac_hbm": loss_bytes / (t_loss * 1e-3) / PEAK_HBM,
+            "copy_GBps": copy_gbps,
+            "loss_frac_copy": loss_bytes / (t_loss * 1e-3) / 1e9 / copy_gbps,
             "scoring_loss_ms_per_group": t_score,
             "scoring_loss_GBps": score_bytes / (t_score * 1e-3) / 1e9,
             "lmhead": lm,

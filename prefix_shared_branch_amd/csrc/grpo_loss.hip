@@ -1,6 +1,6 @@
 // Fused clipped-GRPO token objective (LongStraw study notes, §1-1, L_policy equation).
 //
-// One workgroup per token row. The bf16 logits row is read from HBM exactly once into
+// A workgroup handles one token row at a time. The bf16 logits row is read from HBM exactly once into
 // VGPRs (16-byte loads, consecutive threads on consecutive 16-byte chunks); the row max
 // and the sum of exponentials are wave reductions combined through LDS; the dlogits row is
 // then produced from the same registers and written once. HBM traffic per token is the
@@ -66,72 +66,111 @@ __device__ __forceinline__ float row_scalar(const GrpoArgs& a, int64_t row, floa
 // Rows are read through a buffer resource (one VGPR offset per thread, the chunk column in
 // the SGPR offset) so no per-chunk 64-bit addresses stay live; chunks past the row end are
 // masked to -inf after the load and never stored.
+// A row fills most of a CU's registers at the large vocabularies, so one workgroup per CU loops
+// over rows (row = blockIdx.x, + gridDim.x, ...). In the gradient pass the registers of chunk j
+// are reloaded with chunk j of the next row as soon as chunk j's dlogits are stored: the next
+// row streams in while this row's output is formed and written, and the stores drain while the
+// next row's max and sum are taken.
 template <int NT, int NCH>
 __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
   __shared__ float red[NT / 64];
-  __shared__ float xy_s;
-  const int64_t row = blockIdx.x;
   const int nch = a.V >> 3;
-  const int y = a.targets[row];
-  const bool y_ok = (y >= 0) && (y < a.V);
-  const __amdgpu_buffer_rsrc_t src =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(a.logits + row * (int64_t)a.V), 0, a.V * 2, kBufferWord3);
   const int voff = threadIdx.x * 16;
+  const int64_t stride = gridDim.x;
+  int64_t row = blockIdx.x;
+  if (row >= a.T) return;
+  auto row_src = [&](int64_t r) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(a.logits + r * (int64_t)a.V), 0, a.V * 2, kBufferWord3);
+  };
 
   u32x4 v[NCH];
+  {
+    const __amdgpu_buffer_rsrc_t src = row_src(row);
 #pragma unroll
-  for (int j = 0; j < NCH; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(src, voff, j * NT * 16, kSlc);
-#pragma unroll
-  for (int j = 0; j < NCH; ++j)
-    if ((int)threadIdx.x + j * NT >= nch) v[j] = u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
-  if (threadIdx.x == 0) xy_s = y_ok ? bf16_to_f32(a.logits[row * (int64_t)a.V + y]) : 0.0f;
-
-  float m = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    m = fmaxf(m, fmaxf(fmaxf(bf16_lo(v[j].x), bf16_hi(v[j].x)), fmaxf(bf16_lo(v[j].y), bf16_hi(v[j].y))));
-    m = fmaxf(m, fmaxf(fmaxf(bf16_lo(v[j].z), bf16_hi(v[j].z)), fmaxf(bf16_lo(v[j].w), bf16_hi(v[j].w))));
+    for (int j = 0; j < NCH; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(src, voff, j * NT * 16, kSlc);
   }
-  m = block_reduce<NT>(m, red, true);
-  // keep only the packed row live across the passes (re-derive floats on use, no spills)
+  for (;;) {
+    // chunk offsets and chunk-validity masks are formed from a value the compiler cannot see
+    // through, so they are materialised at their use instead of being hoisted out of the row loop
+    // (where 19 lane masks and offsets would be live SGPRs across it)
+    int zoff = 0;
+    asm volatile("" : "+s"(zoff));
+    const int64_t next = row + stride;
+    const bool more = next < a.T;  // uniform
+    const int y = a.targets[row];
+    const bool y_ok = (y >= 0) && (y < a.V);
+    const float xy = y_ok ? bf16_to_f32(a.logits[row * (int64_t)a.V + y]) : 0.0f;
 #pragma unroll
-  for (int j = 0; j < NCH; ++j) asm volatile("" : "+v"(v[j]));
-  const float mb = m * kLog2e;
-  float s = 0.0f;
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      s += fast_exp2(__builtin_fmaf(bf16_lo(v[j][q]), kLog2e, -mb));
-      s += fast_exp2(__builtin_fmaf(bf16_hi(v[j][q]), kLog2e, -mb));
-    }
-  }
-  s = block_reduce<NT>(s, red, false);
-  const float lse = m + fast_log2(s) * kLn2;
-  const float c = row_scalar(a, row, xy_s, y_ok, lse);
-  if (a.dlogits == nullptr) return;  // scoring only: no gradient pass
-  const float lb = lse * kLog2e;
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) asm volatile("" : "+v"(v[j]));
+    for (int j = 0; j < NCH; ++j)
+      if ((int)threadIdx.x + j * NT + zoff >= nch) v[j] = u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
 
-  // Stores are global (FLAT) stores: the compiler protects their data registers from the
-  // next VALU write, which it does not do for buffer stores with an SGPR offset.
-  char* dst = reinterpret_cast<char*>(a.dlogits + row * (int64_t)a.V);
+    float m = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int cj = (int)threadIdx.x + j * NT;
-    const int e0 = cj * 8;
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = e0 + 2 * q;
-      float p0 = fast_exp2(__builtin_fmaf(bf16_lo(v[j][q]), kLog2e, -lb));
-      float p1 = fast_exp2(__builtin_fmaf(bf16_hi(v[j][q]), kLog2e, -lb));
-      p0 -= (e == y) ? 1.0f : 0.0f;
-      p1 -= (e + 1 == y) ? 1.0f : 0.0f;
-      o[q] = pack_bf16x2(c * p0, c * p1);
+    for (int j = 0; j < NCH; ++j) {
+      m = fmaxf(m, fmaxf(fmaxf(bf16_lo(v[j].x), bf16_hi(v[j].x)), fmaxf(bf16_lo(v[j].y), bf16_hi(v[j].y))));
+      m = fmaxf(m, fmaxf(fmaxf(bf16_lo(v[j].z), bf16_hi(v[j].z)), fmaxf(bf16_lo(v[j].w), bf16_hi(v[j].w))));
     }
-    if (cj < nch) __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst + voff + j * NT * 16));
+    m = block_reduce<NT>(m, red, true);
+    // keep only the packed row live across the passes (re-derive floats on use, no spills)
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) asm volatile("" : "+v"(v[j]));
+    const float mb = m * kLog2e;
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s += fast_exp2(__builtin_fmaf(bf16_lo(v[j][q]), kLog2e, -mb));
+        s += fast_exp2(__builtin_fmaf(bf16_hi(v[j][q]), kLog2e, -mb));
+      }
+    }
+    s = block_reduce<NT>(s, red, false);
+    const float lse = m + fast_log2(s) * kLn2;
+    const float c = row_scalar(a, row, xy, y_ok, lse);
+    // after the last row the reloads go through an empty resource: no memory access, zeros returned
+    const __amdgpu_buffer_rsrc_t nsrc =
+        more ? row_src(next) : __builtin_amdgcn_make_buffer_rsrc((void*)a.logits, 0, 0, kBufferWord3);
+    if (a.dlogits != nullptr) {
+      const float lb = lse * kLog2e;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) asm volatile("" : "+v"(v[j]));
+      const int yc = y_ok ? (y >> 3) : -1;  // the chunk holding the target (one lane of the row)
+      // Stores are global (FLAT) stores: the compiler protects their data registers from the
+      // next VALU write, which it does not do for buffer stores with an SGPR offset.
+      char* dst = reinterpret_cast<char*>(a.dlogits + row * (int64_t)a.V);
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int cj = (int)threadIdx.x + j * NT + zoff;
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float p0 = fast_exp2(__builtin_fmaf(bf16_lo(v[j][q]), kLog2e, -lb));
+          const float p1 = fast_exp2(__builtin_fmaf(bf16_hi(v[j][q]), kLog2e, -lb));
+          o[q] = pack_bf16x2(c * p0, c * p1);
+        }
+        if (cj == yc) {
+          // the one-hot term (one lane of the row): the target's element becomes c (p_y - 1), p_y
+          // formed from the same logit value as the other elements
+          const float py = fast_exp2(__builtin_fmaf(xy, kLog2e, -lb)) - 1.0f;
+          const uint32_t t = pack_bf16x2(c * py, 0.0f) & 0xffffu;
+          const int qy = (y & 7) >> 1;
+          const uint32_t keep = (y & 1) ? 0x0000ffffu : 0xffff0000u;
+          const uint32_t ins = (y & 1) ? (t << 16) : t;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = (q == qy) ? ((o[q] & keep) | ins) : o[q];
+        }
+        if (cj < nch) __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst + voff + j * NT * 16));
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(nsrc, voff, zoff + j * NT * 16, kSlc);
+        // chunk by chunk: the reload of chunk j is not hoisted above the output of chunks < j,
+        // which would keep two rows' chunks live at once
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if (more) {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(nsrc, voff, zoff + j * NT * 16, kSlc);
+    }
+    if (!more) break;
+    row = next;
   }
 }
 
@@ -174,9 +213,15 @@ __global__ __launch_bounds__(256) void grpo_sum(const float* row_loss, int64_t T
   if (threadIdx.x == 0) *loss_accum = (float)((double)*loss_accum + part[0]);
 }
 
+// Workgroups of the row loop: one per CU at 1024 threads (a row fills most of a CU's registers),
+// four per CU at 256 threads.
+constexpr int64_t kLossCUs = 256;
+
 template <int NT, int NCH>
 hipError_t go_vec(const GrpoArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((grpo_rows_vec<NT, NCH>), dim3((unsigned)a.T), dim3(NT), 0, st, a);
+  const int64_t wgs = kLossCUs * (NT == 1024 ? 1 : 4);
+  const int64_t grid = a.T < wgs ? a.T : wgs;
+  hipLaunchKernelGGL((grpo_rows_vec<NT, NCH>), dim3((unsigned)grid), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 

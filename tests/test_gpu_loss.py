@@ -154,3 +154,23 @@ def test_loss_scoring_only_matches_full_pass_and_oracle(cfgname, lengths, V):
     assert np.array_equal(logp_s, logp_f) and np.array_equal(clip_s, clip_f)
     logp_ref = grpo.token_logp(d["x"], d["y"])
     assert np.max(np.abs(logp_s - logp_ref)) <= 1e-4
+
+
+@pytest.mark.parametrize("cfgname,lengths", [("mid", [170, 120]), ("tiny_clip", [700, 500])])
+def test_loss_rows_looped_per_workgroup(cfgname, lengths):
+    """More rows than the row loop has workgroups (256 at the full vocabulary, 1024 below it), so a
+    workgroup streams several rows, reloading each chunk's registers with the next row's chunk as its
+    dlogits are written. Full pass and scoring pass against the oracle; per-response calls (each
+    starting the loop afresh) give the same dlogits and log-probs bit for bit."""
+    import torch
+    d = _setup(inputs.CONFIGS[cfgname], lengths=lengths)
+    G = d["G"]
+    got = _run(d, 0, G)
+    _compare(d, 0, G, got)
+    _, logp_s, clip_s = _run_scoring(d, 0, G)
+    assert np.array_equal(logp_s, got[2]) and np.array_equal(clip_s, got[3])
+    cu = np.concatenate([[0], np.cumsum(d["R"])])
+    for i in range(G):
+        _, dl_i, logp_i, _ = _run(d, i, 1)
+        assert torch.equal(dl_i, got[1][cu[i]:cu[i + 1]])
+        assert np.array_equal(logp_i, got[2][cu[i]:cu[i + 1]])
