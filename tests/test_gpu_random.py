@@ -47,3 +47,28 @@ def test_random_case(seed):
         got = dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp)
     # with a short or empty prompt, gradients are of order one: the relative bars apply
     _check_all(got, case.oracle(accumulate=exact), literal_abs=P >= 1000)
+
+
+def _draw_blocks(seed):
+    g = np.random.default_rng(seed)
+    shape = SHAPES[g.integers(len(SHAPES))]
+    P = int(g.choice([0, 1, 63, 65, 1000, 2049]))
+    R = int(g.integers(1, 401))
+    nb = int(g.integers(1, 5))
+    cuts = sorted({int(c) for c in g.integers(1, R, size=nb - 1)}) if R > 1 else []
+    return shape, P, R, [0, *cuts, R]
+
+
+@pytest.mark.parametrize("seed", list(range(950, 962)))
+def test_random_blocks(seed):
+    """One response replayed in randomly cut blocks against the unblocked oracle."""
+    from tests.test_gpu_block import _blockwise, _check
+    shape, P, R, bounds = _draw_blocks(seed)
+    if shape[0] == "mla":
+        cfg = inputs.replace(inputs.CONFIGS["mla"], P=P, seed=seed)
+    else:
+        D, Hq, Hkv = shape
+        cfg = inputs.replace(inputs.CONFIGS["tiny"], Hq=Hq, Hkv=Hkv, Dqk=D, Dv=D, P=P, seed=seed)
+    case = Case(cfg, [R])
+    exact = P > 0
+    _check(_blockwise(case, bounds, exact), case.oracle(accumulate=exact), exact, literal_abs=P >= 1000)
