@@ -180,7 +180,8 @@ int ls_grpo_workspace_bytes(int64_t T, int32_t V, size_t* bytes);
  *   A_i = (r_i - mean(r)) / (std(r) + 1e-6)  (population std over the G rewards; the
  *   pages say only that the advantage is built from the group rewards).
  * This call handles responses first .. first+count-1, whose rows are packed in `logits`.
- *  V         vocabulary size, 1..196608 (larger: LS_ERR_UNSUPPORTED).
+ *  V         vocabulary size, 1..2^24 (larger: LS_ERR_UNSUPPORTED). Rows of up to 196608 entries
+ *            (V % 8 == 0, 16-byte aligned) are read once; longer rows are read twice.
  *  G, R, rewards  group size and host arrays [G] of all response lengths (each >= 1) and
  *            rewards (finite); A and 1/(G R_i) are formed on the host in float64.
  *  eps       clip range, 0 < eps < 1.
@@ -217,7 +218,7 @@ int ls_grpo_lmhead_workspace_bytes(int64_t T, int32_t V, int32_t d, size_t* byte
  *   dH = dlogits W (bf16, overwritten)  and  dW += dlogits^T H (fp32, added in place).
  * The GEMMs run on rocBLAS (atomics disabled, run-to-run identical), whose handle the library
  * creates per device on first use; this entry point therefore allocates on its first call.
- *  V, d      vocabulary size (8 .. 196608, a multiple of 8) and hidden size (a multiple of 8);
+ *  V, d      vocabulary size (8 .. 2^24, a multiple of 8) and hidden size (a multiple of 8);
  *            V * d < 2^31. Other values: LS_ERR_UNSUPPORTED.
  *  G, R, rewards, eps, first, count  as for ls_grpo_token_loss.
  *  H         device bf16 [T, d] hidden states of the selected responses' tokens, packed.

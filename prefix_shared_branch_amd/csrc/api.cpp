@@ -12,7 +12,7 @@
 namespace {
 
 using lsr::kMaxResp;
-constexpr int32_t kMaxVocab = 196608;  // largest row the loss kernel holds in registers
+constexpr int32_t kMaxVocab = 1 << 24;  // rows above 196608 stream twice (32-bit element offsets)
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

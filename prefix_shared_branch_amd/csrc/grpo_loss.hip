@@ -174,6 +174,69 @@ __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
   }
 }
 
+// Rows too long for registers (V > 196608, V % 8 == 0, 16-byte aligned): two passes over the row.
+// The first keeps a per-thread running max and sum of exponentials (the sum rescaled whenever the
+// max moves) and combines them over the workgroup; the second forms dlogits. The row is read twice
+// and written once.
+template <int NT>
+__global__ __launch_bounds__(NT) void grpo_rows_stream(GrpoArgs a) {
+  __shared__ float red[NT / 64];
+  const int64_t row = blockIdx.x;
+  const int nch = a.V >> 3;
+  const u32x4* x = reinterpret_cast<const u32x4*>(a.logits + row * (int64_t)a.V);
+  const int y = a.targets[row];
+  const bool y_ok = (y >= 0) && (y < a.V);
+  float m = -INFINITY, s = 0.0f;
+  for (int cj = threadIdx.x; cj < nch; cj += NT) {
+    const u32x4 v = x[cj];
+    float cm = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cm = fmaxf(cm, fmaxf(bf16_lo(v[q]), bf16_hi(v[q])));
+    if (cm > m) {
+      s = (m == -INFINITY) ? 0.0f : s * fast_exp2((m - cm) * kLog2e);
+      m = cm;
+    }
+    if (m != -INFINITY) {  // while every value so far is -inf the sum stays 0
+      const float mb = m * kLog2e;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s += fast_exp2(__builtin_fmaf(bf16_lo(v[q]), kLog2e, -mb));
+        s += fast_exp2(__builtin_fmaf(bf16_hi(v[q]), kLog2e, -mb));
+      }
+    }
+  }
+  const float M = block_reduce<NT>(m, red, true);
+  const float sl = (m == -INFINITY) ? 0.0f : s * fast_exp2((m - M) * kLog2e);
+  const float S = block_reduce<NT>(sl, red, false);
+  const float lse = M + fast_log2(S) * kLn2;
+  const float xy = y_ok ? bf16_to_f32(a.logits[row * (int64_t)a.V + y]) : 0.0f;
+  const float c = row_scalar(a, row, xy, y_ok, lse);
+  if (a.dlogits == nullptr) return;  // scoring only: no gradient pass
+  const float lb = lse * kLog2e;
+  const int yc = y_ok ? (y >> 3) : -1;
+  u32x4* d = reinterpret_cast<u32x4*>(a.dlogits + row * (int64_t)a.V);
+  for (int cj = threadIdx.x; cj < nch; cj += NT) {
+    const u32x4 v = x[cj];
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float p0 = fast_exp2(__builtin_fmaf(bf16_lo(v[q]), kLog2e, -lb));
+      const float p1 = fast_exp2(__builtin_fmaf(bf16_hi(v[q]), kLog2e, -lb));
+      o[q] = pack_bf16x2(c * p0, c * p1);
+    }
+    if (cj == yc) {  // the one-hot term, as in grpo_rows_vec
+      const float py = fast_exp2(__builtin_fmaf(xy, kLog2e, -lb)) - 1.0f;
+      const uint32_t t = pack_bf16x2(c * py, 0.0f) & 0xffffu;
+      const int qy = (y & 7) >> 1;
+      const uint32_t keep = (y & 1) ? 0x0000ffffu : 0xffff0000u;
+      const uint32_t ins = (y & 1) ? (t << 16) : t;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = (q == qy) ? ((o[q] & keep) | ins) : o[q];
+    }
+    __builtin_nontemporal_store(o, d + cj);
+  }
+}
+
 // Element-wise path for any V / alignment: three passes over the row (L2-resident).
 __global__ __launch_bounds__(256) void grpo_rows_scalar(GrpoArgs a) {
   constexpr int NT = 256;
@@ -243,7 +306,11 @@ hipError_t launch_grpo(const GrpoArgs& a, bool vec, hipStream_t st) {
     else if (nch <= 1024 * 12) e = go_vec<1024, 12>(a, st);
     else if (nch <= 1024 * 16) e = go_vec<1024, 16>(a, st);
     else if (nch <= 1024 * 19) e = go_vec<1024, 19>(a, st);
-    else e = go_vec<1024, 24>(a, st);  // V <= 196608 (checked by the host API)
+    else if (nch <= 1024 * 24) e = go_vec<1024, 24>(a, st);
+    else {
+      hipLaunchKernelGGL((grpo_rows_stream<1024>), dim3((unsigned)a.T), dim3(1024), 0, st, a);
+      e = hipGetLastError();
+    }
   } else {
     hipLaunchKernelGGL(grpo_rows_scalar, dim3((unsigned)a.T), dim3(256), 0, st, a);
     e = hipGetLastError();

@@ -25,7 +25,7 @@
 namespace {
 
 constexpr int64_t kLmChunk = 2048;        // tokens per chunk
-constexpr int32_t kLmMaxVocab = 196608;   // the loss kernel's row limit
+constexpr int32_t kLmMaxVocab = 1 << 24;  // the loss kernel's row limit
 constexpr int kMaxDevices = 64;
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }

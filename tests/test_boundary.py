@@ -158,7 +158,7 @@ def _loss(V=4096, G=2, R=(3, 4), rewards=(0.0, 1.0), eps=0.2, first=0, count=2, 
 
 def test_loss_validation():
     assert _loss(V=0) == L.LS_ERR_INVALID_ARG
-    assert _loss(V=200000) == L.LS_ERR_UNSUPPORTED
+    assert _loss(V=(1 << 24) + 8) == L.LS_ERR_UNSUPPORTED           # beyond 32-bit element offsets
     assert _loss(eps=0.0) == L.LS_ERR_INVALID_ARG
     assert _loss(eps=1.0) == L.LS_ERR_INVALID_ARG
     assert _loss(eps=float("nan")) == L.LS_ERR_INVALID_ARG
@@ -234,7 +234,7 @@ def test_lmhead_validation():
     assert L.lib().ls_grpo_lmhead_workspace_bytes(-1, 4096, 256, ctypes.byref(n)) == L.LS_ERR_INVALID_ARG
     assert _lm(V=4100) == L.LS_ERR_UNSUPPORTED                   # rows of the loss kernel: V % 8 == 0
     assert _lm(d=250) == L.LS_ERR_UNSUPPORTED
-    assert _lm(V=200000) == L.LS_ERR_UNSUPPORTED
+    assert _lm(V=(1 << 24) + 8) == L.LS_ERR_UNSUPPORTED
     assert _lm(dH=None) == L.LS_ERR_INVALID_ARG                  # gradients come in pairs
     assert _lm(dW=None) == L.LS_ERR_INVALID_ARG
     assert _lm(H=None) == L.LS_ERR_INVALID_ARG

@@ -87,9 +87,13 @@ def _check(s, got, first=0, count=None):
     ("tiny", [70, 1500, 900], 256),       # 2,470 tokens: two chunks, a response across the boundary
     ("tiny_clip", [33, 64], 96),          # clipped tokens in play
     ("mid", [40, 60], 64),                # the full 151,936-word vocabulary
+    ("mid", [9, 14], 32),                 # V = 262,144 below: rows read twice by the streaming kernel
 ])
 def test_lmhead_loss_matches_oracle(cfg_name, lengths, d):
-    s = _setup(inputs.CONFIGS[cfg_name], lengths, d)
+    cfg = inputs.CONFIGS[cfg_name]
+    if d == 32:
+        cfg = inputs.replace(cfg, V=262144)
+    s = _setup(cfg, lengths, d)
     _check(s, _run(s))
 
 

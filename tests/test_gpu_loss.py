@@ -174,3 +174,14 @@ def test_loss_rows_looped_per_workgroup(cfgname, lengths):
         _, dl_i, logp_i, _ = _run(d, i, 1)
         assert torch.equal(dl_i, got[1][cu[i]:cu[i + 1]])
         assert np.array_equal(logp_i, got[2][cu[i]:cu[i + 1]])
+
+
+@pytest.mark.parametrize("V", [262144, 262152, 196616])
+def test_loss_rows_longer_than_registers(V):
+    """Vocabularies above 196,608: the row is streamed twice (running max and rescaled sum, then
+    dlogits). Full pass and scoring pass against the oracle."""
+    d = _setup(inputs.CONFIGS["tiny_clip"], lengths=[3, 5], V=V)
+    got = _run(d, 0, 2)
+    _compare(d, 0, 2, got)
+    _, logp_s, clip_s = _run_scoring(d, 0, 2)
+    assert np.array_equal(logp_s, got[2]) and np.array_equal(clip_s, got[3])
