@@ -8,7 +8,8 @@
 //
 // replay_bwd_dkdv: key-tile owner. One workgroup = 4 waves x 32 keys of one kv head (one wave per
 // SIMD); the wave keeps its keys' K and V fragments (AGPRs) and dK^T, dV^T accumulators for the
-// whole sweep over every query row that sees those keys, 32 GQA-packed rows per step. The rows
+// whole sweep over every query row that sees those keys, 32 GQA-packed rows per step, software
+// pipelined so that step j's dV / dK products overlap step j + 1's S / dP and softmax. The rows
 // were repacked per kv head before the launch (pack.hip): row-major Q and dO (A operands of
 // S = Q K^T and dP = dO V^T) and dimension-major, slot-permuted Q^T and dO^T (A operands of
 // dV^T += dO^T P and dK^T += Q^T dS, whose B operands come straight from the S / dP accumulators),
@@ -199,122 +200,208 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
   // fp16 operand scales of this call
   const float s_ds = a.scales[2];
 
-  // One step: S and dP MFMAs; 2^15 P under the dP MFMAs; dV MFMAs; scaled dS under the dV MFMAs;
-  // dK MFMAs. Fragments are read in batches ahead of their MFMAs.
-  // The loads of the step two ahead (row mn, stage nbuf) are issued between the S and dP MFMAs,
-  // one at a time, so that they enter the memory pipeline spread out.
-  auto compute = [&](const char* buf, int m0, int mn, char* nbuf) {
-    // S[row][key] = Q K^T and dP = dO V^T: lane holds key (lane & 31), rows 8(r/4) + 4hl + r%4
-    f32x16 s, dp;
-    {
-      bf16x8 af[C::KS], bfr[C::VS];
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) af[ks] = lds_b128_at(buf, qoff[ks]);
-#pragma unroll
-      for (int ks = 0; ks < C::VS; ++ks) bfr[ks] = lds_b128_at(buf, ooff[ks]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < kPerStep; ++i) issue_load(i, mn, nbuf);
-      s = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) s = mfma32(af[ks], kf[ks], s);
-      dp = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < C::VS; ++ks) dp = mfma32(bfr[ks], vf[ks], dp);
-      static_assert(kPerStep <= C::KS + C::VS, "one load after each MFMA at most");
-#pragma unroll
-      for (int i = 0; i < C::KS + C::VS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < kPerStep) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
+  // Software-pipelined steps. Step j's dV and dK products run while step j + 1's S and dP are
+  // formed, so every phase pairs one run of MFMAs with VALU work that does not depend on it and
+  // with the LDS reads of a later phase:
+  //   A  dV(j) MFMAs         | scaled dS(j), first half      | Q rows of step j + 1
+  //   B  S(j + 1) MFMAs      | scaled dS(j), second half     | dO rows of step j + 1, tile loads
+  //   C  dK(j) MFMAs         | 2^15 P(j + 1), first half     | row statistics, dO^T of step j + 1
+  //   D  dP(j + 1) MFMAs     | 2^15 P(j + 1), second half    | Q^T of step j + 1
+  // Within one wave only about a dozen cycles of VALU hide under each MFMA, so the VALU work is
+  // spread over all four runs instead of following the MFMAs it depends on.
+  // an empty asm use keeps a value's computation in the MFMA run it is written in (instruction
+  // selection would otherwise sink it to its first real use)
+  auto pin = [](float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  auto p_elem = [&](const f32x16& s, const f32x4 (&st)[4][2], int r, int m0) {
+    const int q = r >> 2, e = r & 3;
+    float pv = fast_exp2(__builtin_fmaf(s[r], c2, -st[q][e >> 1][2 * (e & 1)]));
+    if (!PROMPT) {
+      // causal within the response (row t at key position t + qo); rows of other responses see
+      // none of these keys
+      const int t = (m0 + 8 * q + 4 * hl + e) / g - tokb;
+      pv = (t >= 0 && t < R && key0 + mykey <= t + qo) ? pv : 0.0f;
     }
+    return pv;
+  };
+  auto ds_elem = [&](const f32x16& p, const f32x16& dpv, const f32x4 (&st)[4][2], int r) {
+    const int q = r >> 2, e = r & 3;
+    return p[r] * __builtin_fmaf(dpv[r], s_ds, -st[q][e >> 1][2 * (e & 1) + 1]);
+  };
+  auto read_stats = [&](const char* buf, f32x4 (&st)[4][2]) {
     // row statistics of rows 8q + 4hl + 0..3: {l0, d0, l1, d1}, {l2, d2, l3, d3}
-    f32x4 st[4][2];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       st[q][0] = __builtin_bit_cast(f32x4, lds_b128_at(buf, C::OFF_LD + (8 * q + 4 * hl) * 8));
       st[q][1] = __builtin_bit_cast(f32x4, lds_b128_at(buf, C::OFF_LD + (8 * q + 4 * hl) * 8 + 16));
     }
-    // dO^T fragments (fp16, scaled) for the dV MFMAs
-    f16x8 ot[2][C::VB];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int b = 0; b < C::VB; ++b) ot[h][b] = lds_h128_at(buf, C::OFF_OT + b * 32 * C::TROW + toff[h]);
-    __builtin_amdgcn_sched_barrier(0);
-    // 2^15 P = exp2(S scale log2 e - (LSE log2 e - 15)), under the dP MFMAs
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int q = r >> 2, e = r & 3;
-      float pv = fast_exp2(__builtin_fmaf(s[r], c2, -st[q][e >> 1][2 * (e & 1)]));
-      if (!PROMPT) {
-        // causal within the response (row t at key position t + qo); rows of other responses see
-        // none of these keys
-        const int t = (m0 + 8 * q + 4 * hl + e) / g - tokb;
-        pv = (t >= 0 && t < R && key0 + mykey <= t + qo) ? pv : 0.0f;
-      }
-      s[r] = pv;
-    }
-    // dV^T[dv][key] += dO^T P (A operands: one 16-byte read of packed slots)
-    {
-      const f16x8 p0 = c_regs_to_f16x8(s, 0), p1 = c_regs_to_f16x8(s, 8);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int b = 0; b < C::VB; ++b) dv[b] = mfma32h(ot[0][b], p0, dv[b]);
-#pragma unroll
-      for (int b = 0; b < C::VB; ++b) dv[b] = mfma32h(ot[1][b], p1, dv[b]);
-    }
-    // Q^T fragments (fp16, scaled) for the dK MFMAs
-    f16x8 qt[2][C::DB];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int b = 0; b < C::DB; ++b) qt[h][b] = lds_h128_at(buf, C::OFF_QT + b * 32 * C::TROW + toff[h]);
-    __builtin_amdgcn_sched_barrier(0);
-    // scaled dS = 2^15 P (dP s_dS - Delta s_dS), under the dV MFMAs
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int q = r >> 2, e = r & 3;
-      dp[r] = s[r] * __builtin_fmaf(dp[r], s_ds, -st[q][e >> 1][2 * (e & 1) + 1]);
-    }
-    // dK^T[d][key] += Q^T dS
-    {
-      const f16x8 d0 = c_regs_to_f16x8(dp, 0), d1 = c_regs_to_f16x8(dp, 8);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int b = 0; b < C::DB; ++b) dk[b] = mfma32h(qt[0][b], d0, dk[b]);
-#pragma unroll
-      for (int b = 0; b < C::DB; ++b) dk[b] = mfma32h(qt[1][b], d1, dk[b]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // three-stage ring over the steps: before step t each wave waits for its own loads of step t
-  // (step t + 1's may be in flight) and the barrier publishes the step; every wave is then past
-  // step t - 1, whose stage receives step t + 2 (issued inside the step's MFMAs). Past the last
-  // step the last step's rows are loaded again into that free stage, so every step issues the same
-  // number of loads and the wait count is fixed.
+  // State carried from one step to the next: 2^15 P (fp32 and fp16), dP, the dO^T and Q^T
+  // fragments and the row statistics of the step whose dV / dK products are still to run.
+  f32x16 p, dp;
+  f16x8 pf[2];
+  f16x8 ot[2][C::VB], qt[2][C::DB];
+  f32x4 st[4][2];
+
+  // Three-stage ring. The barrier of step j + 1 (top of pipelined step j) publishes step j + 1's
+  // tiles (each wave first waits for its own loads of it) and frees step j's stage: every read
+  // of that stage was issued during pipelined step j - 1 and has returned (lgkmcnt(0) before the
+  // barrier). That stage then receives step j + 3, issued under the S(j + 1) MFMAs, two steps
+  // before it is read. Past the last step the last step's rows are loaded again, so every step
+  // issues the same number of loads and the wait count is fixed.
   char* const st0 = smem;
   char* const st1 = smem + C::STAGE;
   char* const st2 = smem + 2 * C::STAGE;
   auto mrow = [&](int t) { return row_begin + min(t, nsteps - 1) * C::BR; };
+
+  // the reads and products of one step's S and dP, 2^15 P and its fp16 copy, with the fragments
+  // of the step's dV / dK products; used once, for step 0
+  auto first_step = [&](const char* buf) {
+    bf16x8 af[C::KS], bfr[C::VS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) af[ks] = lds_b128_at(buf, qoff[ks]);
+#pragma unroll
+    for (int ks = 0; ks < C::VS; ++ks) bfr[ks] = lds_b128_at(buf, ooff[ks]);
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) s = mfma32(af[ks], kf[ks], s);
+    dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::VS; ++ks) dp = mfma32(bfr[ks], vf[ks], dp);
+    read_stats(buf, st);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < C::VB; ++b) ot[h][b] = lds_h128_at(buf, C::OFF_OT + b * 32 * C::TROW + toff[h]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < C::DB; ++b) qt[h][b] = lds_h128_at(buf, C::OFF_QT + b * 32 * C::TROW + toff[h]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = p_elem(s, st, r, row_begin);
+    pf[0] = c_regs_to_f16x8(p, 0);
+    pf[1] = c_regs_to_f16x8(p, 8);
+  };
+
+  // pipelined step j: finishes step j (buf of step j + 1 = nb, free stage fb receives step j + 3)
+  auto step = [&](int j, const char* nb, char* fb) {
+    const int mn = row_begin + (j + 1) * C::BR;  // first packed row of step j + 1
+    const int ml = mrow(j + 3);
+    constexpr int NA = 2 * C::VB, NB = C::KS, NC = 2 * C::DB, ND = C::VS;
+    // A: dV(j) += dO^T P; scaled dS(j) rows 0..7; Q rows of step j + 1
+    bf16x8 af[C::KS];
+    f32x16 ds = dp;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      dv[i % C::VB] = mfma32h(ot[i / C::VB][i % C::VB], pf[i / C::VB], dv[i % C::VB]);
+#pragma unroll
+      for (int k = 0; k < C::KS; ++k)
+        if (k * NA / C::KS == i) af[k] = lds_b128_at(nb, qoff[k]);
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (r * NA / 8 == i) ds[r] = pin(ds_elem(p, dp, st, r));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // B: S(j + 1) = Q K^T; scaled dS(j) rows 8..15; dO rows of step j + 1; step j + 3's tiles
+    const f16x8 d0 = c_regs_to_f16x8(ds, 0);
+    bf16x8 bfr[C::VS];
+    f32x16 sn = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      sn = mfma32(af[i], kf[i], sn);
+#pragma unroll
+      for (int k = 0; k < C::VS; ++k)
+        if (k * NB / C::VS == i) bfr[k] = lds_b128_at(nb, ooff[k]);
+#pragma unroll
+      for (int r = 8; r < 16; ++r)
+        if ((r - 8) * NB / 8 == i) ds[r] = pin(ds_elem(p, dp, st, r));
+#pragma unroll
+      for (int l = 0; l < kPerStep; ++l)
+        if (l * NB / kPerStep == i) issue_load(l, ml, fb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const f16x8 d1 = c_regs_to_f16x8(ds, 8);
+    // C: dK(j) += Q^T dS; row statistics and dO^T of step j + 1; 2^15 P(j + 1) rows 0..7
+    f32x4 stn[4][2];
+    read_stats(nb, stn);
+    f16x8 otn[2][C::VB];
+    f32x16 pn;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      dk[i % C::DB] = mfma32h(qt[i / C::DB][i % C::DB], i / C::DB ? d1 : d0, dk[i % C::DB]);
+#pragma unroll
+      for (int k = 0; k < 2 * C::VB; ++k)
+        if (k * NC / (2 * C::VB) == i) otn[k / C::VB][k % C::VB] = lds_h128_at(nb, C::OFF_OT + (k % C::VB) * 32 * C::TROW + toff[k / C::VB]);
+      // P needs the S MFMAs' results: start it half-way through the run
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (NC / 2 + r * (NC - NC / 2) / 8 == i) pn[r] = pin(p_elem(sn, stn, r, mn));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pf[0] = c_regs_to_f16x8(pn, 0);
+    // D: dP(j + 1) = dO V^T; Q^T of step j + 1; 2^15 P(j + 1) rows 8..15
+    f16x8 qtn[2][C::DB];
+    f32x16 dpn = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      dpn = mfma32(bfr[i], vf[i], dpn);
+#pragma unroll
+      for (int k = 0; k < 2 * C::DB; ++k)
+        if (k * ND / (2 * C::DB) == i) qtn[k / C::DB][k % C::DB] = lds_h128_at(nb, C::OFF_QT + (k % C::DB) * 32 * C::TROW + toff[k / C::DB]);
+#pragma unroll
+      for (int r = 8; r < 16; ++r)
+        if ((r - 8) * ND / 8 == i) pn[r] = pin(p_elem(sn, stn, r, mn));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pf[1] = c_regs_to_f16x8(pn, 8);
+    p = pn;
+    dp = dpn;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int b = 0; b < C::VB; ++b) ot[h][b] = otn[h][b];
+#pragma unroll
+      for (int b = 0; b < C::DB; ++b) qt[h][b] = qtn[h][b];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      st[q][0] = stn[q][0];
+      st[q][1] = stn[q][1];
+    }
+  };
+
   if (nsteps > 0) {
     issue_step(mrow(0), st0);
     issue_step(mrow(1), st1);
+    issue_step(mrow(2), st2);
+    wait_vmem_le<2 * kPerStep>();
+    bare_barrier();
+    first_step(st0);
   }
+  // Pipelined step j runs whether or not step j + 1 exists: past the last step it forms S and dP
+  // of a repeated tile (rows clamped, results unused), so every wave passes the same barriers.
   for (int it = 0; it < nsteps; it += 3) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int t = it + j;
-      if (t >= nsteps) break;
-      char* cur = j == 0 ? st0 : (j == 1 ? st1 : st2);
-      char* nxt = j == 0 ? st2 : (j == 1 ? st0 : st1);
+    for (int jj = 0; jj < 3; ++jj) {
+      const int j = it + jj;
+      if (j >= nsteps) break;
+      char* nb = jj == 0 ? st1 : (jj == 1 ? st2 : st0);  // stage of step j + 1
+      char* fb = jj == 0 ? st0 : (jj == 1 ? st1 : st2);  // stage of step j, free after the barrier
       wait_vmem_le<kPerStep>();
-      wait_lds();      // this wave's reads of the stage refilled next have returned
+      wait_lds();      // this wave's reads of step j's stage have returned
       bare_barrier();  // no fence: it would wait for every direct load in flight
-      compute(cur, row_begin + t * C::BR, mrow(t + 2), nxt);
+      step(j, nb, fb);
     }
   }
+  // no direct load may still be writing into LDS when the waves end
+  wait_vmem();
 
   if (!kvalid) return;
   // C layout of dV^T / dK^T: lane holds key (lane & 31), dims 32b + 8(r/4) + 4hl + r%4.
