@@ -115,7 +115,7 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
       off = align256(off + (size_t)Hkv * pl->mpad * Dv * 2);
     }
     pl->off_rs = off;
-    off = align256(off + (size_t)Hkv * pl->mpad * 8);
+    off = align256(off + (size_t)Hkv * pl->mpad * (wide ? 8 : 32));
     pl->off_sc = off;  // fp16 operand scales: partial maxima (8 per block), then the scales
     off = align256(off + (size_t)(kScaleBlocks + 1) * 8 * 4);
   }

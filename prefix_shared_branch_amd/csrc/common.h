@@ -48,6 +48,9 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x16 mfma32x8(const s16x4& a, const s16x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
@@ -192,6 +195,10 @@ __device__ __forceinline__ f16x8 lds_h128_at(const char* base, int byte_off) {
 
 __device__ __forceinline__ bf16x8 lds_b128_at(const char* base, int byte_off) {
   return *reinterpret_cast<const LSR_LDS bf16x8*>(reinterpret_cast<uintptr_t>(base + byte_off));
+}
+
+__device__ __forceinline__ s16x4 lds_s16x4_at(const char* base, int byte_off) {
+  return *reinterpret_cast<const LSR_LDS s16x4*>(reinterpret_cast<uintptr_t>(base + byte_off));
 }
 
 __device__ __forceinline__ s16x4 lds_tr_at(const char* base, int byte_off) {

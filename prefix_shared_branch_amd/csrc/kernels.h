@@ -99,11 +99,18 @@ struct RowStatArgs {
   const float* lse;      // [Hq, T]
   const float* delta;    // [Hq, T]
   const float* scales;   // BwdScales (Delta is stored multiplied by the dS scale)
-  float* out;            // [Hkv, mpad, 2]
+  float* out;            // pack_rowstats: [Hkv, mpad, 2]; pack_rowext: [Hkv, mpad, 8] (32 bytes per row)
   int32_t T, Hq, g, Hkv;
   int64_t M, mpad;       // packed rows per kv head (T * g) and their padded count
+  float c2;              // softmax scale * log2(e) (pack_rowext)
 };
 hipError_t launch_pack_rowstats(const RowStatArgs& a, hipStream_t st);
+// Row terms of the D = 64 / 128 dK/dV kernel as MFMA operands: per packed row, 16 bf16 values
+// [x_hi, x_mid, x_lo, 0, 0, 0, 0, 0, d_hi, d_mid, d_lo, 0, 0, 0, 0, 0] with
+// x = -(LSE log2 e - 15) / (scale log2 e) and d = -Delta, each split into three bf16 parts whose sum
+// is the fp32 value to about 24 significant bits. A 32x32x8 product of these rows with a constant
+// [1, 1, 1, 0] operand starts the S and dP accumulators at x and d.
+hipError_t launch_pack_rowext(const RowStatArgs& a, hipStream_t st);
 
 // Power-of-two scales of the fp16 operands of the dK/dV products (pack.hip), in device memory:
 //   [0] s_dO: dO * s_dO has |values| <= 2^15      [1] s_Q: Q * s_Q has |values| <= 2^15
@@ -170,7 +177,8 @@ struct BwdArgs {
   uint16_t* dOr;        // [Hkv, mpad, Dv]
   uint16_t* QT;         // dimension-major, slot-permuted: [Hkv * Dqk, mpad]
   uint16_t* dOT;        // [Hkv * Dv, mpad]
-  float* rowstat;       // [Hkv, mpad, 2]: {LSE log2 e - 15, Delta * s_dS}
+  float* rowstat;       // latent KV: [Hkv, mpad, 2] {LSE log2 e - 15, Delta * s_dS}; D = 64 / 128:
+                        // [Hkv, mpad, 8], the bf16 row terms of pack_rowext
   float* scale_part;    // [kScaleBlocks, 8] partial maxima
   float* scales;        // [4] fp16 operand scales (see ScaleArgs)
   int64_t mpad;         // packed query rows per kv head (T * g) rounded up to 64

@@ -121,6 +121,34 @@ __global__ __launch_bounds__(256) void pack_rowstats(RowStatArgs a) {
   reinterpret_cast<float2*>(a.out)[(int64_t)k * a.mpad + m] = make_float2(l, d);
 }
 
+// bf16 parts hi, mid, lo of v (hi + mid + lo = v to about 24 significant bits), then a zero; a
+// non-finite v keeps hi = v and zero parts
+__device__ __forceinline__ u32x2 split3_bf16(float v) {
+  const float hi = (float)(__bf16)v;
+  const float r1 = __builtin_isfinite(v) ? v - hi : 0.0f;
+  const float mid = (float)(__bf16)r1;
+  const float lo = r1 - mid;
+  return u32x2{pack_bf16x2(hi, mid), pack_bf16x2(lo, 0.0f)};
+}
+
+__global__ __launch_bounds__(256) void pack_rowext(RowStatArgs a) {
+  const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int k = blockIdx.y;
+  if (m >= a.mpad) return;
+  float x = -INFINITY, d = 0.0f;  // padding rows: S starts at -inf, so P = 0
+  if (m < a.M) {
+    const int64_t t = m / a.g;
+    const int h = k * a.g + (int)(m - t * a.g);
+    // 2^15 P = exp2(scale log2 e (S + x)) with x = -(LSE log2 e - 15) / (scale log2 e)
+    x = -(a.lse[(int64_t)h * a.T + t] * kLog2e - 15.0f) / a.c2;
+    d = -a.delta[(int64_t)h * a.T + t];
+  }
+  const u32x2 xs = split3_bf16(x), ds = split3_bf16(d);
+  u32x4* o = reinterpret_cast<u32x4*>(a.out + ((int64_t)k * a.mpad + m) * 8);
+  o[0] = u32x4{xs[0], xs[1], 0u, 0u};
+  o[1] = u32x4{ds[0], ds[1], 0u, 0u};
+}
+
 // Partial maxima for the fp16 operand scales: {max |dO|, max row norm of dO, max |Q|, max row norm
 // of V over the prompt and the responses}. Rows are read 16 bytes per thread; a row's squared
 // norm is summed over the DIM / 8 consecutive lanes that hold it.
@@ -281,6 +309,12 @@ hipError_t launch_pack_rows(const PackArgs& a, hipStream_t st) {
 hipError_t launch_pack_rowstats(const RowStatArgs& a, hipStream_t st) {
   if (a.mpad == 0) return hipSuccess;
   hipLaunchKernelGGL(pack_rowstats, dim3((unsigned)((a.mpad + 255) / 256), (unsigned)a.Hkv), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_rowext(const RowStatArgs& a, hipStream_t st) {
+  if (a.mpad == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_rowext, dim3((unsigned)((a.mpad + 255) / 256), (unsigned)a.Hkv), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -13,7 +13,9 @@
 // were repacked per kv head before the launch (pack.hip): row-major Q and dO (A operands of
 // S = Q K^T and dP = dO V^T) and dimension-major, slot-permuted Q^T and dO^T (A operands of
 // dV^T += dO^T P and dK^T += Q^T dS, whose B operands come straight from the S / dP accumulators),
-// plus each row's {LSE log2 e, Delta}. Per step all of them stream global -> LDS by direct DMA into
+// plus each row's LSE and Delta as bf16 row terms (pack_rowext) that one 32x32x8 MFMA each turns
+// into the starting values of the S and dP accumulators. Per step all of them stream global -> LDS
+// by direct DMA into
 // a three-stage ring of XOR-swizzled tiles, so every MFMA operand is one 16-byte LDS read.
 // The dV / dK products run in fp16 (11 significant bits; bf16's 8 would cost ~1.7e-3 relative error
 // in the fp32 sums over 10^6-10^7 terms, fp16 ~2e-4) with exact power-of-two scaling so every
@@ -42,12 +44,12 @@ struct DkvCfg {
   static constexpr int OBYTES = BR * OROW;
   static constexpr int QTBYTES = D * TROW;
   static constexpr int OTBYTES = DV * TROW;
-  static constexpr int LDBYTES = BR * 8;      // {LSE log2 e, Delta} per row
+  static constexpr int LDBYTES = BR * 32;     // bf16 row terms of S and dP, 32 bytes per row
   static constexpr int OFF_O = QBYTES;
   static constexpr int OFF_QT = OFF_O + OBYTES;
   static constexpr int OFF_OT = OFF_QT + QTBYTES;
   static constexpr int OFF_LD = OFF_OT + OTBYTES;
-  static constexpr int STAGE = OFF_LD + 1024;  // row statistics padded to 1 KB
+  static constexpr int STAGE = OFF_LD + LDBYTES;
   static constexpr int NSTAGE = 3;
   static constexpr int QINS = QBYTES / 4096;  // 1 KB direct loads per wave per step
   static constexpr int OINS = OBYTES / 4096;
@@ -145,9 +147,9 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t ro = buf_rsrc(a.dOr + (int64_t)kvh * mpad * DV, mpad * C::OROW);
   const __amdgpu_buffer_rsrc_t rqt = buf_rsrc(a.QT + (int64_t)kvh * D * mpad, (int64_t)D * mpad * 2);
   const __amdgpu_buffer_rsrc_t rot = buf_rsrc(a.dOT + (int64_t)kvh * DV * mpad, (int64_t)DV * mpad * 2);
-  const __amdgpu_buffer_rsrc_t rld = buf_rsrc(a.rowstat + (int64_t)kvh * mpad * 2, mpad * 8);
+  const __amdgpu_buffer_rsrc_t rld = buf_rsrc(a.rowstat + (int64_t)kvh * mpad * 8, mpad * 32);
   // lane-constant byte offsets of the direct loads within one step's slabs: Q / dO rows row-major
-  // with XOR-swizzled chunks, Q^T / dO^T rows of 32 slots, 4 bytes of row statistics per lane
+  // with XOR-swizzled chunks, Q^T / dO^T rows of 32 slots, 4 bytes of row terms per lane
   uint32_t qdo[C::QINS], odo[C::OINS], qtdo[C::QTINS], otdo[C::OTINS];
 #pragma unroll
   for (int u = 0; u < C::QINS; ++u) {
@@ -169,9 +171,9 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
     const int row = (wv * C::OTINS + u) * 16 + (lane >> 2);
     otdo[u] = (uint32_t)(row * mpad * 2 + (((lane & 3) ^ swz<4>(row)) << 4));
   }
-  const uint32_t ldo = (uint32_t)lane * 4;
-  // load i of this wave's kPerStep loads of the step at packed row m0 into stage buffer buf. Every
-  // wave also loads the 256 bytes of row statistics (the same bytes; no branch on the wave).
+  const uint32_t ldo = (uint32_t)(wv * 256 + lane * 4);
+  // load i of this wave's kPerStep loads of the step at packed row m0 into stage buffer buf; the
+  // last one is this wave's quarter of the step's 1 KB of row terms.
   constexpr int kPerStep = C::QINS + C::OINS + C::QTINS + C::OTINS + 1;
   auto issue_load = [&](int i, int m0, char* buf) {
     if (i < C::QINS) {
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
       const int u = i - C::QINS - C::OINS - C::QTINS;
       lds_dma16_buf(rot, otdo[u], buf + C::OFF_OT + (wv * C::OTINS + u) * 1024, m0 * 2);
     } else {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (LSR_LDS void*)(buf + C::OFF_LD), 4, (int)ldo, m0 * 8, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (LSR_LDS void*)(buf + C::OFF_LD + wv * 256), 4, (int)ldo, m0 * 32, 0, 0);
     }
   };
   auto issue_step = [&](int m0, char* buf) {
@@ -215,9 +217,9 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
     asm volatile("" : "+v"(v));
     return v;
   };
-  auto p_elem = [&](const f32x16& s, const f32x4 (&st)[4][2], int r, int m0) {
+  auto p_elem = [&](const f32x16& s, int r, int m0) {
     const int q = r >> 2, e = r & 3;
-    float pv = fast_exp2(__builtin_fmaf(s[r], c2, -st[q][e >> 1][2 * (e & 1)]));
+    float pv = fast_exp2(s[r] * c2);
     if (!PROMPT) {
       // causal within the response (row t at key position t + qo); rows of other responses see
       // none of these keys
@@ -226,25 +228,21 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
     }
     return pv;
   };
-  auto ds_elem = [&](const f32x16& p, const f32x16& dpv, const f32x4 (&st)[4][2], int r) {
-    const int q = r >> 2, e = r & 3;
-    return p[r] * __builtin_fmaf(dpv[r], s_ds, -st[q][e >> 1][2 * (e & 1) + 1]);
+  auto ds_elem = [&](const f32x16& p, const f32x16& dpv, int r) { return p[r] * (dpv[r] * s_ds); };
+  // row terms of the step's 32 rows, as the A operands of the 32x32x8 products that start the S and
+  // dP accumulators (lanes 32..63 read the zero half of each row)
+  auto read_terms = [&](const char* buf, s16x4& xq, s16x4& xo) {
+    xq = lds_s16x4_at(buf, C::OFF_LD + l32 * 32 + hl * 8);
+    xo = lds_s16x4_at(buf, C::OFF_LD + l32 * 32 + 16 + hl * 8);
   };
-  auto read_stats = [&](const char* buf, f32x4 (&st)[4][2]) {
-    // row statistics of rows 8q + 4hl + 0..3: {l0, d0, l1, d1}, {l2, d2, l3, d3}
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      st[q][0] = __builtin_bit_cast(f32x4, lds_b128_at(buf, C::OFF_LD + (8 * q + 4 * hl) * 8));
-      st[q][1] = __builtin_bit_cast(f32x4, lds_b128_at(buf, C::OFF_LD + (8 * q + 4 * hl) * 8 + 16));
-    }
-  };
+  // B operand of those products: [1, 1, 1, 0] over k = 0..3 for every key, zero for k = 4..7
+  const s16x4 ones = hl ? s16x4{0, 0, 0, 0} : s16x4{0x3F80, 0x3F80, 0x3F80, 0};
 
-  // State carried from one step to the next: 2^15 P (fp32 and fp16), dP, the dO^T and Q^T
-  // fragments and the row statistics of the step whose dV / dK products are still to run.
+  // State carried from one step to the next: 2^15 P (fp32 and fp16), dP - Delta, and the dO^T and
+  // Q^T fragments of the step whose dV / dK products are still to run.
   f32x16 p, dp;
   f16x8 pf[2];
   f16x8 ot[2][C::VB], qt[2][C::DB];
-  f32x4 st[4][2];
 
   // Three-stage ring. The barrier of step j + 1 (top of pipelined step j) publishes step j + 1's
   // tiles (each wave first waits for its own loads of it) and frees step j's stage: every read
@@ -261,17 +259,18 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
   // of the step's dV / dK products; used once, for step 0
   auto first_step = [&](const char* buf) {
     bf16x8 af[C::KS], bfr[C::VS];
+    s16x4 xq, xo;
+    read_terms(buf, xq, xo);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) af[ks] = lds_b128_at(buf, qoff[ks]);
 #pragma unroll
     for (int ks = 0; ks < C::VS; ++ks) bfr[ks] = lds_b128_at(buf, ooff[ks]);
-    f32x16 s = f32x16{};
+    f32x16 s = mfma32x8(xq, ones, f32x16{});
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) s = mfma32(af[ks], kf[ks], s);
-    dp = f32x16{};
+    dp = mfma32x8(xo, ones, f32x16{});
 #pragma unroll
     for (int ks = 0; ks < C::VS; ++ks) dp = mfma32(bfr[ks], vf[ks], dp);
-    read_stats(buf, st);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -281,7 +280,7 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
 #pragma unroll
       for (int b = 0; b < C::DB; ++b) qt[h][b] = lds_h128_at(buf, C::OFF_QT + b * 32 * C::TROW + toff[h]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = p_elem(s, st, r, row_begin);
+    for (int r = 0; r < 16; ++r) p[r] = p_elem(s, r, row_begin);
     pf[0] = c_regs_to_f16x8(p, 0);
     pf[1] = c_regs_to_f16x8(p, 8);
   };
@@ -291,8 +290,10 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
     const int mn = row_begin + (j + 1) * C::BR;  // first packed row of step j + 1
     const int ml = mrow(j + 3);
     constexpr int NA = 2 * C::VB, NB = C::KS, NC = 2 * C::DB, ND = C::VS;
-    // A: dV(j) += dO^T P; scaled dS(j) rows 0..7; Q rows of step j + 1
+    // A: dV(j) += dO^T P; scaled dS(j) rows 0..7; row terms and Q rows of step j + 1
     bf16x8 af[C::KS];
+    s16x4 xq, xo;
+    read_terms(nb, xq, xo);
     f32x16 ds = dp;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -303,13 +304,13 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
         if (k * NA / C::KS == i) af[k] = lds_b128_at(nb, qoff[k]);
 #pragma unroll
       for (int r = 0; r < 8; ++r)
-        if (r * NA / 8 == i) ds[r] = pin(ds_elem(p, dp, st, r));
+        if (r * NA / 8 == i) ds[r] = pin(ds_elem(p, dp, r));
       __builtin_amdgcn_sched_barrier(0);
     }
     // B: S(j + 1) = Q K^T; scaled dS(j) rows 8..15; dO rows of step j + 1; step j + 3's tiles
     const f16x8 d0 = c_regs_to_f16x8(ds, 0);
     bf16x8 bfr[C::VS];
-    f32x16 sn = f32x16{};
+    f32x16 sn = mfma32x8(xq, ones, f32x16{});
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -319,16 +320,14 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
         if (k * NB / C::VS == i) bfr[k] = lds_b128_at(nb, ooff[k]);
 #pragma unroll
       for (int r = 8; r < 16; ++r)
-        if ((r - 8) * NB / 8 == i) ds[r] = pin(ds_elem(p, dp, st, r));
+        if ((r - 8) * NB / 8 == i) ds[r] = pin(ds_elem(p, dp, r));
 #pragma unroll
       for (int l = 0; l < kPerStep; ++l)
         if (l * NB / kPerStep == i) issue_load(l, ml, fb);
       __builtin_amdgcn_sched_barrier(0);
     }
     const f16x8 d1 = c_regs_to_f16x8(ds, 8);
-    // C: dK(j) += Q^T dS; row statistics and dO^T of step j + 1; 2^15 P(j + 1) rows 0..7
-    f32x4 stn[4][2];
-    read_stats(nb, stn);
+    // C: dK(j) += Q^T dS; dO^T of step j + 1; 2^15 P(j + 1) rows 0..7
     f16x8 otn[2][C::VB];
     f32x16 pn;
     __builtin_amdgcn_sched_barrier(0);
@@ -341,13 +340,13 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
       // P needs the S MFMAs' results: start it half-way through the run
 #pragma unroll
       for (int r = 0; r < 8; ++r)
-        if (NC / 2 + r * (NC - NC / 2) / 8 == i) pn[r] = pin(p_elem(sn, stn, r, mn));
+        if (NC / 2 + r * (NC - NC / 2) / 8 == i) pn[r] = pin(p_elem(sn, r, mn));
       __builtin_amdgcn_sched_barrier(0);
     }
     pf[0] = c_regs_to_f16x8(pn, 0);
     // D: dP(j + 1) = dO V^T; Q^T of step j + 1; 2^15 P(j + 1) rows 8..15
     f16x8 qtn[2][C::DB];
-    f32x16 dpn = f32x16{};
+    f32x16 dpn = mfma32x8(xo, ones, f32x16{});
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
@@ -357,7 +356,7 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
         if (k * ND / (2 * C::DB) == i) qtn[k / C::DB][k % C::DB] = lds_h128_at(nb, C::OFF_QT + (k % C::DB) * 32 * C::TROW + toff[k / C::DB]);
 #pragma unroll
       for (int r = 8; r < 16; ++r)
-        if ((r - 8) * ND / 8 == i) pn[r] = pin(p_elem(sn, stn, r, mn));
+        if ((r - 8) * ND / 8 == i) pn[r] = pin(p_elem(sn, r, mn));
       __builtin_amdgcn_sched_barrier(0);
     }
     pf[1] = c_regs_to_f16x8(pn, 8);
@@ -369,11 +368,6 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
       for (int b = 0; b < C::VB; ++b) ot[h][b] = otn[h][b];
 #pragma unroll
       for (int b = 0; b < C::DB; ++b) qt[h][b] = qtn[h][b];
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      st[q][0] = stn[q][0];
-      st[q][1] = stn[q][1];
     }
   };
 
@@ -527,6 +521,7 @@ hipError_t dkdv_go(BwdArgs& a, hipStream_t st) {
   p.f16_scale = a.scales + 0;
   if ((e = launch_pack_keys_t(p, st)) != hipSuccess) return e;
   RowStatArgs r;
+  r.c2 = G.scale_log2;
   r.lse = a.lse;
   r.delta = a.delta;
   r.scales = a.scales;
@@ -537,7 +532,7 @@ hipError_t dkdv_go(BwdArgs& a, hipStream_t st) {
   r.Hkv = G.Hkv;
   r.M = M;
   r.mpad = a.mpad;
-  if ((e = launch_pack_rowstats(r, st)) != hipSuccess) return e;
+  if ((e = launch_pack_rowext(r, st)) != hipSuccess) return e;
 
   if (a.ktiles_prompt > 0) {
     const long long W = (long long)a.ktiles_prompt * G.Hkv;
