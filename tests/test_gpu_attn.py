@@ -272,3 +272,21 @@ def test_backward_without_output_residual():
     dq, dks, dvs = case.bwd(o, lse, dkp, dvp)
     t.cuda.synchronize()
     _check_all(dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp), case.oracle())
+
+
+@pytest.mark.parametrize("base,scale", [("tiny", 0.01), ("tiny", 1.0), ("mid", 0.01), ("mid", 1.0)])
+def test_softmax_scale_extremes(base, scale):
+    """A caller-chosen softmax scale far from 1/sqrt(D): nearly flat (0.01) and nearly one-hot (1.0)
+    attention. The dK/dV kernel takes LSE and Delta as three-part bf16 row terms inside its MFMAs,
+    with LSE divided by the scale, so both ends of the scale range check those terms."""
+    import dataclasses
+    import types
+    cfg = inputs.replace(inputs.CONFIGS[base], P=2000, seed=41)
+    case = Case(cfg, [70, 129])
+    case.cfg = types.SimpleNamespace(**dataclasses.asdict(cfg), scale=scale)
+    t = case.torch
+    dkp, dvp = case.accums()
+    o, lse = case.fwd()
+    dq, dks, dvs = case.bwd(o, lse, dkp, dvp)
+    t.cuda.synchronize()
+    _check_all(dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp), case.oracle(), literal_abs=False)
