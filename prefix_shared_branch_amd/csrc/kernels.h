@@ -105,11 +105,12 @@ struct RowStatArgs {
   float c2;              // softmax scale * log2(e) (pack_rowext)
 };
 hipError_t launch_pack_rowstats(const RowStatArgs& a, hipStream_t st);
-// Row terms of the D = 64 / 128 dK/dV kernel as MFMA operands: per packed row, 16 bf16 values
-// [x_hi, x_mid, x_lo, 0, 0, 0, 0, 0, d_hi, d_mid, d_lo, 0, 0, 0, 0, 0] with
-// x = -(LSE log2 e - 15) / (scale log2 e) and d = -Delta, each split into three bf16 parts whose sum
-// is the fp32 value to about 24 significant bits. A 32x32x8 product of these rows with a constant
-// [1, 1, 1, 0] operand starts the S and dP accumulators at x and d.
+// Row terms of the D = 64 / 128 dK/dV kernel as MFMA operands: x = -(LSE log2 e - 15) /
+// (scale log2 e) and d = -Delta of each packed row, each split into three bf16 parts whose sum is
+// the fp32 value to about 24 significant bits, stored as [hi, mid, lo, 0]. Per block of 32 rows
+// (1 KB): the x parts of rows 0..31, 256 zero bytes, the d parts, 256 zero bytes. A 32x32x8 product
+// of these rows (k = 0..3, zeros for k = 4..7) with a constant [1, 1, 1, 0] operand starts the S and
+// dP accumulators at x and d.
 hipError_t launch_pack_rowext(const RowStatArgs& a, hipStream_t st);
 
 // Power-of-two scales of the fp16 operands of the dK/dV products (pack.hip), in device memory:

@@ -143,10 +143,14 @@ __global__ __launch_bounds__(256) void pack_rowext(RowStatArgs a) {
     x = -(a.lse[(int64_t)h * a.T + t] * kLog2e - 15.0f) / a.c2;
     d = -a.delta[(int64_t)h * a.T + t];
   }
+  // 32-row blocks of 1 KB, each [x parts of rows 0..31 | zeros | d parts | zeros] at 8 bytes per row,
+  // so the 32 lanes that read one quarter read 256 contiguous bytes
   const u32x2 xs = split3_bf16(x), ds = split3_bf16(d);
-  u32x4* o = reinterpret_cast<u32x4*>(a.out + ((int64_t)k * a.mpad + m) * 8);
-  o[0] = u32x4{xs[0], xs[1], 0u, 0u};
-  o[1] = u32x4{ds[0], ds[1], 0u, 0u};
+  u32x2* o = reinterpret_cast<u32x2*>(a.out + ((int64_t)k * a.mpad + (m & ~(int64_t)31)) * 8) + (m & 31);
+  o[0] = xs;
+  o[32] = u32x2{0u, 0u};
+  o[64] = ds;
+  o[96] = u32x2{0u, 0u};
 }
 
 // Partial maxima for the fp16 operand scales: {max |dO|, max row norm of dO, max |Q|, max row norm

@@ -230,10 +230,10 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
   };
   auto ds_elem = [&](const f32x16& p, const f32x16& dpv, int r) { return p[r] * (dpv[r] * s_ds); };
   // row terms of the step's 32 rows, as the A operands of the 32x32x8 products that start the S and
-  // dP accumulators (lanes 32..63 read the zero half of each row)
+  // dP accumulators (lanes 32..63 read the zero quarters; each half-wave reads 256 contiguous bytes)
   auto read_terms = [&](const char* buf, s16x4& xq, s16x4& xo) {
-    xq = lds_s16x4_at(buf, C::OFF_LD + l32 * 32 + hl * 8);
-    xo = lds_s16x4_at(buf, C::OFF_LD + l32 * 32 + 16 + hl * 8);
+    xq = lds_s16x4_at(buf, C::OFF_LD + hl * 256 + l32 * 8);
+    xo = lds_s16x4_at(buf, C::OFF_LD + 512 + hl * 256 + l32 * 8);
   };
   // B operand of those products: [1, 1, 1, 0] over k = 0..3 for every key, zero for k = 4..7
   const s16x4 ones = hl ? s16x4{0, 0, 0, 0} : s16x4{0x3F80, 0x3F80, 0x3F80, 0};
