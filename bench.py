@@ -29,8 +29,13 @@ sys.path.insert(0, ROOT)
 from prefix_shared_branch_amd import inputs  # noqa: E402
 
 METRIC = "replayed response tokens/s (fwd+bwd) at prompt P; % bf16 MFMA peak; loss GB/s"
-PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
+PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s (at the 2.4 GHz peak clock)
 PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
+PEAK_CLOCK_GHZ = 2.4
+# Shader clock the chip holds under these MFMA-dense kernels: SQ_BUSY_CYCLES over the dispatch time
+# in the SQ counter runs of the attention kernels (1.68-1.77 GHz measured); the MFMA pipes peak at
+# PEAK_BF16 * SUSTAINED_CLOCK_GHZ / PEAK_CLOCK_GHZ at that clock.
+SUSTAINED_CLOCK_GHZ = 1.75
 
 
 def parse():
@@ -149,12 +154,12 @@ def flops(cfg, R):
     """Algorithmic and executed MFMA flops of one response (per visible pair and query head)."""
     pairs = R * cfg.P + R * (R + 1) // 2
     d, dv = cfg.Dqk, cfg.Dv
-    prompt_pairs = R * cfg.P
     alg = 6 * (d + dv) * pairs * cfg.Hq
-    hilo = 1 if cfg.mla else 2   # the latent-KV dK/dV kernel runs its fp16 products once
+    # each product runs once (the dV / dK products in single-pass fp16): 1.5x the algorithmic work
+    # at d = dv (2304 flops per pair-head at D = 128)
     executed = (2 * (d + dv) * pairs             # forward: S, PV
                 + (2 * d + 2 * dv) * pairs       # dK/dV kernel: S, dP recomputed
-                + hilo * (2 * dv + 2 * d) * prompt_pairs + (2 * dv + 2 * d) * (pairs - prompt_pairs)  # dV, dK
+                + (2 * dv + 2 * d) * pairs       # dK/dV kernel: dV, dK
                 + (4 * d + 2 * dv) * pairs) * cfg.Hq   # dQ kernel: S, dP, dQ
     return alg, executed, pairs
 
@@ -384,6 +389,11 @@ def main():
             "attn_alg_TFLOPs": alg / ((t_fwd + t_bwd) * 1e-3) / 1e12,
             "attn_alg_frac_peak": alg / ((t_fwd + t_bwd) * 1e-3) / PEAK_BF16,
             "attn_exec_TFLOPs": exe / ((t_fwd + t_bwd) * 1e-3) / 1e12,
+            "attn_exec_over_alg": exe / alg,
+            # executed rate over the MFMA peak at the sustained clock: an estimate of the share of
+            # cycles the MFMA pipes are busy (the SQ counter runs measure it per kernel)
+            "mfma_busy_est": exe / ((t_fwd + t_bwd) * 1e-3) / (PEAK_BF16 * SUSTAINED_CLOCK_GHZ / PEAK_CLOCK_GHZ),
+            "sustained_clock_GHz": SUSTAINED_CLOCK_GHZ,
             "fwd_ms_per_group": t_fwd, "bwd_ms_per_group": t_bwd, "loss_ms_per_group": t_loss,
             "fwd_alg_TFLOPs": fwd_alg / (t_fwd * 1e-3) / 1e12,
             "loss_GBps": loss_bytes / (t_loss * 1e-3) / 1e9,

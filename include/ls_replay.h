@@ -47,7 +47,8 @@ typedef enum {
  *  P        prompt length (>= 0; 0 gives plain causal attention over the response).
  *  Hq, Hkv  query / key-value heads, Hq % Hkv == 0; query head h reads kv head h / (Hq/Hkv).
  *  Dqk, Dv  head dims; supported pairs: (64,64), (128,128), and (576,512) for latent KV (the
- *           absorbed-latent attention of the GLM run's latent pages, LongStraw study notes §3-3).
+ *           absorbed-latent attention over the GLM run's latent pages, LongStraw study notes §3-1 overview
+ *           table and §3-2 (1), (5)).
  *           Other pairs: LS_ERR_UNSUPPORTED.
  *  ldk, ldv elements between consecutive tokens of K and of V, for prompt and suffix alike;
  *           element (token j, kv head k, dim d) sits at K[j*ldk + k*Dqk + d] and

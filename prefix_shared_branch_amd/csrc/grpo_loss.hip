@@ -63,9 +63,8 @@ __device__ __forceinline__ float row_scalar(const GrpoArgs& a, int64_t row, floa
 }
 
 // Vector path: V % 8 == 0, 16-byte aligned rows; NCH 16-byte chunks per thread in registers.
-// Rows are read through a buffer resource (one VGPR offset per thread, the chunk column in
-// the SGPR offset) so no per-chunk 64-bit addresses stay live; chunks past the row end are
-// masked to -inf after the load and never stored.
+// Rows are read through a buffer resource over the row (no per-chunk 64-bit addresses stay live);
+// chunks past the row end read zeros, are masked to -inf after the load and never stored.
 // A row fills most of a CU's registers at the large vocabularies, so one workgroup per CU loops
 // over rows (row = blockIdx.x, + gridDim.x, ...). In the gradient pass the registers of chunk j
 // are reloaded with chunk j of the next row as soon as chunk j's dlogits are stored: the next
@@ -83,11 +82,20 @@ __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(a.logits + r * (int64_t)a.V), 0, a.V * 2, kBufferWord3);
   };
 
+  // 16 bytes of chunk j of a row for this thread. The whole byte offset goes in the VGPR offset,
+  // which the buffer range check covers (the SGPR offset is not range-checked), so chunks past the
+  // row end read zeros without touching memory. The offset is materialised at the load (opaque z)
+  // rather than hoisted out of the row loop as one live register per chunk.
+  auto ld_chunk = [&](__amdgpu_buffer_rsrc_t r, int j, int z) {
+    int o = voff + j * NT * 16 + z;
+    asm volatile("" : "+v"(o));
+    return __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, kSlc);
+  };
   u32x4 v[NCH];
   {
     const __amdgpu_buffer_rsrc_t src = row_src(row);
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(src, voff, j * NT * 16, kSlc);
+    for (int j = 0; j < NCH; ++j) v[j] = ld_chunk(src, j, 0);
   }
   for (;;) {
     // chunk offsets and chunk-validity masks are formed from a value the compiler cannot see
@@ -160,14 +168,14 @@ __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
           for (int q = 0; q < 4; ++q) o[q] = (q == qy) ? ((o[q] & keep) | ins) : o[q];
         }
         if (cj < nch) __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst + voff + j * NT * 16));
-        v[j] = __builtin_amdgcn_raw_buffer_load_b128(nsrc, voff, zoff + j * NT * 16, kSlc);
+        v[j] = ld_chunk(nsrc, j, zoff);
         // chunk by chunk: the reload of chunk j is not hoisted above the output of chunks < j,
         // which would keep two rows' chunks live at once
         __builtin_amdgcn_sched_barrier(0);
       }
     } else if (more) {
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(nsrc, voff, zoff + j * NT * 16, kSlc);
+      for (int j = 0; j < NCH; ++j) v[j] = ld_chunk(nsrc, j, zoff);
     }
     if (!more) break;
     row = next;

@@ -1,5 +1,5 @@
 // Replay attention backward for latent-KV heads on gfx950 (LongStraw study notes, §2-1 step 4 and
-// §2-2; the latent-KV layout of the GLM run, §3-3): Dqk = 576, Dv = 512, one kv head, V = the
+// §2-2; the latent-KV pages of the GLM run: the §3-1 overview table and §3-2 (1), (5)): Dqk = 576, Dv = 512, one kv head, V = the
 // leading 512 dims of every K row. With P = exp(S scale - LSE), dP = dO V^T, Delta = rowsum(dO * O)
 // and dS = P (dP - Delta):
 //   dV_j += sum_rows P_rj dO_r,  dK_j += scale sum_rows dS_rj Q_r,  dQ_r = scale sum_j dS_rj K_j.

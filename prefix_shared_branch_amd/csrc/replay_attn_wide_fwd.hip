@@ -1,5 +1,5 @@
 // Replay attention forward for latent-KV heads on gfx950 (LongStraw study notes, §2-1 step 4 and
-// §3-2 (2)/(4); the latent-KV layout of the GLM run, §3-3): Dqk = 576, Dv = 512, one kv head, and
+// §3-2 (2)/(4); the latent-KV pages of the GLM run: the §3-1 overview table and §3-2 (1), (5)): Dqk = 576, Dv = 512, one kv head, and
 // V is the leading 512 dims of every K row (same rows, same row stride), so a single K tile in LDS
 // serves both products.
 //

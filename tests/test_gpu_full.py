@@ -2,10 +2,13 @@
 
 Replay attention at P = 262,144 and P = 1,048,576 (LongStraw study notes §2-1 step 4, §3-2 (2)/(4)).
 
-* **Short responses.** The GPU runs every head of the configuration. The oracle recomputes kv head 0
-  and its query heads in full: O, LSE, dQ, dKs, dVs, and the prompt dK/dV accumulators. Heads are
-  independent, and a response's first rows form an exact sub-problem, since row t sees only suffix
-  keys up to t.
+* **Short responses.** The GPU runs every head of the configuration. The oracle recomputes the first
+  and the last kv head and their query heads in full: O, LSE, dQ, dKs, dVs, and the prompt dK/dV
+  accumulators element by element (the last kv head's accumulator rows sit at the highest
+  addresses). Heads are independent, and a response's first rows form an exact sub-problem, since
+  row t sees only suffix keys up to t. At the Million-token prompt 64 rows are checked: 320
+  GQA-packed rows, ten 32-row steps of the dK/dV kernel's sweep, so its load ring turns over
+  several times.
 * **Full response.** Response 0 of the Million workload runs in the launch configuration the
   benchmark times: one call per 4,096-token response, with exact prompt gradients.
   * O, LSE and dQ are checked on sampled rows. Each row depends on that row alone.
@@ -26,14 +29,18 @@ f64 = inputs.bf16_bits_to_f64
 
 
 class Prompt:
-    """Full-size prompt K/V of a config: device copies (all heads) and float64 kv-head-0 slices."""
+    """Full-size prompt K/V of a config: device copies (all heads) and float64 slices of the first
+    and the last kv head."""
 
     def __init__(self, cfg):
         import torch
         self.cfg = cfg
         kp, vp = inputs.prompt_k(cfg), inputs.prompt_v(cfg)
         self.kp, self.vp = dev_bf16(kp), dev_bf16(vp)
-        self.kp0, self.vp0 = f64(kp[:, :1, :]), f64(vp[:, :1, :])
+        self.heads = sorted({0, cfg.Hkv - 1})
+        self.kph = {k: f64(kp[:, k:k + 1, :]) for k in self.heads}
+        self.vph = {k: f64(vp[:, k:k + 1, :]) for k in self.heads}
+        self.kp0, self.vp0 = self.kph[0], self.vph[0]
         del kp, vp
         self.torch = torch
 
@@ -54,28 +61,34 @@ class Prompt:
         return bits, dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp)
 
 
-def _head0_operands(cfg, bits):
+def _head_operands(cfg, bits, k):
+    """float64 operands of kv head k: its g query heads, its keys / values, their output gradients."""
     g = cfg.Hq // cfg.Hkv
-    return (f64(bits["q"][:, :g, :]), f64(bits["ks"][:, :1, :]), f64(bits["vs"][:, :1, :]),
-            f64(bits["do"][:, :g, :]), g)
+    qs = slice(k * g, (k + 1) * g)
+    return (f64(bits["q"][:, qs, :]), f64(bits["ks"][:, k:k + 1, :]), f64(bits["vs"][:, k:k + 1, :]),
+            f64(bits["do"][:, qs, :]), g)
 
 
 def _check_short(pr, r):
     cfg = pr.cfg
     bits, got = pr.run(r)
-    Q, Ks, Vs, dO, g = _head0_operands(cfg, bits)
     cu = [0, r]
-    O, LSE = attn.replay_attn_fwd(pr.kp0, pr.vp0, Q, Ks, Vs, cu, cfg.scale)
-    dKp, dVp = np.zeros(pr.kp0.shape), np.zeros(pr.vp0.shape)
-    dQ, dKs, dVs = attn.replay_attn_bwd(pr.kp0, pr.vp0, Q, Ks, Vs, dO, cu, cfg.scale, dKp, dVp)
-    check_bf16_out(host_f64(got["O"][:, :g]), O, "O")
-    lse = host_f64(got["LSE"][:g])
-    assert np.max(np.abs(lse - LSE)) <= 1e-4, np.max(np.abs(lse - LSE))
-    check_bf16_out(host_f64(got["dQ"][:, :g]), dQ, "dQ")
-    check_bf16_out(host_f64(got["dKs"][:, :1]), dKs, "dKs")
-    check_bf16_out(host_f64(got["dVs"][:, :1]), dVs, "dVs")
-    check_fp32_accum(host_f64(got["dKp"][:, :1]), dKp, "dKp")
-    check_fp32_accum(host_f64(got["dVp"][:, :1]), dVp, "dVp")
+    for k in pr.heads:
+        print(f"[parity] P={cfg.P} rows={r} kv head {k}", flush=True)
+        Q, Ks, Vs, dO, g = _head_operands(cfg, bits, k)
+        qs, ks = slice(k * g, (k + 1) * g), slice(k, k + 1)
+        kp, vp = pr.kph[k], pr.vph[k]
+        O, LSE = attn.replay_attn_fwd(kp, vp, Q, Ks, Vs, cu, cfg.scale)
+        dKp, dVp = np.zeros(kp.shape), np.zeros(vp.shape)
+        dQ, dKs, dVs = attn.replay_attn_bwd(kp, vp, Q, Ks, Vs, dO, cu, cfg.scale, dKp, dVp)
+        check_bf16_out(host_f64(got["O"][:, qs]), O, "O")
+        lse = host_f64(got["LSE"][qs])
+        assert np.max(np.abs(lse - LSE)) <= 1e-4, np.max(np.abs(lse - LSE))
+        check_bf16_out(host_f64(got["dQ"][:, qs]), dQ, "dQ")
+        check_bf16_out(host_f64(got["dKs"][:, ks]), dKs, "dKs")
+        check_bf16_out(host_f64(got["dVs"][:, ks]), dVs, "dVs")
+        check_fp32_accum(host_f64(got["dKp"][:, ks]), dKp, f"dKp kv head {k}")
+        check_fp32_accum(host_f64(got["dVp"][:, ks]), dVp, f"dVp kv head {k}")
 
 
 def test_long_prompt_short_response():
@@ -89,14 +102,14 @@ def million():
 
 
 def test_million_prompt_short_response(million):
-    _check_short(million, 16)
+    _check_short(million, 64)
 
 
 def test_million_full_response_sampled_rows_and_column_sums(million):
     pr, cfg = million, million.cfg
     r = int(inputs.response_lengths(cfg)[0])
     bits, got = pr.run(r)
-    Q, Ks, Vs, dO, g = _head0_operands(cfg, bits)
+    Q, Ks, Vs, dO, g = _head_operands(cfg, bits, 0)
     rows = np.array([0, 63, 2047, r - 1])
     O, LSE = attn.replay_attn_fwd(pr.kp0, pr.vp0, Q, Ks, Vs, [0, r], cfg.scale, rows=rows)
     check_bf16_out(host_f64(got["O"][rows, :g]), O[rows], "O rows")
@@ -114,3 +127,26 @@ def test_million_full_response_sampled_rows_and_column_sums(million):
     for k in range(cfg.Hkv):
         rel = np.linalg.norm(have[k] - want[k]) / np.linalg.norm(want[k])
         assert rel <= 1e-3, (k, rel)
+
+    # Key-gradient identities, every kv head, over the prompt and the response keys. Each row's dS
+    # sums to zero over its keys (its softmax weights sum to one and Delta = dO . O), so
+    # sum_j dK_j = 0. And dK = scale dS^T Q with dQ = scale dS K gives dK^T K = Q^T dQ, summed over
+    # the kv head's query heads. The first bounds the accumulated sums against their absolute sums
+    # (each key's error enters alone, a wrong tile shows), the second fixes their scale.
+    import torch
+    Qd = dev_bf16(bits["q"]).double().reshape(r, cfg.Hkv, g, cfg.Dqk)
+    dQd = got["dQ"].double().reshape(r, cfg.Hkv, g, cfg.Dqk)
+    for k in range(cfg.Hkv):
+        dkp = got["dKp"][:, k, :].double()
+        dks = got["dKs"][:, k, :].double()
+        tot = dkp.sum(dim=0) + dks.sum(dim=0)
+        mag = dkp.abs().sum(dim=0) + dks.abs().sum(dim=0)
+        e1 = float(torch.linalg.norm(tot) / torch.linalg.norm(mag))
+        lhs = (dkp.T.contiguous() @ pr.kp[:, k, :].double().contiguous()
+               + dks.T.contiguous() @ dev_bf16(bits["ks"][:, k, :]).double().contiguous())
+        qk = Qd[:, k].reshape(r * g, cfg.Dqk)
+        rhs = qk.T.contiguous() @ dQd[:, k].reshape(r * g, cfg.Dqk).contiguous()
+        e2 = float(torch.linalg.norm(lhs - rhs) / torch.linalg.norm(rhs))
+        print(f"[parity] kv head {k}: |sum dK| / sum |dK| = {e1:.2e}, dK^T K vs Q^T dQ rel {e2:.2e}", flush=True)
+        assert e1 <= 1e-4, (k, e1)
+        assert e2 <= 2e-2, (k, e2)

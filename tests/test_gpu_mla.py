@@ -1,6 +1,6 @@
 """GPU parity of replay attention on latent-KV heads (Dqk 576, Dv 512, one kv head, V = the leading
 512 dims of every K row) against the fp64 oracle (LongStraw study notes §2-1 step 4, §3-2 (2)/(4);
-the latent-KV pages of the GLM run, §3-3). Sizes span several query and key tiles with ragged tails."""
+the latent-KV pages of the GLM run: the §3-1 overview table and §3-2 (1), (5)). Sizes span several query and key tiles with ragged tails."""
 import numpy as np
 import pytest
 

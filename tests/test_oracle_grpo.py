@@ -147,3 +147,36 @@ def test_equal_rewards_zero_gradient():
     old = scipy.special.log_softmax(x, 1)[np.arange(x.shape[0]), y] + 0.7
     loss, dl, _, _ = grpo.grpo_token_loss(x, y, old, R, [1.0, 1.0, 1.0], 3, 0.2, 0, 3)
     assert loss == 0.0 and np.all(dl == 0.0)
+
+
+def test_abs_term_scale_closed_forms():
+    """S_abs = sum_i (1/(G R_i)) sum_t |term_it|, the scale of the loss bar, pinned by hand values.
+
+    rho = 1: every term is A_i, so S_abs = (1/G) sum_i |A_i|; with G = 2 and rewards {0, 1} the
+    population std is 1/2 and |A_i| = 0.5 / (0.5 + 1e-6). Clipped tokens: uniform logits over V = 4
+    give logp = -log 4 exactly, and old = logp - log(rho) sets each token's ratio; with eps = 0.2 the
+    terms are min(rho A, clip(rho) A). Unequal lengths catch a dropped 1/R_i, the clipped tokens a
+    dropped clip, the negative advantage a dropped absolute value."""
+    a = 0.5 / (0.5 + 1e-6)
+    R = np.array([3, 5])
+    rewards = np.array([0.0, 1.0])
+    g = np.random.default_rng(7)
+    x = g.standard_normal((8, 9))
+    y = g.integers(0, 9, size=8)
+    lp = grpo.token_logp(x, y)
+    s = grpo.abs_term_scale(x, y, lp, R, rewards, 2, 0.2, 0, 2)
+    assert abs(s - a) < 1e-12 * a
+    # response 0 (reward 1, A = +a): rho = 1.5 (clipped: 1.2 a), 0.5 (0.5 a)
+    # response 1 (reward 0, A = -a): rho = 0.5 (clipped: -0.8 a), 1.5 (-1.5 a), 1.0 (-a)
+    R = np.array([2, 3])
+    rewards = np.array([1.0, 0.0])
+    rho = np.array([1.5, 0.5, 0.5, 1.5, 1.0])
+    u = np.zeros((5, 4))
+    y = np.array([0, 3, 1, 2, 0])
+    old = -np.log(4.0) - np.log(rho)
+    want_all = 0.5 * ((1.2 + 0.5) * a / 2 + (0.8 + 1.5 + 1.0) * a / 3)
+    s = grpo.abs_term_scale(u, y, old, R, rewards, 2, 0.2, 0, 2)
+    assert abs(s - want_all) < 1e-12 * want_all, (s, want_all)
+    s1 = grpo.abs_term_scale(u[2:], y[2:], old[2:], R, rewards, 2, 0.2, 1, 1)
+    want_1 = 0.5 * (0.8 + 1.5 + 1.0) * a / 3
+    assert abs(s1 - want_1) < 1e-12 * want_1, (s1, want_1)
