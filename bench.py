@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--workload", default="million", choices=["tiny", "mid", "long", "million", "mla"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = automatic)")
+    ap.add_argument("--no-memory-receipt", action="store_true",
+                    help="skip the peak-memory receipt (G = 2 vs G = 8 at mid, G = 2 vs G = 16 at million)")
+    ap.add_argument("--memory-receipt-only", action="store_true", help="only run the peak-memory receipt")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of known size (HBM counter calibration)")
     return ap.parse_args()
@@ -148,6 +151,66 @@ class Workload:
         self.loss.zero_()
         for i in range(self.G):
             self.response(i, times)
+
+
+def memory_receipt(cfg, group_sizes):
+    """Peak device memory of serial replay with each response's buffers alive only during its own
+    replay (the response lifetime of the LongStraw study notes, §1-1 lifetime table and §2-1: the
+    live graph is bounded by the current suffix). Per group size G: zero the resident accumulators,
+    then for each of the G responses create its inputs (queries, suffix K/V, output gradient, logits,
+    targets, old log-probs), its outputs and workspaces, run forward, loss and backward, and free
+    them all. Resident across the group: prompt K/V and the fp32 prompt-gradient accumulators. The
+    peak should not grow with G."""
+    import torch
+    from prefix_shared_branch_amd import lsreplay as L
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    kp = to_dev(inputs.prompt_k(cfg))
+    vp = kp[:, :, :cfg.Dv] if cfg.mla else to_dev(inputs.prompt_v(cfg))
+    dkp = torch.zeros(cfg.P, cfg.Hkv, cfg.Dqk, dtype=torch.float32, device="cuda")
+    dvp = torch.zeros(cfg.P, cfg.Hkv, cfg.Dv, dtype=torch.float32, device="cuda")
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    R_all = inputs.response_lengths(cfg)
+    resident = torch.cuda.memory_allocated()
+    out = {"workload": cfg.name, "resident_GiB": resident / 2**30, "peak_GiB": {}, "response_buffers_GiB": {}}
+    for G in group_sizes:
+        R = R_all[:G]
+        rewards = inputs.rewards(cfg)[:G]
+        cu = inputs.cu_seqlens(R_all)
+        dkp.zero_()
+        dvp.zero_()
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        biggest = 0
+        for i in range(G):
+            r = int(R[i])
+            t0 = int(cu[i])
+            q = to_dev(inputs.suffix_q(cfg, t0, t0 + r))
+            ks = to_dev(inputs.suffix_k(cfg, t0, t0 + r))
+            vs = ks[:, :, :cfg.Dv] if cfg.mla else to_dev(inputs.suffix_v(cfg, t0, t0 + r))
+            do = to_dev(inputs.suffix_do(cfg, t0, t0 + r))
+            lg = to_dev(inputs.logits(cfg, i, 0, r))
+            y = torch.from_numpy(inputs.targets(cfg, i, r)).cuda()
+            old = torch.from_numpy(inputs.old_logp_noise(cfg, i, r)).cuda()
+            for r0 in range(0, r, 256):   # old = current log-probs + noise (input synthesis)
+                old[r0:r0 + 256] += torch.log_softmax(lg[r0:r0 + 256].float(), dim=1).gather(
+                    1, y[r0:r0 + 256, None].long())[:, 0]
+            lo = torch.empty(r, cfg.Hq, cfg.Dv, dtype=torch.bfloat16, device="cuda")
+            o, lse = L.ls_replay_attn_fwd(q, ks, vs, kp, vp, [0, r], cfg.scale, o_lo=lo)
+            dl = L.ls_grpo_token_loss(lg, y, old, R, rewards, cfg.eps, i, 1, loss)
+            L.ls_replay_attn_bwd(q, ks, vs, kp, vp, [0, r], o, lse, do, dkp, dvp, cfg.scale, o_lo=lo)
+            torch.cuda.synchronize()
+            biggest = max(biggest, torch.cuda.memory_allocated() - resident)
+            del q, ks, vs, do, lg, y, old, lo, o, lse, dl
+        torch.cuda.synchronize()
+        out["peak_GiB"][str(G)] = torch.cuda.max_memory_allocated() / 2**30
+        out["response_buffers_GiB"][str(G)] = biggest / 2**30
+        log(f"memory receipt {cfg.name}: G={G} peak {out['peak_GiB'][str(G)]:.3f} GiB")
+    gs = [str(g) for g in group_sizes]
+    out["peak_delta_GiB"] = out["peak_GiB"][gs[-1]] - out["peak_GiB"][gs[0]]
+    del kp, vp, dkp, dvp, loss
+    torch.cuda.empty_cache()
+    return out
 
 
 def flops(cfg, R):
@@ -306,6 +369,10 @@ def main():
     L.lib()   # fail loudly if the HIP library is missing
     cfg = inputs.CONFIGS[args.workload]
     torch.cuda.set_device(0)
+    if args.memory_receipt_only:
+        print(json.dumps([memory_receipt(inputs.CONFIGS["mid"], [2, 8]),
+                          memory_receipt(inputs.CONFIGS["million"], [2, 16])]), flush=True)
+        return
     wl = Workload(cfg)
     for _ in range(args.warmup):
         wl.step()
@@ -403,15 +470,21 @@ def main():
             "scoring_loss_ms_per_group": t_score,
             "scoring_loss_GBps": score_bytes / (t_score * 1e-3) / 1e9,
             "lmhead": lm,
-            "peak_mem_GiB": torch.cuda.max_memory_allocated() / 2**30,
+            # the timed run keeps every response's logits resident (input generation stays out of the
+            # timed region); memory_receipt below measures the per-response lifetime instead
+            "peak_mem_GiB_timed_run": torch.cuda.max_memory_allocated() / 2**30,
             "pages_context": "2.1M token positions on eight H20 GPUs (whole model, end to end; not comparable)",
         },
     }
+    del wl
+    torch.cuda.empty_cache()
+    if not args.no_memory_receipt:
+        # outside the timed region: each response's buffers live only during its own replay
+        out["detail"]["memory_receipt"] = [memory_receipt(inputs.CONFIGS["mid"], [2, 8]),
+                                           memory_receipt(inputs.CONFIGS["million"], [2, 16])]
     if not args.no_cpu_baseline:
         # about 10-30 s of oracle work: the sample shrinks as the prompt grows
         rows = args.cpu_rows or int(min(256, max(1, (1 << 25) // max(1, cfg.P))))
-        del wl
-        torch.cuda.empty_cache()
         log(f"cpu baseline: oracle on {rows} rows")
         out["cpu_baseline"] = cpu_baseline(cfg, rows)
     print(json.dumps(out), flush=True)
