@@ -207,6 +207,26 @@ int ls_grpo_token_loss(void* stream, int32_t V, int32_t G,
                        float* logp_out, uint8_t* clipped_out,
                        void* workspace, size_t workspace_bytes);
 
+/* ls_grpo_token_loss without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Arguments,
+ * outputs and errors are those of ls_grpo_token_loss, and so are the kernels and every result. The
+ * per-row loss terms that the workspace held go to a fixed array of LS_NOALLOC_MAX_ROWS floats
+ * (4 MiB) in the library's device memory, one per GPU, held until the process ends. This call
+ * allocates no device memory; its first call on a device looks the array's address up (a HIP symbol
+ * query; a failure returns LS_ERR_HIP).
+ *  Rows per call (the summed R_i of the selected responses) at most LS_NOALLOC_MAX_ROWS; more
+ *  returns LS_ERR_WORKSPACE before anything is launched.
+ * Every call on one GPU uses that GPU's array and leaves the last call's terms in it. Calls that
+ * overlap on one GPU (several streams, or host threads without ordering) race on it: the caller
+ * orders them. */
+#define LS_NOALLOC_MAX_ROWS 1048576
+int ls_grpo_token_loss_noalloc(void* stream, int32_t V, int32_t G,
+                               const int32_t* R, const float* rewards,
+                               float eps, int32_t first, int32_t count,
+                               const void* logits, const int32_t* targets, const float* old_logp,
+                               void* dlogits, float* loss_accum,
+                               float* logp_out, uint8_t* clipped_out);
+
 /* Workspace bytes for ls_grpo_lmhead_loss over T rows (written to *bytes): the logits and
  * dlogits of one chunk of at most 2048 tokens plus per-row loss terms. */
 int ls_grpo_lmhead_workspace_bytes(int64_t T, int32_t V, int32_t d, size_t* bytes);

@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "liblsreplay.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_SOURCES = ["grpo_loss.hip", "replay_attn_fwd.hip", "replay_attn_bwd.hip", "replay_attn_dq.hip", "replay_attn_dkdv.hip", "pack.hip",
-               "replay_attn_wide_fwd.hip", "replay_attn_wide_bwd.hip"]
+               "replay_attn_wide_fwd.hip", "replay_attn_wide_bwd.hip", "noalloc.hip"]
 CXX_SOURCES = ["api.cpp", "attn_plan.cpp", "timer.cpp", "lmhead.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 # the packed-fp32 feature stays off: every v_pk_*_f32 is left out of the kernels

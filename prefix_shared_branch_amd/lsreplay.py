@@ -17,9 +17,11 @@ LIB_PATH = os.path.join(_HERE, "liblsreplay.so")
 
 LS_OK, LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP = 0, -1, -2, -3, -4
 LS_MAX_RESPONSES_PER_CALL = 64
+LS_NOALLOC_MAX_ROWS = 1048576
 EXPORTED = ("ls_replay_attn_workspace_bytes", "ls_replay_attn_fwd", "ls_replay_attn_bwd",
             "ls_replay_attn_block_workspace_bytes", "ls_replay_attn_fwd_block", "ls_replay_attn_bwd_block",
-            "ls_grpo_workspace_bytes", "ls_grpo_token_loss", "ls_grpo_lmhead_workspace_bytes",
+            "ls_grpo_workspace_bytes", "ls_grpo_token_loss", "ls_grpo_token_loss_noalloc",
+            "ls_grpo_lmhead_workspace_bytes",
             "ls_grpo_lmhead_loss", "ls_status_string", "ls_kernel_timer_start", "ls_kernel_timer_stop")
 LS_KERNEL_ATTN_FWD, LS_KERNEL_DKDV_PROMPT, LS_KERNEL_DQ, LS_KERNEL_GRPO_ROWS = 0, 1, 2, 3
 
@@ -71,6 +73,8 @@ def lib():
         L.ls_grpo_workspace_bytes.argtypes = [i64, i32, ctypes.POINTER(sz)]
         L.ls_grpo_token_loss.restype = ctypes.c_int
         L.ls_grpo_token_loss.argtypes = [vp, i32, i32, pi32, pf32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz]
+        L.ls_grpo_token_loss_noalloc.restype = ctypes.c_int
+        L.ls_grpo_token_loss_noalloc.argtypes = [vp, i32, i32, pi32, pf32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         L.ls_grpo_lmhead_workspace_bytes.restype = ctypes.c_int
         L.ls_grpo_lmhead_workspace_bytes.argtypes = [i64, i32, i32, ctypes.POINTER(sz)]
         L.ls_grpo_lmhead_loss.restype = ctypes.c_int
@@ -322,6 +326,32 @@ def ls_grpo_token_loss(logits, targets, old_logp, R, rewards, eps, first, count,
     _check("ls_grpo_token_loss", lib().ls_grpo_token_loss(
         _stream(), V, len(Ra), Rp, rp, float(eps), int(first), int(count), _ptr(logits), _ptr(targets),
         _ptr(old_logp), _ptr(dlogits), _ptr(loss_accum), _ptr(logp_out), _ptr(clipped_out), _ptr(ws), ws.numel()))
+    return dlogits
+
+
+def ls_grpo_token_loss_noalloc(logits, targets, old_logp, R, rewards, eps, first, count, loss_accum, dlogits,
+                               logp_out=None, clipped_out=None):
+    """ls_grpo_token_loss with the library's fixed per-GPU scratch array instead of a workspace: the
+    caller passes every output (dlogits, or None for scoring only); nothing is allocated."""
+    import torch
+    T, V = logits.shape
+    _check_tensor(logits, "logits", torch.bfloat16)
+    _check_tensor(targets, "targets", torch.int32, (T,))
+    _check_tensor(old_logp, "old_logp", torch.float32, (T,))
+    _check_tensor(loss_accum, "loss_accum", torch.float32)
+    if not logits.is_contiguous():
+        raise ValueError("logits must be contiguous")
+    if dlogits is not None:
+        _check_tensor(dlogits, "dlogits", torch.bfloat16, (T, V))
+    if logp_out is not None:
+        _check_tensor(logp_out, "logp_out", torch.float32, (T,))
+    if clipped_out is not None:
+        _check_tensor(clipped_out, "clipped_out", torch.uint8, (T,))
+    Ra, Rp = _i32_array(R)
+    ra, rp = _f32_array(rewards)
+    _check("ls_grpo_token_loss_noalloc", lib().ls_grpo_token_loss_noalloc(
+        _stream(), V, len(Ra), Rp, rp, float(eps), int(first), int(count), _ptr(logits), _ptr(targets),
+        _ptr(old_logp), _ptr(dlogits), _ptr(loss_accum), _ptr(logp_out), _ptr(clipped_out)))
     return dlogits
 
 
