@@ -8,7 +8,7 @@
 // attention partials of prompt pages held by different owners (LongStraw study notes,
 // §3-2 (2): cross-rank log-sum-exp and output merge). S is chosen to fill the chip.
 //
-// dK/dV kernel: one workgroup owns kDKTile keys of one kv head, for every prompt key tile
+// dK/dV kernel: one workgroup owns a tile of keys of one kv head, for every prompt key tile
 // (exact prompt-gradient mode only) and every response's suffix key tile.
 #include <algorithm>
 #include <cstring>
@@ -19,7 +19,9 @@ namespace lsr {
 
 namespace {
 constexpr int kKTile = 64;    // keys per forward / dQ tile
-constexpr int kDKTileStd = 128;  // keys per dK/dV workgroup (latent-KV heads: kDKTileWide)
+constexpr int kDKTilePrompt = 256;  // keys per dK/dV workgroup over the prompt at head dim 128
+                                    // (64: kDKTileResp; latent-KV heads: kDKTileWide)
+constexpr int kDKTileResp = 128;    // keys per dK/dV workgroup over a response's own keys
 constexpr int kTargetBlocks = 2048;
 constexpr int kMinTilesPerSplit = 8;
 constexpr int kMaxSplits = 64;
@@ -36,7 +38,8 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
   const int g = Hq / Hkv;
   const long long T = cu[n_resp];
   const int kQTile = wide ? (which == 0 ? kQTileFwdWide : kQTileDqWide) : (which == 0 ? kQTileFwd : kQTileDq);
-  const int kDKTile = wide ? kDKTileWide : kDKTileStd;
+  const int kDKTileP = wide ? kDKTileWide : (Dqk == 128 ? kDKTilePrompt : kDKTileResp);
+  const int kDKTileR = wide ? kDKTileWide : kDKTileResp;
   int qt = 0, kt = 0, sp = 0;
   for (int i = 0; i < n_resp; ++i) {
     pl->tile0[i] = qt;
@@ -45,7 +48,7 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
     const long long R = cu[i + 1] - cu[i];     // query rows
     const long long Rk = kcu[i + 1] - kcu[i];  // response keys (>= R: a block's keys start earlier)
     qt += (int)((R * g + kQTile - 1) / kQTile);
-    kt += (int)((Rk + kDKTile - 1) / kDKTile);
+    kt += (int)((Rk + kDKTileR - 1) / kDKTileR);
     sp += (int)((Rk + kKTile - 1) / kKTile * kKTile);
   }
   for (int i = n_resp; i <= kMaxResp; ++i) {
@@ -57,7 +60,7 @@ bool plan_attn(int which, int P, int Hq, int Hkv, int Dqk, int Dv, int n_resp, c
   pl->tpad = sp;
   pl->qtiles = qt;
   pl->ptiles = (P + kKTile - 1) / kKTile;
-  pl->ktiles_prompt = which == 1 ? (P + kDKTile - 1) / kDKTile : 0;
+  pl->ktiles_prompt = which == 1 ? (P + kDKTileP - 1) / kDKTileP : 0;
 
   int S = 1;
   const long long w0 = (long long)qt * Hkv;

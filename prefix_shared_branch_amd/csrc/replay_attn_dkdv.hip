@@ -6,20 +6,21 @@
 // With P = exp(S scale - LSE), dP = dO V^T, Delta = rowsum(dO * O), dS = P (dP - Delta):
 //   dV_j += sum_rows P_rj dO_r,   dK_j += scale sum_rows dS_rj Q_r.
 //
-// replay_bwd_dkdv: key-tile owner. One workgroup = 4 waves x 32 keys of one kv head (one wave per
-// SIMD); the wave keeps its keys' K and V fragments (AGPRs) and dK^T, dV^T accumulators for the
-// whole sweep over every query row that sees those keys, 32 GQA-packed rows per step, software
-// pipelined so that step j's dV / dK products overlap step j + 1's S / dP and softmax. The rows
-// were repacked per kv head before the launch (pack.hip): row-major Q and dO (A operands of
-// S = Q K^T and dP = dO V^T) and dimension-major, slot-permuted Q^T and dO^T (A operands of
-// dV^T += dO^T P and dK^T += Q^T dS, whose B operands come straight from the S / dP accumulators),
-// plus each row's LSE and Delta as bf16 row terms (pack_rowext) that one 32x32x8 MFMA each turns
-// into the starting values of the S and dP accumulators. Per step all of them stream global -> LDS
-// by direct DMA into
-// a three-stage ring of XOR-swizzled tiles, so every MFMA operand is one 16-byte LDS read.
+// replay_bwd_dkdv: key-tile owner. One workgroup = 8 waves x 32 keys of one kv head, two waves per
+// SIMD; each wave keeps its keys' K and V fragments and its dK^T, dV^T accumulators in registers for
+// the whole sweep over every query row that sees those keys, 32 GQA-packed rows per step. While one
+// wave of a SIMD forms P and dS on the VALU, the other issues its MFMAs. The rows were repacked per
+// kv head before the launch (pack.hip): row-major Q and dO (A operands of S = Q K^T and
+// dP = dO V^T) and dimension-major, slot-permuted Q^T and dO^T (A operands of dV^T += dO^T P and
+// dK^T += Q^T dS, whose B operands come straight from the S / dP accumulators), plus each row's LSE
+// and Delta as bf16 row terms (pack_rowext) that one 32x32x8 MFMA each turns into the starting
+// values of the S and dP accumulators. Per step all of them stream global -> LDS by direct loads
+// into a three-stage ring of XOR-swizzled tiles shared by the eight waves, so every MFMA operand is
+// one 16-byte LDS read.
 // The dV / dK products run in fp16 (11 significant bits; bf16's 8 would cost ~1.7e-3 relative error
 // in the fp32 sums over 10^6-10^7 terms, fp16 ~2e-4) with exact power-of-two scaling so every
-// operand sits in fp16's normal range: 2^15 P (folded into the exponent), dO s_dO and Q s_Q
+// operand sits in fp16's normal range: 2^15 P (folded into the exponent; dS is formed from the same
+// fp16 2^15 P), dO s_dO and Q s_Q
 // (s from max |dO|, max |Q|), and 2^15 P (dP - Delta) s_dS with s_dS from the bound
 // |dP - Delta| <= 2 max_r |dO_r| max_j |V_j| (pack.hip computes the scales per call). Prompt keys:
 // the sums are added to dKp / dVp in place (each element is read and written by exactly one
@@ -31,10 +32,11 @@ namespace lsr {
 
 namespace {
 
-template <int D, int DV>
+template <int D, int DV, int NW_>
 struct DkvCfg {
-  static constexpr int BN = 128;              // keys per workgroup (32 per wave)
-  static constexpr int BR = 32;               // query rows per step
+  static constexpr int NW = NW_;              // waves per workgroup (8: two per SIMD)
+  static constexpr int BN = NW * 32;          // keys per workgroup (32 per wave)
+  static constexpr int BR = 32;               // packed query rows per step
   static constexpr int QCH = D / 8;           // 16-byte chunks per Q row
   static constexpr int OCH = DV / 8;
   static constexpr int QROW = D * 2;
@@ -50,20 +52,29 @@ struct DkvCfg {
   static constexpr int OFF_OT = OFF_QT + QTBYTES;
   static constexpr int OFF_LD = OFF_OT + OTBYTES;
   static constexpr int STAGE = OFF_LD + LDBYTES;
-  static constexpr int NSTAGE = 3;
-  static constexpr int QINS = QBYTES / 4096;  // 1 KB direct loads per wave per step
-  static constexpr int OINS = OBYTES / 4096;
-  static constexpr int QTINS = QTBYTES / 4096;
-  static constexpr int OTINS = OTBYTES / 4096;
+  static constexpr int NSTAGE = 4;
+  // 1 KB direct loads of a step's Q, dO, Q^T and dO^T tiles, in that order, spread evenly over the
+  // waves; each wave also loads a 256-byte quarter of the row terms
+  static constexpr int QJ = QBYTES / 1024, OJ = OBYTES / 1024, QTJ = QTBYTES / 1024, OTJ = OTBYTES / 1024;
+  static constexpr int NJOB = QJ + OJ + QTJ + OTJ;
+  static constexpr int JPW = NJOB / NW;
+  static_assert(NJOB % NW == 0 && LDBYTES == 4 * 256, "loads per wave");
+  static constexpr int LPS = JPW + 1;         // direct loads per wave and step
   static constexpr int KS = D / 16;
   static constexpr int VS = DV / 16;
   static constexpr int DB = D / 32;
   static constexpr int VB = DV / 32;
 };
 
+// Prompt keys at head dim 128: 8 waves (256 keys per workgroup, thousands of workgroups). Response keys
+// (a response has few key tiles) and head dim 64 (whose 16 tile loads per step do not split into
+// whole tiles per wave over 8 waves): 4 waves, 128 keys. The plan's key tiles match (attn_plan.cpp).
+template <int D, bool PROMPT>
+constexpr int dkdv_waves() { return (PROMPT && D == 128) ? 8 : 4; }
+
 template <int D, int DV, bool PROMPT>
-__global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
-  using C = DkvCfg<D, DV>;
+__global__ __launch_bounds__((64 * dkdv_waves<D, PROMPT>()), 1) void replay_bwd_dkdv(BwdArgs a) {
+  using C = DkvCfg<D, DV, dkdv_waves<D, PROMPT>()>;
   __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE];
 
   const AttnGeom& G = a.geo;
@@ -100,13 +111,14 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
   }
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  // wave index as a scalar: the load assignment below branches on it
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int hl = lane >> 5;
   const int l32 = lane & 31;
   const int mykey = wv * 32 + l32;  // within the tile
   const bool kvalid = mykey < nkeys;
 
-  // K, V fragments of this wave's 32 keys (B operands of S = Q K^T and dP = dO V^T), in AGPRs
+  // K, V fragments of this wave's 32 keys (B operands of S = Q K^T and dP = dO V^T)
   bf16x8 kf[C::KS], vf[C::VS];
   {
     const uint16_t* kr = PROMPT ? G.Kp + (int64_t)(key0 + mykey) * G.ldk + kvh * D
@@ -114,15 +126,9 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
     const uint16_t* vr = PROMPT ? G.Vp + (int64_t)(key0 + mykey) * G.ldv + kvh * DV
                                 : G.Vs + (int64_t)(ktokb + key0 + mykey) * G.ldv + kvh * DV;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      kf[ks] = kvalid ? ld_bf16x8(kr + ks * 16 + hl * 8) : zero_bf16x8();
-      asm volatile("" : "+a"(kf[ks]));
-    }
+    for (int ks = 0; ks < C::KS; ++ks) kf[ks] = kvalid ? ld_bf16x8(kr + ks * 16 + hl * 8) : zero_bf16x8();
 #pragma unroll
-    for (int ks = 0; ks < C::VS; ++ks) {
-      vf[ks] = kvalid ? ld_bf16x8(vr + ks * 16 + hl * 8) : zero_bf16x8();
-      asm volatile("" : "+a"(vf[ks]));
-    }
+    for (int ks = 0; ks < C::VS; ++ks) vf[ks] = kvalid ? ld_bf16x8(vr + ks * 16 + hl * 8) : zero_bf16x8();
   }
 
   f32x16 dk[C::DB], dv[C::VB];
@@ -131,269 +137,212 @@ __global__ __launch_bounds__(256, 1) void replay_bwd_dkdv(BwdArgs a) {
 #pragma unroll
   for (int b = 0; b < C::VB; ++b) dv[b] = f32x16{};
 
-  // lane-constant LDS byte offsets within a stage
-  int qoff[C::KS], ooff[C::VS], toff[2];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) qoff[ks] = l32 * C::QROW + (((2 * ks + hl) ^ swz<C::QCH>(l32)) << 4);
-#pragma unroll
-  for (int ks = 0; ks < C::VS; ++ks) ooff[ks] = C::OFF_O + l32 * C::OROW + (((2 * ks + hl) ^ swz<C::OCH>(l32)) << 4);
-#pragma unroll
-  for (int h = 0; h < 2; ++h) toff[h] = l32 * C::TROW + (((2 * h + hl) ^ swz<4>(l32)) << 4);
-
   // Direct loads of a step go through buffer resources over this kv head's packed slabs (one base
-  // per slab; the step moves the scalar offset; loads past a slab's end read as zeros).
+  // per slab; the step moves the scalar offset, which stays inside the slab: the last step's rows
+  // end at or before the slab's padded row count).
   const int64_t mpad = a.mpad;
   const __amdgpu_buffer_rsrc_t rq = buf_rsrc(a.Qr + (int64_t)kvh * mpad * D, mpad * C::QROW);
   const __amdgpu_buffer_rsrc_t ro = buf_rsrc(a.dOr + (int64_t)kvh * mpad * DV, mpad * C::OROW);
   const __amdgpu_buffer_rsrc_t rqt = buf_rsrc(a.QT + (int64_t)kvh * D * mpad, (int64_t)D * mpad * 2);
   const __amdgpu_buffer_rsrc_t rot = buf_rsrc(a.dOT + (int64_t)kvh * DV * mpad, (int64_t)DV * mpad * 2);
   const __amdgpu_buffer_rsrc_t rld = buf_rsrc(a.rowstat + (int64_t)kvh * mpad * 8, mpad * 32);
-  // lane-constant byte offsets of the direct loads within one step's slabs: Q / dO rows row-major
-  // with XOR-swizzled chunks, Q^T / dO^T rows of 32 slots, 4 bytes of row terms per lane
-  uint32_t qdo[C::QINS], odo[C::OINS], qtdo[C::QTINS], otdo[C::OTINS];
-#pragma unroll
-  for (int u = 0; u < C::QINS; ++u) {
-    const int row = (wv * C::QINS + u) * (64 / C::QCH) + lane / C::QCH;
-    qdo[u] = (uint32_t)(row * C::QROW + (((lane % C::QCH) ^ swz<C::QCH>(row)) << 4));
-  }
-#pragma unroll
-  for (int u = 0; u < C::OINS; ++u) {
-    const int row = (wv * C::OINS + u) * (64 / C::OCH) + lane / C::OCH;
-    odo[u] = (uint32_t)(row * C::OROW + (((lane % C::OCH) ^ swz<C::OCH>(row)) << 4));
-  }
-#pragma unroll
-  for (int u = 0; u < C::QTINS; ++u) {
-    const int row = (wv * C::QTINS + u) * 16 + (lane >> 2);
-    qtdo[u] = (uint32_t)(row * mpad * 2 + (((lane & 3) ^ swz<4>(row)) << 4));
-  }
-#pragma unroll
-  for (int u = 0; u < C::OTINS; ++u) {
-    const int row = (wv * C::OTINS + u) * 16 + (lane >> 2);
-    otdo[u] = (uint32_t)(row * mpad * 2 + (((lane & 3) ^ swz<4>(row)) << 4));
-  }
-  const uint32_t ldo = (uint32_t)(wv * 256 + lane * 4);
-  // load i of this wave's kPerStep loads of the step at packed row m0 into stage buffer buf; the
-  // last one is this wave's quarter of the step's 1 KB of row terms.
-  constexpr int kPerStep = C::QINS + C::OINS + C::QTINS + C::OTINS + 1;
-  auto issue_load = [&](int i, int m0, char* buf) {
-    if (i < C::QINS) {
-      lds_dma16_buf(rq, qdo[i], buf + (wv * C::QINS + i) * 1024, m0 * C::QROW);
-    } else if (i < C::QINS + C::OINS) {
-      const int u = i - C::QINS;
-      lds_dma16_buf(ro, odo[u], buf + C::OFF_O + (wv * C::OINS + u) * 1024, m0 * C::OROW);
-    } else if (i < C::QINS + C::OINS + C::QTINS) {
-      const int u = i - C::QINS - C::OINS;
-      lds_dma16_buf(rqt, qtdo[u], buf + C::OFF_QT + (wv * C::QTINS + u) * 1024, m0 * 2);
-    } else if (i < kPerStep - 1) {
-      const int u = i - C::QINS - C::OINS - C::QTINS;
-      lds_dma16_buf(rot, otdo[u], buf + C::OFF_OT + (wv * C::OTINS + u) * 1024, m0 * 2);
+  // load u of this wave's JPW 1 KB loads of the step at packed row m0 into stage buffer buf: job
+  // j = u * NW + wv of the step's Q, dO, Q^T, dO^T tiles (row-major rows with XOR-swizzled chunks,
+  // transposed rows of 32 slots). Each tile is a whole number of loads per wave, so the tile of load
+  // u is known at compile time and the loop body has no branches (a branch there splits the loop into
+  // blocks at whose joins the compiler copies the accumulators).
+  static_assert(C::QJ % C::NW == 0 && C::OJ % C::NW == 0 && C::QTJ % C::NW == 0 && C::OTJ % C::NW == 0,
+                "whole tiles per wave");
+  auto issue_load = [&](int u, int m0, char* buf) {
+    const int j0 = u * C::NW;  // compile-time: the tile of this load
+    if (j0 < C::QJ) {
+      const int jj = j0 + wv;
+      const int row = jj * (64 / C::QCH) + lane / C::QCH;
+      const uint32_t off = (uint32_t)(row * C::QROW + (((lane % C::QCH) ^ swz<C::QCH>(row)) << 4));
+      lds_dma16_buf(rq, off, buf + jj * 1024, m0 * C::QROW);
+    } else if (j0 < C::QJ + C::OJ) {
+      const int jj = j0 - C::QJ + wv;
+      const int row = jj * (64 / C::OCH) + lane / C::OCH;
+      const uint32_t off = (uint32_t)(row * C::OROW + (((lane % C::OCH) ^ swz<C::OCH>(row)) << 4));
+      lds_dma16_buf(ro, off, buf + C::OFF_O + jj * 1024, m0 * C::OROW);
+    } else if (j0 < C::QJ + C::OJ + C::QTJ) {
+      const int jj = j0 - C::QJ - C::OJ + wv;
+      const int row = jj * 16 + (lane >> 2);
+      const uint32_t off = (uint32_t)(row * mpad * 2 + (((lane & 3) ^ swz<4>(row)) << 4));
+      lds_dma16_buf(rqt, off, buf + C::OFF_QT + jj * 1024, m0 * 2);
     } else {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (LSR_LDS void*)(buf + C::OFF_LD + wv * 256), 4, (int)ldo, m0 * 32, 0, 0);
+      const int jj = j0 - C::QJ - C::OJ - C::QTJ + wv;
+      const int row = jj * 16 + (lane >> 2);
+      const uint32_t off = (uint32_t)(row * mpad * 2 + (((lane & 3) ^ swz<4>(row)) << 4));
+      lds_dma16_buf(rot, off, buf + C::OFF_OT + jj * 1024, m0 * 2);
     }
   };
   auto issue_step = [&](int m0, char* buf) {
 #pragma unroll
-    for (int i = 0; i < kPerStep; ++i) issue_load(i, m0, buf);
+    for (int u = 0; u < C::JPW; ++u) issue_load(u, m0, buf);
+    // row terms in dwords: waves 0-3 load the four 256-byte quarters, waves 4-7 load the same bytes
+    // to the same places (identical data; every wave issues the same number of loads)
+    const int qtr = wv & 3;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (LSR_LDS void*)(buf + C::OFF_LD + qtr * 256), 4, qtr * 256 + lane * 4,
+                                             m0 * 32, 0, 0);
   };
 
   const float c2 = G.scale_log2;
   const int nsteps = row_end > row_begin ? (row_end - row_begin + C::BR - 1) / C::BR : 0;
+  const float s_ds = a.scales[2];  // fp16 scale of dS
 
-  // fp16 operand scales of this call
-  const float s_ds = a.scales[2];
-
-  // Software-pipelined steps. Step j's dV and dK products run while step j + 1's S and dP are
-  // formed, so every phase pairs one run of MFMAs with VALU work that does not depend on it and
-  // with the LDS reads of a later phase:
-  //   A  dV(j) MFMAs         | scaled dS(j), first half      | Q rows of step j + 1
-  //   B  S(j + 1) MFMAs      | scaled dS(j), second half     | dO rows of step j + 1, tile loads
-  //   C  dK(j) MFMAs         | 2^15 P(j + 1), first half     | row statistics, dO^T of step j + 1
-  //   D  dP(j + 1) MFMAs     | 2^15 P(j + 1), second half    | Q^T of step j + 1
-  // Within one wave only about a dozen cycles of VALU hide under each MFMA, so the VALU work is
-  // spread over all four runs instead of following the MFMAs it depends on.
-  // an empty asm use keeps a value's computation in the MFMA run it is written in (instruction
-  // selection would otherwise sink it to its first real use)
-  auto pin = [](float v) {
-    asm volatile("" : "+v"(v));
-    return v;
-  };
+  // Response keys: packed row m (token t = m / g - tokb, at key position t + qo) sees this lane's key
+  // (position kp) iff 0 <= t < R and kp <= t + qo, i.e. iff m_lo <= m < m_hi with the bounds below;
+  // rows of other responses see none of these keys.
+  const int kp = key0 + mykey;
+  const int m_lo = (tokb + max(0, kp - qo)) * g, m_hi = (tokb + R) * g;
   auto p_elem = [&](const f32x16& s, int r, int m0) {
-    const int q = r >> 2, e = r & 3;
     float pv = fast_exp2(s[r] * c2);
     if (!PROMPT) {
-      // causal within the response (row t at key position t + qo); rows of other responses see
-      // none of these keys
-      const int t = (m0 + 8 * q + 4 * hl + e) / g - tokb;
-      pv = (t >= 0 && t < R && key0 + mykey <= t + qo) ? pv : 0.0f;
+      const int m = m0 + 8 * (r >> 2) + 4 * hl + (r & 3);  // the packed row of register r
+      pv = (m >= m_lo && m < m_hi) ? pv : 0.0f;
     }
     return pv;
   };
-  auto ds_elem = [&](const f32x16& p, const f32x16& dpv, int r) { return p[r] * (dpv[r] * s_ds); };
-  // row terms of the step's 32 rows, as the A operands of the 32x32x8 products that start the S and
-  // dP accumulators (lanes 32..63 read the zero quarters; each half-wave reads 256 contiguous bytes)
-  auto read_terms = [&](const char* buf, s16x4& xq, s16x4& xo) {
-    xq = lds_s16x4_at(buf, C::OFF_LD + hl * 256 + l32 * 8);
-    xo = lds_s16x4_at(buf, C::OFF_LD + 512 + hl * 256 + l32 * 8);
-  };
-  // B operand of those products: [1, 1, 1, 0] over k = 0..3 for every key, zero for k = 4..7
+  // B operand of the row-term products: [1, 1, 1, 0] over k = 0..3 for every key, zero for k = 4..7
   const s16x4 ones = hl ? s16x4{0, 0, 0, 0} : s16x4{0x3F80, 0x3F80, 0x3F80, 0};
+  // LDS byte offsets of a lane's fragments within a stage. Row-major tiles store logical 16-byte
+  // chunk c of row r at chunk c ^ swz(r); the lane's fragment k (chunks 2k + hl of row l32) sits at
+  // xb ^ (k << 5) with xb = row offset | ((hl ^ swz(l32)) << 4): the XOR touches bits 5..7 only, so
+  // it commutes with adding the stage offset and the tile offsets (multiples of 1 KB). The packed
+  // Q^T / dO^T tiles (64-byte rows of 32 slots) work the same way with k = the row half h.
+  static_assert(C::STAGE % 1024 == 0 && C::OFF_O % 1024 == 0 && C::OFF_QT % 1024 == 0 && C::OFF_OT % 1024 == 0,
+                "stage and tile offsets must not touch bits 5..7");
+  const int qx0 = (l32 * C::QROW) | ((hl ^ swz<C::QCH>(l32)) << 4);
+  const int ox0 = C::OFF_O + ((l32 * C::OROW) | ((hl ^ swz<C::OCH>(l32)) << 4));
+  const int tx0 = (l32 * C::TROW) | ((hl ^ swz<4>(l32)) << 4);
 
-  // State carried from one step to the next: 2^15 P (fp32 and fp16), dP - Delta, and the dO^T and
-  // Q^T fragments of the step whose dV / dK products are still to run.
-  f32x16 p, dp;
-  f16x8 pf[2];
-  f16x8 ot[2][C::VB], qt[2][C::DB];
+  // One step: 32 packed rows against this wave's 32 keys, in two phases
+  //   X:  S = row term + Q K^T;  2^15 P = exp2(c S)      (the row term holds -(LSE log2 e - 15) / c)
+  //       dP - Delta = row term + dO V^T;  dS' = 2^15 P (dP - Delta) s_dS
+  //   Y:  dV^T += dO^T (2^15 P),  dK^T += Q^T dS'         (fp16 operands)
+  // X holds all of the step's VALU work, Y only MFMAs. Every MFMA takes one 16-byte LDS fragment,
+  // read PD slots ahead (LDS latency under this load is several MFMAs long); a slot is one MFMA with
+  // its read, fenced so the compiler keeps the reads (and their registers) where they are written.
+  // Y reads the same stage as X, so its first fragments are read during X's last slots, across the
+  // barrier between the phases.
+  constexpr int NQ = C::KS, NO = C::VS, NOT = 2 * C::VB, NQT = 2 * C::DB;
+  constexpr int NX = NQ + NO, NF = NX + NOT + NQT;
+  constexpr int PD = 2;
 
-  // Three-stage ring. The barrier of step j + 1 (top of pipelined step j) publishes step j + 1's
-  // tiles (each wave first waits for its own loads of it) and frees step j's stage: every read
-  // of that stage was issued during pipelined step j - 1 and has returned (lgkmcnt(0) before the
-  // barrier). That stage then receives step j + 3, issued under the S(j + 1) MFMAs, two steps
-  // before it is read. Past the last step the last step's rows are loaded again, so every step
-  // issues the same number of loads and the wait count is fixed.
-  char* const st0 = smem;
-  char* const st1 = smem + C::STAGE;
-  char* const st2 = smem + 2 * C::STAGE;
+  // Four-stage ring; the two wave groups (waves 0-3 and 4-7, one of each per SIMD) run half a step
+  // apart, so that one group's VALU-heavy phase X overlaps the other's MFMA-only phase Y. Every
+  // phase starts at a workgroup barrier; the trailing group passes one extra barrier at the start and
+  // the leading group one at the end, so both pass the same number. At the barrier before the
+  // leading group's X(j) the trailing group stands before Y(j - 1). Hence:
+  //  * step j's tiles must be complete before the trailing group's Y(j - 1): each wave waits for its
+  //    own loads of step j + 1 at the end of its X(j) (loads of steps j + 1 and j + 2 in flight);
+  //  * a wave issues its loads of step j + 3 at the barrier before its Y(j), into the stage of step
+  //    j - 1, which both groups have finished reading by then (the trailing group is before X(j));
+  //    each wave's reads of a stage have returned before the barrier that precedes its next X.
+  // Past the last step the last step's rows are loaded again, so every step issues the same number
+  // of loads and the wait count is fixed.
+  const bool trailing = C::NW == 8 && wv >= 4;  // wave-uniform; four waves run in step
+  auto stage = [&](int j) { return smem + (j & 3) * C::STAGE; };
   auto mrow = [&](int t) { return row_begin + min(t, nsteps - 1) * C::BR; };
 
-  // the reads and products of one step's S and dP, 2^15 P and its fp16 copy, with the fragments
-  // of the step's dV / dK products; used once, for step 0
-  auto first_step = [&](const char* buf) {
-    bf16x8 af[C::KS], bfr[C::VS];
-    s16x4 xq, xo;
-    read_terms(buf, xq, xo);
+  auto step = [&](int j) {
+    const char* buf = stage(j);
+    const int m0 = row_begin + j * C::BR;
+    // per-step fragment bases (the opaque copy keeps them from being hoisted out of the loop as one
+    // live register per fragment)
+    int qx = qx0, ox = ox0, tx = tx0;
+    asm volatile("" : "+v"(qx), "+v"(ox), "+v"(tx));
+    const int stg = (int)(buf - smem);
+    qx += stg;
+    ox += stg;
+    tx += stg;
+    const int tx1 = tx ^ 32;
+    auto rd = [&](int i) {
+      int off;
+      if (i < NQ) off = qx ^ (i << 5);
+      else if (i < NX) off = ox ^ ((i - NQ) << 5);
+      else if (i < NX + NOT) {
+        const int k = i - NX, h = k / C::VB, b = k % C::VB;
+        off = (h ? tx1 : tx) + C::OFF_OT + b * 32 * C::TROW;
+      } else {
+        const int k = i - NX - NOT, h = k / C::DB, b = k % C::DB;
+        off = (h ? tx1 : tx) + C::OFF_QT + b * 32 * C::TROW;
+      }
+      return __builtin_bit_cast(u32x4, lds_b128_at(smem, off));
+    };
+    u32x4 fr[NF];
+    const s16x4 xq = lds_s16x4_at(buf, C::OFF_LD + hl * 256 + l32 * 8);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) af[ks] = lds_b128_at(buf, qoff[ks]);
-#pragma unroll
-    for (int ks = 0; ks < C::VS; ++ks) bfr[ks] = lds_b128_at(buf, ooff[ks]);
-    f32x16 s = mfma32x8(xq, ones, f32x16{});
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) s = mfma32(af[ks], kf[ks], s);
-    dp = mfma32x8(xo, ones, f32x16{});
-#pragma unroll
-    for (int ks = 0; ks < C::VS; ++ks) dp = mfma32(bfr[ks], vf[ks], dp);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int b = 0; b < C::VB; ++b) ot[h][b] = lds_h128_at(buf, C::OFF_OT + b * 32 * C::TROW + toff[h]);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int b = 0; b < C::DB; ++b) qt[h][b] = lds_h128_at(buf, C::OFF_QT + b * 32 * C::TROW + toff[h]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = p_elem(s, r, row_begin);
-    pf[0] = c_regs_to_f16x8(p, 0);
-    pf[1] = c_regs_to_f16x8(p, 8);
-  };
-
-  // pipelined step j: finishes step j (buf of step j + 1 = nb, free stage fb receives step j + 3)
-  auto step = [&](int j, const char* nb, char* fb) {
-    const int mn = row_begin + (j + 1) * C::BR;  // first packed row of step j + 1
-    const int ml = mrow(j + 3);
-    constexpr int NA = 2 * C::VB, NB = C::KS, NC = 2 * C::DB, ND = C::VS;
-    // A: dV(j) += dO^T P; scaled dS(j) rows 0..7; row terms and Q rows of step j + 1
-    bf16x8 af[C::KS];
-    s16x4 xq, xo;
-    read_terms(nb, xq, xo);
-    f32x16 ds = dp;
+    for (int i = 0; i < PD; ++i) fr[i] = rd(i);
+    f32x16 s = mfma32x8(xq, ones, f32x16{}), dp;
+    f16x8 h0, h1, d0, d1;  // fp16 2^15 P and dS'
+    s16x4 xo;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      dv[i % C::VB] = mfma32h(ot[i / C::VB][i % C::VB], pf[i / C::VB], dv[i % C::VB]);
+    for (int i = 0; i < NF; ++i) {
+      if (i == NX) {
+        // between the phases: own loads of step j + 1 complete, then the barrier before Y(j), then
+        // this wave's loads of step j + 3 into the stage of step j - 1
+        wait_vmem_le<C::LPS>();
+        bare_barrier();
+        issue_step(mrow(j + 3), stage(j + 3));
+      }
+      if (i + PD < NF) fr[i + PD] = rd(i + PD);
+      if (i == NQ - 1) xo = lds_s16x4_at(buf, C::OFF_LD + 512 + hl * 256 + l32 * 8);
+      if (i < NQ) {
+        s = mfma32(__builtin_bit_cast(bf16x8, fr[i]), kf[i], s);
+        if (i == NQ - 1) {
+          // 2^15 P, kept in fp16 only (the B operand of the dV products; dS' below is formed from it)
 #pragma unroll
-      for (int k = 0; k < C::KS; ++k)
-        if (k * NA / C::KS == i) af[k] = lds_b128_at(nb, qoff[k]);
+          for (int r = 0; r < 16; ++r) s[r] = p_elem(s, r, m0);
+          h0 = c_regs_to_f16x8(s, 0);
+          h1 = c_regs_to_f16x8(s, 8);
+        }
+      } else if (i < NX) {
+        if (i == NQ) dp = mfma32x8(xo, ones, f32x16{});
+        dp = mfma32(__builtin_bit_cast(bf16x8, fr[i]), vf[i - NQ], dp);
+        if (i == NX - 1) {
+          // dS' = 2^15 P (dP - Delta) s_dS in place of dP, from the fp16 2^15 P: its halves are
+          // unpacked here from the packed operand (the opaque copy keeps the compiler from holding a
+          // second, unpacked copy of P since the exponentials)
+          u32x4 hu0 = __builtin_bit_cast(u32x4, h0), hu1 = __builtin_bit_cast(u32x4, h1);
+          asm volatile("" : "+v"(hu0), "+v"(hu1));
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (r * NA / 8 == i) ds[r] = pin(ds_elem(p, dp, r));
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t u = r < 8 ? hu0[(r & 7) >> 1] : hu1[(r & 7) >> 1];
+            const float pv = (float)__builtin_bit_cast(_Float16, (uint16_t)((r & 1) ? (u >> 16) : (u & 0xffffu)));
+            dp[r] = pv * (dp[r] * s_ds);
+          }
+          h0 = __builtin_bit_cast(f16x8, hu0);
+          h1 = __builtin_bit_cast(f16x8, hu1);
+          d0 = c_regs_to_f16x8(dp, 0);
+          d1 = c_regs_to_f16x8(dp, 8);
+        }
+      } else if (i < NX + NOT) {
+        const int k = i - NX, h = k / C::VB, b = k % C::VB;
+        dv[b] = mfma32h(__builtin_bit_cast(f16x8, fr[i]), h ? h1 : h0, dv[b]);
+      } else {
+        const int k = i - NX - NOT, h = k / C::DB, b = k % C::DB;
+        dk[b] = mfma32h(__builtin_bit_cast(f16x8, fr[i]), h ? d1 : d0, dk[b]);
+      }
       __builtin_amdgcn_sched_barrier(0);
-    }
-    // B: S(j + 1) = Q K^T; scaled dS(j) rows 8..15; dO rows of step j + 1; step j + 3's tiles
-    const f16x8 d0 = c_regs_to_f16x8(ds, 0);
-    bf16x8 bfr[C::VS];
-    f32x16 sn = mfma32x8(xq, ones, f32x16{});
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      sn = mfma32(af[i], kf[i], sn);
-#pragma unroll
-      for (int k = 0; k < C::VS; ++k)
-        if (k * NB / C::VS == i) bfr[k] = lds_b128_at(nb, ooff[k]);
-#pragma unroll
-      for (int r = 8; r < 16; ++r)
-        if ((r - 8) * NB / 8 == i) ds[r] = pin(ds_elem(p, dp, r));
-#pragma unroll
-      for (int l = 0; l < kPerStep; ++l)
-        if (l * NB / kPerStep == i) issue_load(l, ml, fb);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const f16x8 d1 = c_regs_to_f16x8(ds, 8);
-    // C: dK(j) += Q^T dS; dO^T of step j + 1; 2^15 P(j + 1) rows 0..7
-    f16x8 otn[2][C::VB];
-    f32x16 pn;
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      dk[i % C::DB] = mfma32h(qt[i / C::DB][i % C::DB], i / C::DB ? d1 : d0, dk[i % C::DB]);
-#pragma unroll
-      for (int k = 0; k < 2 * C::VB; ++k)
-        if (k * NC / (2 * C::VB) == i) otn[k / C::VB][k % C::VB] = lds_h128_at(nb, C::OFF_OT + (k % C::VB) * 32 * C::TROW + toff[k / C::VB]);
-      // P needs the S MFMAs' results: start it half-way through the run
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (NC / 2 + r * (NC - NC / 2) / 8 == i) pn[r] = pin(p_elem(sn, r, mn));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    pf[0] = c_regs_to_f16x8(pn, 0);
-    // D: dP(j + 1) = dO V^T; Q^T of step j + 1; 2^15 P(j + 1) rows 8..15
-    f16x8 qtn[2][C::DB];
-    f32x16 dpn = mfma32x8(xo, ones, f32x16{});
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < ND; ++i) {
-      dpn = mfma32(bfr[i], vf[i], dpn);
-#pragma unroll
-      for (int k = 0; k < 2 * C::DB; ++k)
-        if (k * ND / (2 * C::DB) == i) qtn[k / C::DB][k % C::DB] = lds_h128_at(nb, C::OFF_QT + (k % C::DB) * 32 * C::TROW + toff[k / C::DB]);
-#pragma unroll
-      for (int r = 8; r < 16; ++r)
-        if ((r - 8) * ND / 8 == i) pn[r] = pin(p_elem(sn, r, mn));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    pf[1] = c_regs_to_f16x8(pn, 8);
-    p = pn;
-    dp = dpn;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int b = 0; b < C::VB; ++b) ot[h][b] = otn[h][b];
-#pragma unroll
-      for (int b = 0; b < C::DB; ++b) qt[h][b] = qtn[h][b];
     }
   };
 
   if (nsteps > 0) {
-    issue_step(mrow(0), st0);
-    issue_step(mrow(1), st1);
-    issue_step(mrow(2), st2);
-    wait_vmem_le<2 * kPerStep>();
-    bare_barrier();
-    first_step(st0);
+    issue_step(mrow(0), stage(0));
+    issue_step(mrow(1), stage(1));
+    issue_step(mrow(2), stage(2));
+    wait_vmem_le<2 * C::LPS>();  // own loads of step 0
   }
-  // Pipelined step j runs whether or not step j + 1 exists: past the last step it forms S and dP
-  // of a repeated tile (rows clamped, results unused), so every wave passes the same barriers.
-  for (int it = 0; it < nsteps; it += 3) {
-#pragma unroll
-    for (int jj = 0; jj < 3; ++jj) {
-      const int j = it + jj;
-      if (j >= nsteps) break;
-      char* nb = jj == 0 ? st1 : (jj == 1 ? st2 : st0);  // stage of step j + 1
-      char* fb = jj == 0 ? st0 : (jj == 1 ? st1 : st2);  // stage of step j, free after the barrier
-      wait_vmem_le<kPerStep>();
-      wait_lds();      // this wave's reads of step j's stage have returned
-      bare_barrier();  // no fence: it would wait for every direct load in flight
-      step(j, nb, fb);
-    }
+  if (trailing) bare_barrier();
+  for (int j = 0; j < nsteps; ++j) {
+    wait_lds();      // this wave's reads of the previous stage have returned
+    bare_barrier();  // before X(j); no fence: it would wait for every direct load in flight
+    step(j);
   }
+  if (!trailing) bare_barrier();
   // no direct load may still be writing into LDS when the waves end
   wait_vmem();
 
@@ -537,13 +486,15 @@ hipError_t dkdv_go(BwdArgs& a, hipStream_t st) {
   if (a.ktiles_prompt > 0) {
     const long long W = (long long)a.ktiles_prompt * G.Hkv;
     timer_mark(LS_KERNEL_DKDV_PROMPT, st, false);
-    hipLaunchKernelGGL((replay_bwd_dkdv<D, DV, true>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((replay_bwd_dkdv<D, DV, true>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(64 * dkdv_waves<D, true>()), 0,
+                       st, a);
     timer_mark(LS_KERNEL_DKDV_PROMPT, st, true);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const long long W = (long long)a.ktile0[G.n_resp] * G.Hkv;
   if (W > 0) {
-    hipLaunchKernelGGL((replay_bwd_dkdv<D, DV, false>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((replay_bwd_dkdv<D, DV, false>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(64 * dkdv_waves<D, false>()), 0,
+                       st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
