@@ -2,9 +2,10 @@
 //
 // A workgroup handles one token row at a time. The bf16 logits row is read from HBM exactly once into
 // VGPRs (16-byte loads, consecutive threads on consecutive 16-byte chunks); the row max
-// and the sum of exponentials are wave reductions combined through LDS; the dlogits row is
-// then produced from the same registers and written once. HBM traffic per token is the
-// algorithmic minimum: 2V bytes in, 2V bytes out, plus target, old log-prob, log-prob.
+// and the sum of exponentials are wave reductions combined through LDS; the exponentials replace
+// the logits in the registers (bf16), and the dlogits row is produced from them with one multiply
+// per element and written once. HBM traffic per token is the algorithmic minimum: 2V bytes in, 2V
+// bytes out, plus target, old log-prob, log-prob.
 //
 // Per row t of response i (A = A_i, w = 1/(G R_i)):
 //   lse = max + log(sum exp(x - max)),  logp = x_y - lse,  rho = exp(logp - old)
@@ -70,7 +71,7 @@ __device__ __forceinline__ float row_scalar(const GrpoArgs& a, int64_t row, floa
 // are reloaded with chunk j of the next row as soon as chunk j's dlogits are stored: the next
 // row streams in while this row's output is formed and written, and the stores drain while the
 // next row's max and sum are taken.
-template <int NT, int NCH>
+template <int NT, int NCH, bool SCORE>
 __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
   __shared__ float red[NT / 64];
   const int nch = a.V >> 3;
@@ -112,6 +113,9 @@ __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
     for (int j = 0; j < NCH; ++j)
       if ((int)threadIdx.x + j * NT + zoff >= nch) v[j] = u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
 
+    // after the last row the reloads go through an empty resource: no memory access, zeros returned
+    const __amdgpu_buffer_rsrc_t nsrc =
+        more ? row_src(next) : __builtin_amdgcn_make_buffer_rsrc((void*)a.logits, 0, 0, kBufferWord3);
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
@@ -123,22 +127,38 @@ __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) asm volatile("" : "+v"(v[j]));
     const float mb = m * kLog2e;
+    // e = exp2((x - max) log2 e), summed; the gradient pass keeps e (bf16) in place of the logits, so
+    // each element takes one exponential; the scoring pass needs only the sum, and reloads each
+    // chunk's registers with the next row's chunk as soon as its exponentials are summed. Both passes
+    // sum in the same order, so scoring gives bit-identical log-probs and loss.
     float s = 0.0f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        s += fast_exp2(__builtin_fmaf(bf16_lo(v[j][q]), kLog2e, -mb));
-        s += fast_exp2(__builtin_fmaf(bf16_hi(v[j][q]), kLog2e, -mb));
+        const float e0 = fast_exp2(__builtin_fmaf(bf16_lo(v[j][q]), kLog2e, -mb));
+        const float e1 = fast_exp2(__builtin_fmaf(bf16_hi(v[j][q]), kLog2e, -mb));
+        s += e0;
+        s += e1;
+        if (!SCORE) v[j][q] = pack_bf16x2(e0, e1);
       }
+      if (SCORE) {
+        // the reload of chunk j after its exponentials (not hoisted above them: two copies live)
+        __builtin_amdgcn_sched_barrier(0);
+        v[j] = ld_chunk(nsrc, j, zoff);
+      } else {
+        asm volatile("" : "+v"(v[j]));  // the packed exponentials are formed here, not at their use
+      }
+      // chunk by chunk, so that only one chunk's floats are live beside the packed row
+      __builtin_amdgcn_sched_barrier(0);
     }
     s = block_reduce<NT>(s, red, false);
     const float lse = m + fast_log2(s) * kLn2;
     const float c = row_scalar(a, row, xy, y_ok, lse);
-    // after the last row the reloads go through an empty resource: no memory access, zeros returned
-    const __amdgpu_buffer_rsrc_t nsrc =
-        more ? row_src(next) : __builtin_amdgcn_make_buffer_rsrc((void*)a.logits, 0, 0, kBufferWord3);
-    if (a.dlogits != nullptr) {
+    if (!SCORE) {
+      // dlogits = c softmax(x) = (c / sum) e, with the target's element c (p_y - 1) formed from the
+      // logit itself
+      const float f = c / s;
       const float lb = lse * kLog2e;
 #pragma unroll
       for (int j = 0; j < NCH; ++j) asm volatile("" : "+v"(v[j]));
@@ -151,14 +171,9 @@ __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
         const int cj = (int)threadIdx.x + j * NT + zoff;
         u32x4 o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float p0 = fast_exp2(__builtin_fmaf(bf16_lo(v[j][q]), kLog2e, -lb));
-          const float p1 = fast_exp2(__builtin_fmaf(bf16_hi(v[j][q]), kLog2e, -lb));
-          o[q] = pack_bf16x2(c * p0, c * p1);
-        }
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(f * bf16_lo(v[j][q]), f * bf16_hi(v[j][q]));
         if (cj == yc) {
-          // the one-hot term (one lane of the row): the target's element becomes c (p_y - 1), p_y
-          // formed from the same logit value as the other elements
+          // the one-hot term (one lane of the row): the target's element becomes c (p_y - 1)
           const float py = fast_exp2(__builtin_fmaf(xy, kLog2e, -lb)) - 1.0f;
           const uint32_t t = pack_bf16x2(c * py, 0.0f) & 0xffffu;
           const int qy = (y & 7) >> 1;
@@ -173,9 +188,6 @@ __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
         // which would keep two rows' chunks live at once
         __builtin_amdgcn_sched_barrier(0);
       }
-    } else if (more) {
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) v[j] = ld_chunk(nsrc, j, zoff);
     }
     if (!more) break;
     row = next;
@@ -292,7 +304,8 @@ template <int NT, int NCH>
 hipError_t go_vec(const GrpoArgs& a, hipStream_t st) {
   const int64_t wgs = kLossCUs * (NT == 1024 ? 1 : 4);
   const int64_t grid = a.T < wgs ? a.T : wgs;
-  hipLaunchKernelGGL((grpo_rows_vec<NT, NCH>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+  if (a.dlogits) hipLaunchKernelGGL((grpo_rows_vec<NT, NCH, false>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+  else hipLaunchKernelGGL((grpo_rows_vec<NT, NCH, true>), dim3((unsigned)grid), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
