@@ -14,8 +14,8 @@ LIB = os.path.join(PKG, "liblsreplay.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_SOURCES = ["grpo_loss.hip", "replay_attn_fwd.hip", "replay_attn_bwd.hip", "replay_attn_dq.hip", "replay_attn_dkdv.hip", "pack.hip",
-               "replay_attn_wide_fwd.hip", "replay_attn_wide_bwd.hip", "noalloc.hip"]
-CXX_SOURCES = ["api.cpp", "attn_plan.cpp", "timer.cpp", "lmhead.cpp"]
+               "replay_attn_wide_fwd.hip", "replay_attn_wide_bwd.hip", "noalloc.hip", "lmhead.hip"]
+CXX_SOURCES = ["api.cpp", "attn_plan.cpp", "timer.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 # the packed-fp32 feature stays off: every v_pk_*_f32 is left out of the kernels
 HIP_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -70,9 +70,7 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
             raise RuntimeError(f"ISA check failed for {j[-1]}:\n" + "\n".join(bad[:20]))
     objs = [j[-1] for j in jobs]
     tmp = LIB + ".tmp"
-    # rocBLAS serves the plain GEMMs of the LM-head path (lmhead.cpp)
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-L/opt/rocm/lib", "-lrocblas",
-          "-Wl,-rpath,/opt/rocm/lib", "-o", tmp])
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

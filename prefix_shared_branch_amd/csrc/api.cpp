@@ -284,10 +284,8 @@ int bwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void*
 
 namespace lsr {
 
-int grpo_rows(hipStream_t st, int32_t V, int32_t G, const int32_t* R, const float* rewards, float eps, int32_t first,
-              int32_t count, int64_t lo, int64_t hi, const uint16_t* logits, const int32_t* targets,
-              const float* old_logp, uint16_t* dlogits, float* loss_accum, float* logp_out, uint8_t* clipped_out,
-              float* row_loss, bool vec) {
+bool grpo_batches(int32_t G, const int32_t* R, const float* rewards, float eps, int32_t first, int32_t count,
+                  int64_t lo, int64_t hi, const std::function<bool(GrpoArgs&, int64_t)>& fn) {
   // group advantage in float64 on the host: A_i = (r_i - mean) / (std_pop + 1e-6)
   double mean = 0.0;
   for (int i = 0; i < G; ++i) mean += rewards[i];
@@ -296,7 +294,7 @@ int grpo_rows(hipStream_t st, int32_t V, int32_t G, const int32_t* R, const floa
   for (int i = 0; i < G; ++i) var += (rewards[i] - mean) * (rewards[i] - mean);
   const double sd = std::sqrt(var / G);
 
-  // the rows of each response that fall in [lo, hi), launched in batches of at most kMaxResp
+  // the rows of each response that fall in [lo, hi), in batches of at most kMaxResp responses
   GrpoArgs a;
   int nb = 0;
   int64_t brow0 = 0, rows = 0;
@@ -304,19 +302,10 @@ int grpo_rows(hipStream_t st, int32_t V, int32_t G, const int32_t* R, const floa
     if (nb == 0) return true;
     a.n = nb;
     a.T = rows;
-    a.V = V;
     a.eps = eps;
-    a.logits = logits + (brow0 - lo) * V;
-    a.dlogits = dlogits ? dlogits + (brow0 - lo) * V : nullptr;
-    a.targets = targets + brow0;
-    a.old_logp = old_logp + brow0;
-    a.row_loss = row_loss + (brow0 - lo);
-    a.logp_out = logp_out ? logp_out + brow0 : nullptr;
-    a.clipped_out = clipped_out ? clipped_out + brow0 : nullptr;
-    a.loss_accum = loss_accum;
     nb = 0;
     rows = 0;
-    return launch_grpo(a, vec, st) == hipSuccess;
+    return fn(a, brow0);
   };
   int64_t start = 0;
   for (int i = first; i < first + count; ++i) {
@@ -332,9 +321,28 @@ int grpo_rows(hipStream_t st, int32_t V, int32_t G, const int32_t* R, const floa
     a.row_end[nb] = (int32_t)rows;
     a.A[nb] = (float)((rewards[i] - mean) / (sd + 1e-6));
     a.w[nb] = (float)(1.0 / ((double)G * (double)R[i]));
-    if (++nb == kMaxResp && !flush()) return LS_ERR_HIP;
+    if (++nb == kMaxResp && !flush()) return false;
   }
-  return flush() ? LS_OK : LS_ERR_HIP;
+  return flush();
+}
+
+int grpo_rows(hipStream_t st, int32_t V, int32_t G, const int32_t* R, const float* rewards, float eps, int32_t first,
+              int32_t count, int64_t lo, int64_t hi, const uint16_t* logits, const int32_t* targets,
+              const float* old_logp, uint16_t* dlogits, float* loss_accum, float* logp_out, uint8_t* clipped_out,
+              float* row_loss, bool vec) {
+  const bool ok = grpo_batches(G, R, rewards, eps, first, count, lo, hi, [&](GrpoArgs& a, int64_t brow0) {
+    a.V = V;
+    a.logits = logits + (brow0 - lo) * V;
+    a.dlogits = dlogits ? dlogits + (brow0 - lo) * V : nullptr;
+    a.targets = targets + brow0;
+    a.old_logp = old_logp + brow0;
+    a.row_loss = row_loss + (brow0 - lo);
+    a.logp_out = logp_out ? logp_out + brow0 : nullptr;
+    a.clipped_out = clipped_out ? clipped_out + brow0 : nullptr;
+    a.loss_accum = loss_accum;
+    return launch_grpo(a, vec, st) == hipSuccess;
+  });
+  return ok ? LS_OK : LS_ERR_HIP;
 }
 
 }  // namespace lsr

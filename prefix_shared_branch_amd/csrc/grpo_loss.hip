@@ -16,18 +16,12 @@
 // Without a dlogits buffer (scoring old or reference policies) the row kernels stop after the
 // per-row outputs: the logits are read once and nothing of size V is written.
 #include "common.h"
+#include "grpo_row.h"
 #include "kernels.h"
 
 namespace lsr {
 
 namespace {
-
-__device__ __forceinline__ void row_coefs(const GrpoArgs& a, int64_t row, float* A, float* w) {
-  int i = 0;
-  while (i + 1 < a.n && row >= a.row_end[i]) ++i;
-  *A = a.A[i];
-  *w = a.w[i];
-}
 
 template <int NT>
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
@@ -41,26 +35,6 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 #pragma unroll
   for (int k = 1; k < NW; ++k) r = is_max ? fmaxf(r, red[k]) : r + red[k];
   return r;
-}
-
-// Scalar part shared by both row kernels: everything that depends on (x_y, lse) only.
-// Returns the dlogits coefficient c. A target outside [0, V) or NaN data make the row NaN.
-__device__ __forceinline__ float row_scalar(const GrpoArgs& a, int64_t row, float xy, bool y_ok, float lse) {
-  float A, w;
-  row_coefs(a, row, &A, &w);
-  const float logp = y_ok ? xy - lse : __builtin_nanf("");
-  const float rho = expf(logp - a.old_logp[row]);
-  const bool nan = !(rho == rho);
-  const float unclipped = rho * A;
-  const float clipped_v = fminf(fmaxf(rho, 1.0f - a.eps), 1.0f + a.eps) * A;
-  const bool clipped = !nan && (clipped_v < unclipped);
-  const float term = nan ? rho : fminf(unclipped, clipped_v);
-  if (threadIdx.x == 0) {
-    a.row_loss[row] = -w * term;
-    if (a.logp_out) a.logp_out[row] = logp;
-    if (a.clipped_out) a.clipped_out[row] = clipped ? 1 : 0;
-  }
-  return clipped ? 0.0f : w * A * rho;
 }
 
 // Vector path: V % 8 == 0, 16-byte aligned rows; NCH 16-byte chunks per thread in registers.
@@ -154,7 +128,7 @@ __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
     }
     s = block_reduce<NT>(s, red, false);
     const float lse = m + fast_log2(s) * kLn2;
-    const float c = row_scalar(a, row, xy, y_ok, lse);
+    const float c = row_scalar(a, row, xy, y_ok, lse, threadIdx.x == 0);
     if (!SCORE) {
       // dlogits = c softmax(x) = (c / sum) e, with the target's element c (p_y - 1) formed from the
       // logit itself
@@ -230,7 +204,7 @@ __global__ __launch_bounds__(NT) void grpo_rows_stream(GrpoArgs a) {
   const float S = block_reduce<NT>(sl, red, false);
   const float lse = M + fast_log2(S) * kLn2;
   const float xy = y_ok ? bf16_to_f32(a.logits[row * (int64_t)a.V + y]) : 0.0f;
-  const float c = row_scalar(a, row, xy, y_ok, lse);
+  const float c = row_scalar(a, row, xy, y_ok, lse, threadIdx.x == 0);
   if (a.dlogits == nullptr) return;  // scoring only: no gradient pass
   const float lb = lse * kLog2e;
   const int yc = y_ok ? (y >> 3) : -1;
@@ -273,7 +247,7 @@ __global__ __launch_bounds__(256) void grpo_rows_scalar(GrpoArgs a) {
   s = block_reduce<NT>(s, red, false);
   const float lse = m + fast_log2(s) * kLn2;
   const float xy = y_ok ? bf16_to_f32(x[y]) : 0.0f;
-  const float c = row_scalar(a, row, xy, y_ok, lse);
+  const float c = row_scalar(a, row, xy, y_ok, lse, threadIdx.x == 0);
   if (a.dlogits == nullptr) return;  // scoring only: no gradient pass
   uint16_t* d = a.dlogits + row * (int64_t)a.V;
   for (int e = threadIdx.x; e < a.V; e += NT) {
@@ -294,6 +268,56 @@ __global__ __launch_bounds__(256) void grpo_sum(const float* row_loss, int64_t T
     __syncthreads();
   }
   if (threadIdx.x == 0) *loss_accum = (float)((double)*loss_accum + part[0]);
+}
+
+// LM-head row pass: one workgroup per row. The row's log-sum-exp merges the slab partials
+// (max_k, s_k) of the logits GEMM: lse = M + log sum_k s_k exp(max_k - M), M = max_k max_k. With a
+// dlogits buffer, each 16-byte chunk of stored e = exp(x - slab max) becomes
+// dlogits = c exp(x - lse) = c exp(slab max - lse) e, the target's element c (p_y - 1).
+template <int NT>
+__global__ __launch_bounds__(NT) void lm_rows(LmRowArgs la) {
+  __shared__ float red[NT / 64];
+  const GrpoArgs& a = la.g;
+  const int64_t row = blockIdx.x;
+  const float2* p = la.part + row * la.nslab;
+  float m = -INFINITY;
+  for (int i = threadIdx.x; i < la.nslab; i += NT) m = fmaxf(m, p[i].x);
+  m = block_reduce<NT>(m, red, true);
+  const float mb = m * kLog2e;
+  float s = 0.0f;
+  for (int i = threadIdx.x; i < la.nslab; i += NT) {
+    const float2 q = p[i];
+    s += q.y * fast_exp2(__builtin_fmaf(q.x, kLog2e, -mb));
+  }
+  s = block_reduce<NT>(s, red, false);
+  const float lse = m + fast_log2(s) * kLn2;
+  const int y = a.targets[row];
+  const bool y_ok = (y >= 0) && (y < a.V);
+  const float xy = y_ok ? la.xtgt[row] : 0.0f;
+  const float c = row_scalar(a, row, xy, y_ok, lse, threadIdx.x == 0);
+  if (a.dlogits == nullptr) return;  // scoring only
+  const float lb = lse * kLog2e;
+  const int nch = a.V >> 3;
+  const int yc = y_ok ? (y >> 3) : -1;
+  u32x4* d = reinterpret_cast<u32x4*>(a.dlogits + row * (int64_t)a.V);
+#pragma unroll 4
+  for (int cj = threadIdx.x; cj < nch; cj += NT) {
+    const float f = c * fast_exp2(__builtin_fmaf(p[cj >> 4].x, kLog2e, -lb));
+    const u32x4 v = d[cj];
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(f * bf16_lo(v[q]), f * bf16_hi(v[q]));
+    if (cj == yc) {  // the one-hot term, as in grpo_rows_vec
+      const float py = fast_exp2(__builtin_fmaf(xy, kLog2e, -lb)) - 1.0f;
+      const uint32_t t = pack_bf16x2(c * py, 0.0f) & 0xffffu;
+      const int qy = (y & 7) >> 1;
+      const uint32_t keep = (y & 1) ? 0x0000ffffu : 0xffff0000u;
+      const uint32_t ins = (y & 1) ? (t << 16) : t;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = (q == qy) ? ((o[q] & keep) | ins) : o[q];
+    }
+    d[cj] = o;
+  }
 }
 
 // Workgroups of the row loop: one per CU at 1024 threads (a row fills most of a CU's registers),
@@ -339,6 +363,14 @@ hipError_t launch_grpo(const GrpoArgs& a, bool vec, hipStream_t st) {
   timer_mark(LS_KERNEL_GRPO_ROWS, st, true);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(grpo_sum, dim3(1), dim3(256), 0, st, (const float*)a.row_loss, a.T, a.loss_accum);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_rows(const LmRowArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((lm_rows<256>), dim3((unsigned)a.g.T), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(grpo_sum, dim3(1), dim3(256), 0, st, (const float*)a.g.row_loss, a.g.T, a.g.loss_accum);
   return hipGetLastError();
 }
 

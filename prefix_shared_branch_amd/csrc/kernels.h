@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <functional>
+
 #include "../../include/ls_replay.h"
 
 namespace lsr {
@@ -41,6 +43,23 @@ struct GrpoArgs {
 // vec: rows are 16-byte aligned and V % 8 == 0
 hipError_t launch_grpo(const GrpoArgs& a, bool vec, hipStream_t st);
 size_t grpo_workspace_bytes(int64_t T);
+// Row pass of the LM head fused with the loss (grpo_loss.hip): per row, the slab partials of the
+// logits GEMM merged into the log-sum-exp, the row's loss term, log-prob and clip flag, and (when
+// g.dlogits is set) the row's stored e = exp(x - slab max) turned into bf16 dlogits in place; then
+// the fixed-order loss sum. g.logits is unused.
+struct LmRowArgs {
+  GrpoArgs g;
+  const float2* part;  // [T][nslab]: (max, sum exp(x - max)) of each 128-word vocabulary slab
+  int32_t nslab;
+  const float* xtgt;   // [T] the target's logit
+};
+hipError_t launch_lm_rows(const LmRowArgs& a, hipStream_t st);
+// Host side (api.cpp): the rows of responses first .. first+count-1 that fall in the packed range
+// [lo, hi), in batches of at most kMaxResp responses. For each batch, fn(a, brow0) gets a with n, T
+// (the batch's rows), eps, row_end, A and w filled in (everything else zero) and the batch's first
+// packed row. The advantages come from all G rewards. Returns false as soon as fn does.
+bool grpo_batches(int32_t G, const int32_t* R, const float* rewards, float eps, int32_t first, int32_t count,
+                  int64_t lo, int64_t hi, const std::function<bool(GrpoArgs&, int64_t)>& fn);
 // Loss over the packed rows [lo, hi) of responses first .. first+count-1 (host side, api.cpp): the
 // advantages come from all G rewards; `logits`, `dlogits` (or null) and `row_loss` point at row lo,
 // targets / old_logp / logp_out / clipped_out at row 0. Returns an ls_status code.
