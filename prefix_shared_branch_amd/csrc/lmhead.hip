@@ -16,7 +16,7 @@
 //
 // All three products run in the GEMM core below: 4 waves per workgroup, each wave a 128 x 128 block
 // of C as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane), operand tiles of
-// 256 rows x 32 k streamed by direct global -> LDS loads through a 4-stage ring, one workgroup
+// 256 rows x 32 k streamed by direct global -> LDS loads through a ring of LDS stages, one workgroup
 // barrier per k tile. An operand whose rows run along k is read into MFMA fragments with 16-byte
 // LDS reads; one whose rows run along m (or n) with ds_read_b64_tr_b16.
 #include <hip/hip_runtime.h>
@@ -36,12 +36,16 @@ namespace lsr {
 namespace {
 
 constexpr int kBM = 256, kBN = 256, kBK = 32;
-constexpr int kNst = 4;                      // LDS ring stages
+#ifndef LM_STAGES
+#define LM_STAGES 5
+#endif
+constexpr int kNst = LM_STAGES;              // LDS ring stages (all 160 KB of a CU's LDS at 5)
 constexpr int kOpBytes = 256 * kBK * 2;      // one operand's tile: 16 KB
 constexpr int kStage = 2 * kOpBytes;         // A tile, then B tile
 constexpr int kLpw = 8;                      // direct loads per wave per stage (32 KB / 1 KB / 4 waves)
 constexpr uint32_t kOob = 0xFFFFFFF0u;       // buffer offset past every operand: the load returns zeros
 constexpr int kSlabWords = 128;              // vocabulary words per softmax partial (one wave's rows)
+constexpr int kGroupM = 8;                   // m tiles per group of the tile order
 
 enum { kKMajor = 0, kMNMajor = 1 };
 enum { kEpiSoftmax = 0, kEpiStore = 1, kEpiAccum = 2 };
@@ -54,9 +58,8 @@ struct LmGemm {
   int32_t lda, ldb;
   int32_t M, N, K;
   int32_t mt, nt, splits, kts;  // tiles along M and N, K splits, k tiles per split (a multiple of kNst)
-  int32_t order;                // 0: consecutive tiles share an m tile; 1: split, then n tile, then m tile
-  // kEpiStore: splits == 1 -> out16 [M][ldo] bf16; else out + split * split_stride, [M][ldo] fp32.
-  // kEpiAccum: out [M][ldo] fp32 += C.
+  // C is stored transposed, out[n][m]. kEpiStore: splits == 1 -> out16 [N][ldo] bf16; else
+  // out + split * split_stride, [N][ldo] fp32. kEpiAccum: out [N][ldo] fp32 += C^T.
   float* out;
   uint16_t* out16;
   int64_t ldo, split_stride;
@@ -69,7 +72,9 @@ struct LmGemm {
 };
 
 // Workgroup -> (m tile, n tile, split). Workgroups are dealt to the 8 XCDs in turn; each XCD gets a
-// contiguous range of tile ids, so tiles that share an operand stripe share that XCD's L2.
+// contiguous range of tile ids. Within a split, ids run over groups of 8 m tiles: down the group's m
+// tiles, then to the next n tile. The 32 workgroups an XCD runs at once then cover about 8 m tiles x
+// 4 n tiles, whose 12 operand stripes (instead of 32 or more) its L2 serves to all of them.
 struct TileId {
   int m, n, s;
 };
@@ -83,13 +88,11 @@ __device__ __forceinline__ TileId tile_of(const LmGemm& g) {
   TileId t;
   t.s = L / mn;
   const int r = L - t.s * mn;
-  if (g.order == 0) {
-    t.m = r / g.nt;
-    t.n = r - t.m * g.nt;
-  } else {
-    t.n = r / g.mt;
-    t.m = r - t.n * g.mt;
-  }
+  const int gm = r / (kGroupM * g.nt);
+  const int i = r - gm * kGroupM * g.nt;
+  const int gsz = min(kGroupM, g.mt - gm * kGroupM);
+  t.n = i / gsz;
+  t.m = gm * kGroupM + (i - t.n * gsz);
   return t;
 }
 
@@ -158,14 +161,14 @@ struct OperandLoads {
     }
     kstride = LAYOUT == kKMajor ? 2u : (uint32_t)ld * 2u;
   }
-  // k0 = INT_MAX loads nothing (zeros)
+  // piece q of the tile at k0 (k0 = INT_MAX loads nothing: zeros)
+  __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, char* dst, int wv, int k0, int q) const {
+    const uint32_t off = k0 < klim[q] ? base[q] + (uint32_t)k0 * kstride : kOob;
+    lds_dma16_buf(rs, off, dst + (wv * 4 + q) * 1024);
+  }
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* dst, int wv, int k0) const {
-    const uint32_t koff = (uint32_t)k0 * kstride;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t off = k0 < klim[q] ? base[q] + koff : kOob;
-      lds_dma16_buf(rs, off, dst + (wv * 4 + q) * 1024);
-    }
+    for (int q = 0; q < 4; ++q) issue_one(rs, dst, wv, k0, q);
   }
 };
 
@@ -176,6 +179,7 @@ __global__ __launch_bounds__(256) void lm_gemm(LmGemm g) {
   __shared__ __attribute__((aligned(1024))) char st1[kStage];
   __shared__ __attribute__((aligned(1024))) char st2[kStage];
   __shared__ __attribute__((aligned(1024))) char st3[kStage];
+  __shared__ __attribute__((aligned(1024))) char st4[kNst > 4 ? kStage : 16];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wv >> 1, wn = wv & 1;
@@ -222,35 +226,58 @@ __global__ __launch_bounds__(256) void lm_gemm(LmGemm g) {
   issue(1, st1);
   issue(2, st2);
   issue(3, st3);
+  if constexpr (kNst > 4) issue(4, st4);
   wait_vmem_le<(kNst - 1) * kLpw>();
   bare_barrier();
   Frag f0, f1;
   frags(f0, st0, 0);
   wait_lds();
-  // One k tile: step 0's MFMAs overlap the reads of step 1; then, once every wave has read this
-  // tile and the next tile has landed, this stage is refilled (tile kt + 4) and the next tile's
-  // step-0 reads overlap step 1's MFMAs.
-  // (scheduling barriers keep each group of reads ahead of the MFMAs it overlaps)
+  // One k tile in two steps of 16 MFMAs. Step 0 runs on f0 while f1 is read (step 1 of this tile);
+  // then, once every wave has read this tile's stage and the next tile has landed, step 1 runs on f1
+  // while the stage is refilled (tile kt + kNst) and f0 is read (step 0 of the next tile). Each
+  // LDS read and direct load is issued between two MFMAs, so the wave issues them while the matrix
+  // core is busy instead of in a burst at the barrier. (Scheduling barriers hold this order.)
+  auto read_one = [&](Frag& f, const char* s, int step, int p) {
+    if (p < 4) f.a[p] = read_frag<LA>(s, lo, wm, p, step);
+    else f.b[p - 4] = read_frag<LB>(s + kOpBytes, lo, wn, p - 4, step);
+  };
+  auto mfma_pair = [&](const Frag& f, int p) {
+#pragma unroll
+    for (int q = 2 * p; q < 2 * p + 2; ++q) acc[q >> 2][q & 3] = mfma32(f.a[q >> 2], f.b[q & 3], acc[q >> 2][q & 3]);
+  };
   auto tile = [&](int kt, char* cur, char* nxt) {
-    frags(f1, cur, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(f0);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      read_one(f1, cur, 1, p);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_pair(f0, p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     wait_lds();
     wait_vmem_le<(kNst - 2) * kLpw>();
     bare_barrier();
-    issue(kt + kNst, cur);
-    frags(f0, nxt, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(f1);
-    __builtin_amdgcn_sched_barrier(0);
+    const int k0 = kt + kNst < kts ? (kt0 + kt + kNst) * kBK : INT_MAX;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      if (p < 4) la.issue_one(ra, cur, wv, k0, p);
+      else lb.issue_one(rb, cur + kOpBytes, wv, k0, p - 4);
+      read_one(f0, nxt, 0, p);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_pair(f1, p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     wait_lds();
   };
   for (int kt = 0; kt < kts; kt += kNst) {
     tile(kt, st0, st1);
     tile(kt + 1, st1, st2);
     tile(kt + 2, st2, st3);
-    tile(kt + 3, st3, st0);
+    if constexpr (kNst > 4) {
+      tile(kt + 3, st3, st4);
+      tile(kt + 4, st4, st0);
+    } else {
+      tile(kt + 3, st3, st0);
+    }
   }
   wait_vmem();
 
@@ -337,42 +364,65 @@ __global__ __launch_bounds__(256) void lm_gemm(LmGemm g) {
     };
     epi(std::true_type{});
   } else {
-    // stores through a buffer resource over this wave's 128 rows of the output: rows past M fall
-    // outside it and columns past N get an offset outside it, so no store needs a branch
-    constexpr int kEsz = (EPI == kEpiStore) ? 4 : 4;
-    const int mbase = m0 + wm * 128;
-    const int esz = (EPI == kEpiStore && g.splits == 1) ? 2 : kEsz;
-    const int64_t rows_left = (int64_t)g.M - mbase;
+    // C is stored transposed, out[n][m]: a lane's registers 4j .. 4j+3 are 4 consecutive m of one n,
+    // one 16-byte (fp32) or 8-byte (bf16) access. The accesses go through a buffer resource over this
+    // wave's 128 rows n of the output: rows past N fall outside it and columns past M get an offset
+    // outside it, so no access needs a branch.
+    const bool b16 = EPI == kEpiStore && g.splits == 1;
+    const int esz = b16 ? 2 : 4;
+    const int nbase = n0 + wn * 128;
+    const int64_t rows_left = (int64_t)g.N - nbase;
     const int64_t span = rows_left <= 0 ? 0 : rows_left * g.ldo * esz;
-    char* obase = (EPI == kEpiStore && g.splits == 1)
-                      ? reinterpret_cast<char*>(g.out16) + (int64_t)mbase * g.ldo * 2
-                      : reinterpret_cast<char*>(g.out) + ((EPI == kEpiStore ? si * g.split_stride : 0) +
-                                                          (int64_t)mbase * g.ldo) * 4;
+    char* obase = b16 ? reinterpret_cast<char*>(g.out16) + (int64_t)nbase * g.ldo * 2
+                      : reinterpret_cast<char*>(g.out) +
+                            ((EPI == kEpiStore ? si * g.split_stride : 0) + (int64_t)nbase * g.ldo) * 4;
     const __amdgpu_buffer_rsrc_t ro = buf_rsrc(obase, span);
-    const int nw = n0 + wn * 128 + c;
+    const uint32_t rowb = (uint32_t)g.ldo * (uint32_t)esz;
+    const int mw = m0 + wm * 128 + 4 * h;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int nb = 0; nb < 4; ++nb) {
+      const uint32_t orow = (uint32_t)(nb * 32 + c) * rowb;
+      if constexpr (EPI == kEpiAccum) {
+        // all 16 loads of the column block first, then the adds and stores
+        f32x4 v[4][4];
+        uint32_t off[4][4];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int n = nw + nb * 32;
-        const uint32_t rowb = (uint32_t)g.ldo * (uint32_t)esz;
-        const uint32_t o0 = n < g.N ? ((uint32_t)(4 * h + mb * 32) * rowb + (uint32_t)n * esz) : kOob;
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t o = o0 == kOob ? kOob : o0 + (uint32_t)(8 * (r >> 2) + (r & 3)) * rowb;
-          if constexpr (EPI == kEpiAccum) {
-            const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, (int)o, 0, 0));
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v + acc[mb][nb][r]), ro, (int)o, 0, 0);
-          } else if (esz == 2) {
-            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16x2(acc[mb][nb][r], 0.0f) & 0xffffu), ro,
-                                                  (int)o, 0, 0);
-          } else {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mb][nb][r]), ro, (int)o, 0, 0);
+          for (int i = 0; i < 4; ++i) {
+            const int m = mw + mb * 32 + 8 * i;
+            off[mb][i] = m < g.M ? orow + (uint32_t)m * 4u : kOob;
+            v[mb][i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, (int)off[mb][i], 0, 0));
           }
-        }
-        // one 32 x 32 block at a time: its offsets and loaded values are all that is live
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f32x4 w = v[mb][i];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] += acc[mb][nb][4 * i + q];
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, (int)off[mb][i], 0, 0);
+          }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = mw + mb * 32 + 8 * i;
+            const uint32_t o = m < g.M ? orow + (uint32_t)m * (uint32_t)esz : kOob;
+            const f32x16& a = acc[mb][nb];
+            if (b16) {
+              const u32x2 w = {pack_bf16x2(a[4 * i], a[4 * i + 1]), pack_bf16x2(a[4 * i + 2], a[4 * i + 3])};
+              __builtin_amdgcn_raw_buffer_store_b64(w, ro, (int)o, 0, 0);
+            } else {
+              const f32x4 w = {a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]};
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, (int)o, 0, 0);
+            }
+          }
       }
+      // one column block at a time: its offsets and loaded values are all that is live
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -533,7 +583,6 @@ int ls_grpo_lmhead_loss(void* stream, int32_t V, int32_t d, int32_t G, const int
     g.nt = cdiv(tc, kBN);
     g.splits = 1;
     g.kts = round_up(cdiv(d, kBK), kNst);
-    g.order = 0;
     g.part = part;
     g.nslab = lay.nslab;
     g.xtgt = xtgt;
@@ -563,29 +612,29 @@ int ls_grpo_lmhead_loss(void* stream, int32_t V, int32_t d, int32_t G, const int
     if (!ok) return LS_ERR_HIP;
     if (!grad) continue;
 
-    // 3. dH_c [tc][d] = dlogits [tc][V] W [V][d]: split over V, partials summed in split order
+    // 3. dH_c [tc][d] = dlogits [tc][V] W [V][d], formed as C = W^T dlogits^T [d][tc] and stored
+    //    transposed; split over V, the partials summed in split order
     LmGemm h = {};
-    h.a = ebuf;
-    h.a_bytes = e_bytes;
-    h.lda = V;
-    h.b = Wb;
-    h.b_bytes = w_bytes;
-    h.ldb = d;
-    h.M = tc;
-    h.N = d;
+    h.a = Wb;
+    h.a_bytes = w_bytes;
+    h.lda = d;
+    h.b = ebuf;
+    h.b_bytes = e_bytes;
+    h.ldb = V;
+    h.M = d;
+    h.N = tc;
     h.K = V;
-    h.mt = cdiv(tc, kBM);
-    h.nt = cdiv(d, kBN);
+    h.mt = cdiv(d, kBM);
+    h.nt = cdiv(tc, kBN);
     // the partial buffer holds lay.splits x lay.tc rows of d: a shorter last chunk may take more splits
     const int64_t cap = lay.splits > 1 ? (int64_t)lay.splits * lay.tc : 0;
     const int max_splits = (int)std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, cap / tc));
     dh_split(tc, V, d, max_splits, &h.splits, &h.kts);
-    h.order = 1;
     h.out = dhpart;
     h.out16 = dHb + c0 * d;
     h.ldo = d;
     h.split_stride = (int64_t)tc * d;
-    if (go<kKMajor, kMNMajor, kEpiStore>(h, st) != hipSuccess) return LS_ERR_HIP;
+    if (go<kMNMajor, kKMajor, kEpiStore>(h, st) != hipSuccess) return LS_ERR_HIP;
     if (h.splits > 1) {
       const int64_t n4 = (int64_t)tc * d / 4;
       const int64_t grid = std::min<int64_t>((n4 + 255) / 256, 4096);
@@ -594,22 +643,22 @@ int ls_grpo_lmhead_loss(void* stream, int32_t V, int32_t d, int32_t G, const int
       if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
     }
 
-    // 4. dW [V][d] += dlogits^T H_c: both operands read along their rows (k = tokens)
+    // 4. dW [V][d] += dlogits^T H_c, formed as C = H_c^T dlogits [d][V] and added in transposed;
+    //    both operands are read along their rows (k = tokens)
     LmGemm w = {};
-    w.a = ebuf;
-    w.a_bytes = e_bytes;
-    w.lda = V;
-    w.b = Hc;
-    w.b_bytes = h_bytes;
-    w.ldb = d;
-    w.M = V;
-    w.N = d;
+    w.a = Hc;
+    w.a_bytes = h_bytes;
+    w.lda = d;
+    w.b = ebuf;
+    w.b_bytes = e_bytes;
+    w.ldb = V;
+    w.M = d;
+    w.N = V;
     w.K = tc;
-    w.mt = cdiv(V, kBM);
-    w.nt = cdiv(d, kBN);
+    w.mt = cdiv(d, kBM);
+    w.nt = cdiv(V, kBN);
     w.splits = 1;
     w.kts = round_up(cdiv(tc, kBK), kNst);
-    w.order = 0;
     w.out = dW_accum;
     w.ldo = d;
     if (go<kMNMajor, kMNMajor, kEpiAccum>(w, st) != hipSuccess) return LS_ERR_HIP;
