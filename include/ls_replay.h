@@ -227,31 +227,39 @@ int ls_grpo_token_loss_noalloc(void* stream, int32_t V, int32_t G,
                                void* dlogits, float* loss_accum,
                                float* logp_out, uint8_t* clipped_out);
 
-/* Workspace bytes for ls_grpo_lmhead_loss over T rows (written to *bytes): the logits and
- * dlogits of one chunk of at most 2048 tokens plus per-row loss terms. */
+/* Workspace bytes for ls_grpo_lmhead_loss over T rows (written to *bytes): for one chunk of at
+ * most 4096 tokens (fewer where V > 262144, so that a chunk's [tokens, V] bf16 buffer stays under
+ * 2 GiB) the dlogits buffer, the per-slab softmax partials, target logits and per-row loss terms,
+ * and the split partials of dH. */
 int ls_grpo_lmhead_workspace_bytes(int64_t T, int32_t V, int32_t d, size_t* bytes);
 
 /* LM head fused with the clipped-GRPO token objective: the objective above (LongStraw study notes
- * §1-1, L_policy, over the vocabulary) applied to logits = H W^T, formed chunk by chunk (2048
- * tokens at a time) so that a response's full [T, V] logits never exist. Per chunk: a library GEMM
- * forms the bf16 logits (fp32 accumulation), the loss kernel of ls_grpo_token_loss forms the loss
- * share, log-probs, clip flags and bf16 dlogits, and two more GEMMs form
- *   dH = dlogits W (bf16, overwritten)  and  dW += dlogits^T H (fp32, added in place).
- * The GEMMs run on rocBLAS (atomics disabled, run-to-run identical), whose handle the library
- * creates per device on first use; this entry point therefore allocates on its first call.
- *  V, d      vocabulary size (8 .. 2^24, a multiple of 8) and hidden size (a multiple of 8);
- *            V * d < 2^31. Other values: LS_ERR_UNSUPPORTED.
+ * §1-1, L_policy, over the vocabulary) applied to logits = H W^T, formed chunk by chunk so that a
+ * response's [T, V] logits never exist. Per chunk, all on this library's gfx950 kernels:
+ *   a GEMM forms the logits in fp32 and, in its epilogue, rounds them to bf16 and reduces them per
+ *   token and 128-word vocabulary slab to (max, sum of exp(x - max)) and the target's logit; the
+ *   logits are never written to memory. With gradients, the epilogue also stores
+ *   e = exp(x - slab max) (bf16) in the workspace's dlogits buffer;
+ *   a row kernel merges each token's slab partials into its log-sum-exp, forms the loss share,
+ *   log-prob and clip flag as ls_grpo_token_loss does, and rescales the stored e in place into
+ *   bf16 dlogits (the one-hot term from the target's logit);
+ *   two more GEMMs form dH = dlogits W (bf16, overwritten; split over V, fp32 partials summed in a
+ *   fixed order) and dW += dlogits^T H (fp32, added in place).
+ * Results are run-to-run identical (fixed summation orders, no atomics). Nothing is allocated.
+ * The dlogits differ from ls_grpo_token_loss's on the same logits by the extra bf16 rounding of e.
+ *  V, d      vocabulary size (8 .. 2^24, a multiple of 8) and hidden size (8 .. 65536, a multiple
+ *            of 8); V * d < 2^31. Other values: LS_ERR_UNSUPPORTED.
  *  G, R, rewards, eps, first, count  as for ls_grpo_token_loss.
  *  H         device bf16 [T, d] hidden states of the selected responses' tokens, packed.
  *  W         device bf16 [V, d] vocabulary projection; read only.
  *  targets, old_logp, loss_accum, logp_out, clipped_out  as for ls_grpo_token_loss.
  *  dH        device bf16 [T, d], overwritten with dL/dH; and
  *  dW_accum  device fp32 [V, d]; this call ADDS dL/dW (the caller zeroes it once per step).
- *            Both NULL: scoring only (no dlogits, no gradient GEMMs). Exactly one NULL:
+ *            Both NULL: scoring only (no e stores, no gradient GEMMs). Exactly one NULL:
  *            LS_ERR_INVALID_ARG.
  *  workspace >= ls_grpo_lmhead_workspace_bytes(T, V, d), 256-byte aligned.
- * H, W, dH and dW_accum must be 16-byte aligned. Calls that overlap on one device serialise on
- * the library's lock while they enqueue work; the work itself runs on `stream`. */
+ * H, W, dH and dW_accum must be 16-byte aligned. The work runs on `stream`; calls that overlap
+ * on one device must use separate workspaces. */
 int ls_grpo_lmhead_loss(void* stream, int32_t V, int32_t d, int32_t G,
                         const int32_t* R, const float* rewards, float eps,
                         int32_t first, int32_t count,

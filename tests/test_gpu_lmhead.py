@@ -118,3 +118,86 @@ def test_lmhead_scoring_only_and_accumulation():
     torch.cuda.synchronize()
     _, _, dW1, _, _ = _run(s)
     assert torch.allclose(dW, 2 * dW1, rtol=1e-6, atol=0)   # the same sums added twice
+
+
+def test_lmhead_ragged_shapes():
+    """Hidden size 40 (a k tail of 8 in the logits product), V = 1,000 (a partial 128-word slab and a
+    partial vocabulary tile), token counts that fill no tile."""
+    cfg = inputs.replace(inputs.CONFIGS["tiny"], V=1000)
+    s = _setup(cfg, [70, 131], 40)
+    _check(s, _run(s))
+
+
+def test_lmhead_many_short_responses():
+    """70 responses of 1-3 tokens in one chunk: the row kernel runs in batches of at most 64 responses."""
+    R = [1 + (i % 3) for i in range(70)]
+    s = _setup(inputs.CONFIGS["tiny"], R, 64)
+    _check(s, _run(s))
+
+
+def test_lmhead_two_chunks():
+    """4,500 tokens: two chunks of the call, a response across their boundary, and a shorter last chunk
+    (its dH product split differently)."""
+    s = _setup(inputs.CONFIGS["tiny"], [3000, 1500], 64)
+    _check(s, _run(s))
+
+
+def test_lmhead_full_shape_sampled_rows():
+    """The benchmark's shape: one response of 4,096 tokens, d = 5,120, V = 151,936, in the launch
+    configuration the benchmark times. The oracle forms the logits of a few sampled tokens (fp64, W
+    taken in row blocks) and checks their log-probs, clip flags and dH rows."""
+    import torch
+    from prefix_shared_branch_amd import lsreplay as L
+    cfg = inputs.CONFIGS["million"]
+    R0, d = 4096, cfg.Hq * cfg.Dqk
+    R = np.array([R0] + [int(r) for r in inputs.response_lengths(cfg)[1:]], dtype=np.int32)
+    G = len(R)
+    rewards = inputs.rewards(cfg)
+    hb = inputs.hidden(cfg, 0, 0, R0, d)
+    y = inputs.targets(cfg, 0, R0)
+    rows = np.array([0, 1, 777, 2048, 3001, 4095])
+    Hs = inputs.bf16_bits_to_f64(hb[rows])
+    blk = 16384
+    x = np.zeros((len(rows), cfg.V))
+    for v0 in range(0, cfg.V, blk):
+        Wb = inputs.bf16_bits_to_f64(inputs.normal_bf16_rows(cfg.seed, inputs.TID_PROJ, 0, v0, min(cfg.V, v0 + blk), d,
+                                                              cfg.logit_sigma / float(np.sqrt(d))))
+        x[:, v0:v0 + Wb.shape[0]] = Hs @ Wb.T
+    xr = lmhead.round_bf16(x)
+    noise = inputs.old_logp_noise(cfg, 0, R0)
+    old = np.full(R0, -12.0, dtype=np.float32)
+    old[rows] = (grpo.token_logp(xr, y[rows]) + noise[rows]).astype(np.float32)
+    # the sampled rows through the oracle: weight 1/(G R0) and advantage A_0 enter only as their
+    # product (a positive factor), so each row is a one-token response with A scaled to match
+    A0 = grpo.advantages(rewards)[0]
+    dl = np.zeros_like(x)
+    logp_ref = np.zeros(len(rows))
+    clip_ref = np.zeros(len(rows), dtype=bool)
+    for k in range(len(rows)):
+        _, dlk, lpk, ck = grpo.grpo_token_loss(xr[k:k + 1], y[rows[k:k + 1]], old[rows[k:k + 1]], [1], [0.0], 1,
+                                               cfg.eps, 0, 1, A=[A0 / (G * R0)])
+        dl[k], logp_ref[k], clip_ref[k] = dlk[0], lpk[0], ck[0]
+    dH_ref = np.zeros((len(rows), d))
+    for v0 in range(0, cfg.V, blk):
+        Wb = inputs.bf16_bits_to_f64(inputs.normal_bf16_rows(cfg.seed, inputs.TID_PROJ, 0, v0, min(cfg.V, v0 + blk), d,
+                                                              cfg.logit_sigma / float(np.sqrt(d))))
+        dH_ref += dl[:, v0:v0 + Wb.shape[0]] @ Wb
+    H = dev_bf16(hb)
+    W = dev_bf16(inputs.projection(cfg, d))
+    dW = torch.zeros(cfg.V, d, dtype=torch.float32, device="cuda")
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    logp = torch.empty(R0, dtype=torch.float32, device="cuda")
+    clip = torch.empty(R0, dtype=torch.uint8, device="cuda")
+    dH = L.ls_grpo_lmhead_loss(H, W, torch.from_numpy(y).cuda(), torch.from_numpy(old).cuda(), R, rewards, cfg.eps,
+                               0, 1, loss, dW_accum=dW, logp_out=logp, clipped_out=clip)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dW).all() and torch.isfinite(dH.float()).all()
+    xt = x[np.arange(len(rows)), y[rows]]
+    step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(xt), 1e-30))) - 7)
+    slack = np.where(_ambiguous(xt), step, 0.0)
+    got_lp = host_f64(logp)[rows]
+    assert np.all(np.abs(got_lp - logp_ref) <= 1e-4 + slack), np.abs(got_lp - logp_ref)
+    rho = np.exp(logp_ref - old[rows].astype(np.float64))
+    sure = (np.abs(rho - (1 - cfg.eps)) > 1e-3) & (np.abs(rho - (1 + cfg.eps)) > 1e-3)
+    np.testing.assert_array_equal(host_f64(clip)[rows].astype(bool)[sure], clip_ref[sure])
+    check_bf16_out(host_f64(dH)[rows][:, None, :], dH_ref[:, None, :], "dH rows", literal_abs=False)
