@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--no-memory-receipt", action="store_true",
                     help="skip the peak-memory receipt (G = 2 vs G = 8 at mid, G = 2 vs G = 16 at million)")
     ap.add_argument("--memory-receipt-only", action="store_true", help="only run the peak-memory receipt")
+    ap.add_argument("--no-receipts", action="store_true",
+                    help="skip the attention receipts of the other workloads (Mid, Long, latent KV)")
+    ap.add_argument("--receipts-only", action="store_true", help="only run the attention receipts")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of known size (HBM counter calibration)")
     return ap.parse_args()
@@ -151,6 +154,62 @@ class Workload:
         self.loss.zero_()
         for i in range(self.G):
             self.response(i, times)
+
+
+def attn_receipt(cfg, n_resp):
+    """Attention throughput of another workload: forward + backward with exact prompt gradients for
+    its first n_resp responses, serially, after one untimed warm-up call on response 0. Each
+    response's inputs are generated before its calls, outside the timed calls (no logits: the loss is
+    measured by the main line)."""
+    import torch
+    from prefix_shared_branch_amd import lsreplay as L
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    kp = to_dev(inputs.prompt_k(cfg))
+    vp = kp[:, :, :cfg.Dv] if cfg.mla else to_dev(inputs.prompt_v(cfg))
+    dkp = torch.zeros(cfg.P, cfg.Hkv, cfg.Dqk, dtype=torch.float32, device="cuda")
+    dvp = torch.zeros(cfg.P, cfg.Hkv, cfg.Dv, dtype=torch.float32, device="cuda")
+    R = inputs.response_lengths(cfg)[:n_resp]
+    cu = inputs.cu_seqlens(inputs.response_lengths(cfg))
+    t_fwd = t_bwd = 0.0
+    alg = 0
+    for k in range(-1, n_resp):
+        i = max(k, 0)
+        r, t0 = int(R[i]), int(cu[i])
+        q = to_dev(inputs.suffix_q(cfg, t0, t0 + r))
+        ks = to_dev(inputs.suffix_k(cfg, t0, t0 + r))
+        vs = ks[:, :, :cfg.Dv] if cfg.mla else to_dev(inputs.suffix_v(cfg, t0, t0 + r))
+        do = to_dev(inputs.suffix_do(cfg, t0, t0 + r))
+        lo = torch.empty(r, cfg.Hq, cfg.Dv, dtype=torch.bfloat16, device="cuda")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        o, lse = L.ls_replay_attn_fwd(q, ks, vs, kp, vp, [0, r], cfg.scale, o_lo=lo)
+        ev[1].record()
+        L.ls_replay_attn_bwd(q, ks, vs, kp, vp, [0, r], o, lse, do, dkp, dvp, cfg.scale, o_lo=lo)
+        ev[2].record()
+        torch.cuda.synchronize()
+        if k >= 0:
+            t_fwd += ev[0].elapsed_time(ev[1])
+            t_bwd += ev[1].elapsed_time(ev[2])
+            alg += flops(cfg, r)[0]
+        del q, ks, vs, do, lo, o, lse
+    tokens = int(R.sum())
+    t = (t_fwd + t_bwd) * 1e-3
+    out = {"workload": cfg.name, "P": cfg.P, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Dqk": cfg.Dqk, "Dv": cfg.Dv,
+           "responses": [int(x) for x in R], "tokens_per_s": tokens / t, "alg_TFLOPs": alg / t / 1e12,
+           "alg_frac_peak": alg / t / PEAK_BF16, "fwd_ms": t_fwd, "bwd_ms": t_bwd}
+    log(f"attention receipt {cfg.name}: {out['tokens_per_s']:.0f} tok/s, {out['alg_TFLOPs']:.0f} TFLOP/s")
+    del kp, vp, dkp, dvp
+    torch.cuda.empty_cache()
+    return out
+
+
+def receipts():
+    """Attention receipts of the other named workloads: Mid (all 8 responses), Long (its first two
+    responses as drawn, 2,461 and 2,414 tokens) and the latent-KV config at P = 262,144 (two
+    responses of 4,096 tokens)."""
+    mla = inputs.replace(inputs.CONFIGS["mla"], name="mla_p262k", P=262144, G=2, R_lo=4096, R_hi=4096)
+    return [attn_receipt(inputs.CONFIGS["mid"], 8), attn_receipt(inputs.CONFIGS["long"], 2), attn_receipt(mla, 2)]
 
 
 def memory_receipt(cfg, group_sizes):
@@ -369,6 +428,9 @@ def main():
     L.lib()   # fail loudly if the HIP library is missing
     cfg = inputs.CONFIGS[args.workload]
     torch.cuda.set_device(0)
+    if args.receipts_only:
+        print(json.dumps(receipts()), flush=True)
+        return
     if args.memory_receipt_only:
         print(json.dumps([memory_receipt(inputs.CONFIGS["mid"], [2, 8]),
                           memory_receipt(inputs.CONFIGS["million"], [2, 16])]), flush=True)
@@ -478,6 +540,8 @@ def main():
     }
     del wl
     torch.cuda.empty_cache()
+    if not args.no_receipts:
+        out["detail"]["receipts"] = receipts()
     if not args.no_memory_receipt:
         # outside the timed region: each response's buffers live only during its own replay
         out["detail"]["memory_receipt"] = [memory_receipt(inputs.CONFIGS["mid"], [2, 8]),
