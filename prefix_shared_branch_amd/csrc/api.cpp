@@ -284,6 +284,9 @@ int bwd_impl(void* stream, const ls_attn_desc* desc, const void* Kp, const void*
 
 namespace lsr {
 
+// one fp32 loss term per row, summed in a fixed order by grpo_sum
+size_t grpo_workspace_bytes(int64_t T) { return (size_t)((T * 4 + 255) / 256 * 256); }
+
 bool grpo_batches(int32_t G, const int32_t* R, const float* rewards, float eps, int32_t first, int32_t count,
                   int64_t lo, int64_t hi, const std::function<bool(GrpoArgs&, int64_t)>& fn) {
   // group advantage in float64 on the host: A_i = (r_i - mean) / (std_pop + 1e-6)

@@ -335,8 +335,6 @@ hipError_t go_vec(const GrpoArgs& a, hipStream_t st) {
 
 }  // namespace
 
-size_t grpo_workspace_bytes(int64_t T) { return (size_t)((T * 4 + 255) / 256 * 256); }
-
 hipError_t launch_grpo(const GrpoArgs& a, bool vec, hipStream_t st) {
   hipError_t e = hipSuccess;
   timer_mark(LS_KERNEL_GRPO_ROWS, st, false);
