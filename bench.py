@@ -361,7 +361,7 @@ def cpu_baseline(cfg, rows):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {"replay_bwd_dkdv_prompt": ["replay_attn_dkdv.hip", "common.h", "kernels.h"]}
+KERNEL_SOURCES = {"replay_bwd_dkdv_prompt": ["replay_attn_dkdv64.hip", "common.h", "kernels.h"]}
 
 
 def source_digest(kernel):
@@ -511,7 +511,7 @@ def main():
                    "vocab": cfg.V, "eps": cfg.eps, "gradient_semantics": "exact-prompt-grad"},
         "roofline": {"bound": "mfma", "achieved": roof_ach, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
                      "frac": roof_ach / (PEAK_BF16 / 1e12), "traffic": traffic,
-                     "kernel": "replay_bwd_dkdv (prompt keys)", "avg_ms": dkdv_ms, "launches": dk_launches,
+                     "kernel": "replay_bwd_dkdv_w64 (prompt keys)", "avg_ms": dkdv_ms, "launches": dk_launches,
                      "alg_flops_per_launch": dkdv_alg},
         "detail": {
             "attn_tokens_per_s": tokens / ((t_fwd + t_bwd) * 1e-3),

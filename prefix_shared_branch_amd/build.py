@@ -14,7 +14,8 @@ LIB = os.path.join(PKG, "liblsreplay.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_SOURCES = ["grpo_loss.hip", "replay_attn_fwd.hip", "replay_attn_bwd.hip", "replay_attn_dq.hip", "replay_attn_dkdv.hip", "pack.hip",
-               "replay_attn_wide_fwd.hip", "replay_attn_wide_bwd.hip", "noalloc.hip", "lmhead.hip"]
+               "replay_attn_wide_fwd.hip", "replay_attn_wide_bwd.hip", "noalloc.hip", "lmhead.hip",
+               "replay_attn_dkdv64.hip"]
 CXX_SOURCES = ["api.cpp", "attn_plan.cpp", "timer.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 # the packed-fp32 feature stays off: every v_pk_*_f32 is left out of the kernels
@@ -25,6 +26,7 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "
 SOURCE_FLAGS = {"replay_attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                 "replay_attn_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                 "replay_attn_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "replay_attn_dkdv64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                 "replay_attn_wide_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

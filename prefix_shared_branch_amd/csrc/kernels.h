@@ -245,6 +245,9 @@ hipError_t launch_bwd_dq_wide(BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_dkdv_wide(BwdArgs& a, hipStream_t st);
 // dK/dV part (replay_attn_dkdv.hip): query-row packing, prompt and response dK/dV kernels
 hipError_t launch_bwd_dkdv(BwdArgs& a, int Dqk, int Dv, hipStream_t st);
+// prompt-key dK/dV at head dim 128 with 64 keys per wave (replay_attn_dkdv64.hip); same arguments and
+// results as the prompt launch of launch_bwd_dkdv, after the same packing
+hipError_t launch_dkdv_prompt_w64(BwdArgs& a, hipStream_t st);
 
 // Kernel timer hooks (timer.cpp): bracket a launch; no-ops unless the timer is armed for `kernel`
 // (an ls_kernel_id value).

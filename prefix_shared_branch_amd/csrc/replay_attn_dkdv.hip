@@ -6,10 +6,11 @@
 // With P = exp(S scale - LSE), dP = dO V^T, Delta = rowsum(dO * O), dS = P (dP - Delta):
 //   dV_j += sum_rows P_rj dO_r,   dK_j += scale sum_rows dS_rj Q_r.
 //
-// replay_bwd_dkdv: key-tile owner. One workgroup = 8 waves x 32 keys of one kv head, two waves per
+// replay_bwd_dkdv: key-tile owner. One workgroup = 4 waves x 32 keys of one kv head, one wave per
 // SIMD; each wave keeps its keys' K and V fragments and its dK^T, dV^T accumulators in registers for
-// the whole sweep over every query row that sees those keys, 32 GQA-packed rows per step. While one
-// wave of a SIMD forms P and dS on the VALU, the other issues its MFMAs. The rows were repacked per
+// the whole sweep over every query row that sees those keys, 32 GQA-packed rows per step. It serves
+// the response keys and head dim 64; the prompt keys at head dim 128 (the long sweeps) run the
+// 64-keys-per-wave form in replay_attn_dkdv64.hip, on the same packed rows. The rows were repacked per
 // kv head before the launch (pack.hip): row-major Q and dO (A operands of S = Q K^T and
 // dP = dO V^T) and dimension-major, slot-permuted Q^T and dO^T (A operands of dV^T += dO^T P and
 // dK^T += Q^T dS, whose B operands come straight from the S / dP accumulators), plus each row's LSE
@@ -34,7 +35,7 @@ namespace {
 
 template <int D, int DV, int NW_>
 struct DkvCfg {
-  static constexpr int NW = NW_;              // waves per workgroup (8: two per SIMD)
+  static constexpr int NW = NW_;              // waves per workgroup (4: one per SIMD)
   static constexpr int BN = NW * 32;          // keys per workgroup (32 per wave)
   static constexpr int BR = 32;               // packed query rows per step
   static constexpr int QCH = D / 8;           // 16-byte chunks per Q row
@@ -66,15 +67,12 @@ struct DkvCfg {
   static constexpr int VB = DV / 32;
 };
 
-// Prompt keys at head dim 128: 8 waves (256 keys per workgroup, thousands of workgroups). Response keys
-// (a response has few key tiles) and head dim 64 (whose 16 tile loads per step do not split into
-// whole tiles per wave over 8 waves): 4 waves, 128 keys. The plan's key tiles match (attn_plan.cpp).
-template <int D, bool PROMPT>
-constexpr int dkdv_waves() { return (PROMPT && D == 128) ? 8 : 4; }
+// 4 waves, 128 keys per workgroup; the plan's key tiles match (attn_plan.cpp).
+constexpr int kDkvWaves = 4;
 
 template <int D, int DV, bool PROMPT>
-__global__ __launch_bounds__((64 * dkdv_waves<D, PROMPT>()), 1) void replay_bwd_dkdv(BwdArgs a) {
-  using C = DkvCfg<D, DV, dkdv_waves<D, PROMPT>()>;
+__global__ __launch_bounds__(64 * kDkvWaves, 1) void replay_bwd_dkdv(BwdArgs a) {
+  using C = DkvCfg<D, DV, kDkvWaves>;
   __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE];
 
   const AttnGeom& G = a.geo;
@@ -180,10 +178,9 @@ __global__ __launch_bounds__((64 * dkdv_waves<D, PROMPT>()), 1) void replay_bwd_
   auto issue_step = [&](int m0, char* buf) {
 #pragma unroll
     for (int u = 0; u < C::JPW; ++u) issue_load(u, m0, buf);
-    // row terms in dwords: waves 0-3 load the four 256-byte quarters, waves 4-7 load the same bytes
-    // to the same places (identical data; every wave issues the same number of loads)
-    const int qtr = wv & 3;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (LSR_LDS void*)(buf + C::OFF_LD + qtr * 256), 4, qtr * 256 + lane * 4,
+    // row terms in dwords: wave wv loads the 256-byte quarter wv
+    static_assert(C::NW == 4, "one row-term quarter per wave");
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (LSR_LDS void*)(buf + C::OFF_LD + wv * 256), 4, wv * 256 + lane * 4,
                                              m0 * 32, 0, 0);
   };
 
@@ -230,19 +227,14 @@ __global__ __launch_bounds__((64 * dkdv_waves<D, PROMPT>()), 1) void replay_bwd_
   constexpr int NX = NQ + NO, NF = NX + NOT + NQT;
   constexpr int PD = 2;
 
-  // Four-stage ring; the two wave groups (waves 0-3 and 4-7, one of each per SIMD) run half a step
-  // apart, so that one group's VALU-heavy phase X overlaps the other's MFMA-only phase Y. Every
-  // phase starts at a workgroup barrier; the trailing group passes one extra barrier at the start and
-  // the leading group one at the end, so both pass the same number. At the barrier before the
-  // leading group's X(j) the trailing group stands before Y(j - 1). Hence:
-  //  * step j's tiles must be complete before the trailing group's Y(j - 1): each wave waits for its
-  //    own loads of step j + 1 at the end of its X(j) (loads of steps j + 1 and j + 2 in flight);
-  //  * a wave issues its loads of step j + 3 at the barrier before its Y(j), into the stage of step
-  //    j - 1, which both groups have finished reading by then (the trailing group is before X(j));
-  //    each wave's reads of a stage have returned before the barrier that precedes its next X.
+  // Four-stage ring; every phase starts at a workgroup barrier:
+  //  * each wave waits for its own loads of step j + 1 at the end of its X(j) (loads of steps j + 1
+  //    and j + 2 in flight), so step j + 1's tiles are complete at the barrier before X(j + 1);
+  //  * a wave issues its loads of step j + 3 at the barrier before Y(j), into the stage of step
+  //    j - 1, which every wave has finished reading by then (each wave's reads of a stage have
+  //    returned before the barrier that precedes its next X).
   // Past the last step the last step's rows are loaded again, so every step issues the same number
   // of loads and the wait count is fixed.
-  const bool trailing = C::NW == 8 && wv >= 4;  // wave-uniform; four waves run in step
   auto stage = [&](int j) { return smem + (j & 3) * C::STAGE; };
   auto mrow = [&](int t) { return row_begin + min(t, nsteps - 1) * C::BR; };
 
@@ -336,13 +328,11 @@ __global__ __launch_bounds__((64 * dkdv_waves<D, PROMPT>()), 1) void replay_bwd_
     issue_step(mrow(2), stage(2));
     wait_vmem_le<2 * C::LPS>();  // own loads of step 0
   }
-  if (trailing) bare_barrier();
   for (int j = 0; j < nsteps; ++j) {
     wait_lds();      // this wave's reads of the previous stage have returned
     bare_barrier();  // before X(j); no fence: it would wait for every direct load in flight
     step(j);
   }
-  if (!trailing) bare_barrier();
   // no direct load may still be writing into LDS when the waves end
   wait_vmem();
 
@@ -486,14 +476,19 @@ hipError_t dkdv_go(BwdArgs& a, hipStream_t st) {
   if (a.ktiles_prompt > 0) {
     const long long W = (long long)a.ktiles_prompt * G.Hkv;
     timer_mark(LS_KERNEL_DKDV_PROMPT, st, false);
-    hipLaunchKernelGGL((replay_bwd_dkdv<D, DV, true>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(64 * dkdv_waves<D, true>()), 0,
-                       st, a);
+    if constexpr (D == 128) {
+      e = launch_dkdv_prompt_w64(a, st);
+    } else {
+      hipLaunchKernelGGL((replay_bwd_dkdv<D, DV, true>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(64 * kDkvWaves),
+                         0, st, a);
+      e = hipGetLastError();
+    }
     timer_mark(LS_KERNEL_DKDV_PROMPT, st, true);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (e != hipSuccess) return e;
   }
   const long long W = (long long)a.ktile0[G.n_resp] * G.Hkv;
   if (W > 0) {
-    hipLaunchKernelGGL((replay_bwd_dkdv<D, DV, false>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(64 * dkdv_waves<D, false>()), 0,
+    hipLaunchKernelGGL((replay_bwd_dkdv<D, DV, false>), dim3((unsigned)(((W + 7) / 8) * 8)), dim3(64 * kDkvWaves), 0,
                        st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
