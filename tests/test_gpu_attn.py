@@ -120,6 +120,17 @@ def test_ragged_multi_response_call(D):
     _check_all(dict(O=o, LSE=lse, dQ=dq, dKs=dks, dVs=dvs, dKp=dkp, dVp=dvp), case.oracle())
 
 
+@pytest.mark.parametrize("P", [1, 255, 257, 511])
+def test_prompt_dkdv_tile_edges(P):
+    """Head dim 128, serial calls of 1, 8 and 9 tokens (4, 32 and 36 packed rows: one, one and two
+    32-row steps, fewer than the load ring's depth) over prompts of 1, 255, 257 and 511 keys, whose
+    last 256-key tile holds 1 or 255 keys: whole waves, and single 32-key blocks of a wave, without
+    a valid key."""
+    cfg = inputs.replace(inputs.CONFIGS["tiny"], Hq=8, Hkv=2, Dqk=128, Dv=128, P=P, seed=39)
+    case = Case(cfg, [1, 8, 9])
+    _check_all(_serial(case), case.oracle(), literal_abs=False)
+
+
 def test_no_prompt_is_plain_causal():
     cfg = inputs.replace(inputs.CONFIGS["tiny"], P=0, seed=32)
     case = Case(cfg, [70, 5])
