@@ -66,13 +66,30 @@ __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
     asm volatile("" : "+v"(o));
     return __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, kSlc);
   };
+  // Per-row scalars (target, target logit, old log-prob) of this workgroup's first NT rows, one row
+  // per thread, preloaded into LDS before the row loop: those rows read them where they are used,
+  // so no row waits for the dependent gather of its target logit or for its old_logp, and none of
+  // them holds a register across the row's passes. Rows past the first NT (calls of more than
+  // NT x grid rows) load them at their use.
+  __shared__ int s_y[NT];
+  __shared__ float s_xy[NT], s_old[NT];
+  {
+    const int64_t r = row + (int64_t)threadIdx.x * stride;
+    if (r < a.T) {
+      const int y = a.targets[r];
+      s_y[threadIdx.x] = y;
+      s_xy[threadIdx.x] = (y >= 0 && y < a.V) ? bf16_to_f32(a.logits[r * (int64_t)a.V + y]) : 0.0f;
+      s_old[threadIdx.x] = a.old_logp[r];
+    }
+    // published by the barriers of the first row's reductions, before their first read
+  }
   u32x4 v[NCH];
   {
     const __amdgpu_buffer_rsrc_t src = row_src(row);
 #pragma unroll
     for (int j = 0; j < NCH; ++j) v[j] = ld_chunk(src, j, 0);
   }
-  for (;;) {
+  for (int it = 0;; ++it) {
     // chunk offsets and chunk-validity masks are formed from a value the compiler cannot see
     // through, so they are materialised at their use instead of being hoisted out of the row loop
     // (where 19 lane masks and offsets would be live SGPRs across it)
@@ -80,9 +97,6 @@ __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
     asm volatile("" : "+s"(zoff));
     const int64_t next = row + stride;
     const bool more = next < a.T;  // uniform
-    const int y = a.targets[row];
-    const bool y_ok = (y >= 0) && (y < a.V);
-    const float xy = y_ok ? bf16_to_f32(a.logits[row * (int64_t)a.V + y]) : 0.0f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j)
       if ((int)threadIdx.x + j * NT + zoff >= nch) v[j] = u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
@@ -128,7 +142,19 @@ __global__ __launch_bounds__(NT) void grpo_rows_vec(GrpoArgs a) {
     }
     s = block_reduce<NT>(s, red, false);
     const float lse = m + fast_log2(s) * kLn2;
-    const float c = row_scalar(a, row, xy, y_ok, lse, threadIdx.x == 0);
+    int y;
+    float xy, old_lp;
+    if (it < NT) {
+      y = s_y[it];
+      xy = s_xy[it];
+      old_lp = s_old[it];
+    } else {
+      y = a.targets[row];
+      xy = (y >= 0 && y < a.V) ? bf16_to_f32(a.logits[row * (int64_t)a.V + y]) : 0.0f;
+      old_lp = a.old_logp[row];
+    }
+    const bool y_ok = (y >= 0) && (y < a.V);
+    const float c = row_scalar(a, row, xy, y_ok, lse, old_lp, threadIdx.x == 0);
     if (!SCORE) {
       // dlogits = c softmax(x) = (c / sum) e, with the target's element c (p_y - 1) formed from the
       // logit itself
@@ -204,7 +230,7 @@ __global__ __launch_bounds__(NT) void grpo_rows_stream(GrpoArgs a) {
   const float S = block_reduce<NT>(sl, red, false);
   const float lse = M + fast_log2(S) * kLn2;
   const float xy = y_ok ? bf16_to_f32(a.logits[row * (int64_t)a.V + y]) : 0.0f;
-  const float c = row_scalar(a, row, xy, y_ok, lse, threadIdx.x == 0);
+  const float c = row_scalar(a, row, xy, y_ok, lse, a.old_logp[row], threadIdx.x == 0);
   if (a.dlogits == nullptr) return;  // scoring only: no gradient pass
   const float lb = lse * kLog2e;
   const int yc = y_ok ? (y >> 3) : -1;
@@ -247,7 +273,7 @@ __global__ __launch_bounds__(256) void grpo_rows_scalar(GrpoArgs a) {
   s = block_reduce<NT>(s, red, false);
   const float lse = m + fast_log2(s) * kLn2;
   const float xy = y_ok ? bf16_to_f32(x[y]) : 0.0f;
-  const float c = row_scalar(a, row, xy, y_ok, lse, threadIdx.x == 0);
+  const float c = row_scalar(a, row, xy, y_ok, lse, a.old_logp[row], threadIdx.x == 0);
   if (a.dlogits == nullptr) return;  // scoring only: no gradient pass
   uint16_t* d = a.dlogits + row * (int64_t)a.V;
   for (int e = threadIdx.x; e < a.V; e += NT) {
@@ -294,7 +320,7 @@ __global__ __launch_bounds__(NT) void lm_rows(LmRowArgs la) {
   const int y = a.targets[row];
   const bool y_ok = (y >= 0) && (y < a.V);
   const float xy = y_ok ? la.xtgt[row] : 0.0f;
-  const float c = row_scalar(a, row, xy, y_ok, lse, threadIdx.x == 0);
+  const float c = row_scalar(a, row, xy, y_ok, lse, a.old_logp[row], threadIdx.x == 0);
   if (a.dlogits == nullptr) return;  // scoring only
   const float lb = lse * kLog2e;
   const int nch = a.V >> 3;

@@ -16,15 +16,16 @@ __device__ __forceinline__ void row_coefs(const GrpoArgs& a, int64_t row, float*
   *w = a.w[i];
 }
 
-// logp = x_y - lse, rho = exp(logp - old), the clipped term and its flag. The thread with `writer`
-// set stores the row's loss term, log-prob and clip flag. Returns the dlogits coefficient
-// c = clipped ? 0 : w A rho. A target outside [0, V) or NaN data make the row NaN.
+// logp = x_y - lse, rho = exp(logp - old), the clipped term and its flag; old_lp is the row's
+// old_logp entry, which callers load at the start of the row so that its latency is hidden. The
+// thread with `writer` set stores the row's loss term, log-prob and clip flag. Returns the dlogits
+// coefficient c = clipped ? 0 : w A rho. A target outside [0, V) or NaN data make the row NaN.
 __device__ __forceinline__ float row_scalar(const GrpoArgs& a, int64_t row, float xy, bool y_ok, float lse,
-                                            bool writer) {
+                                            float old_lp, bool writer) {
   float A, w;
   row_coefs(a, row, &A, &w);
   const float logp = y_ok ? xy - lse : __builtin_nanf("");
-  const float rho = expf(logp - a.old_logp[row]);
+  const float rho = expf(logp - old_lp);
   const bool nan = !(rho == rho);
   const float unclipped = rho * A;
   const float clipped_v = fminf(fmaxf(rho, 1.0f - a.eps), 1.0f + a.eps) * A;
