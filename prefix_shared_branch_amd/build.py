@@ -67,7 +67,8 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     with ThreadPoolExecutor(max_workers=min(8, len(asm_jobs))) as ex:
         list(ex.map(_run, asm_jobs))
     for j in asm_jobs:
-        bad = isa_check.scan(open(j[-1]).read())
+        text = open(j[-1]).read()
+        bad = isa_check.scan(text) + isa_check.loop_scratch(text)
         if bad:
             raise RuntimeError(f"ISA check failed for {j[-1]}:\n" + "\n".join(bad[:20]))
     objs = [j[-1] for j in jobs]

@@ -10,13 +10,16 @@
 // SIMD. A wave's keys are two 32-key blocks, and every 16-byte LDS fragment of the streamed rows
 // (row-major Q and dO, packed Q^T and dO^T, the same tiles and ring as the 32-key kernel in
 // replay_attn_dkdv.hip) feeds one MFMA per block: half the LDS bytes per MFMA of the 32-key form.
-// The price is the register file: K and V fragments of 64 keys take 128 VGPRs, and the dK^T, dV^T
-// accumulators of 64 keys the 256 AGPRs, so a SIMD holds one wave and its VALU work (P, dS) is not
-// overlapped by another wave's MFMAs. Per 32-row step and wave:
+// The price is the register file: the K and V fragments of 64 keys take 128 registers and the
+// dK^T, dV^T accumulators 256 of the 512 (VGPRs and AGPRs) a lane has, so a SIMD holds one wave, and
+// its VALU work (P, dS) is interleaved with its own MFMAs rather than with another wave's. Per
+// 32-row step and wave:
 //   S = row term + Q K^T (two 32x32 tiles), 2^15 P = exp2(c S) as fp16 B operands;
-//   dP - Delta = row term + dO V^T, dS' = 2^15 P (dP - Delta) s_dS from the fp16 P;
+//   (dP - Delta) s_dS = row term + dO (s_dS V)^T, dS' = 2^15 P (dP - Delta) s_dS from the fp16 P;
 //   dV^T += dO^T (2^15 P), dK^T += Q^T dS' (fp16, exact power-of-two operand scales).
-// Operand layouts, scales, row terms and accumulator updates are those of the 32-key kernel.
+// Operand layouts, scales, row terms and accumulator updates are those of the 32-key kernel, whose
+// results this kernel reproduces bit for bit (s_dS is a power of two, so folding it into V and the
+// row term's operand changes no rounding).
 #include <utility>
 
 #include "common.h"

@@ -1,9 +1,14 @@
-"""Build-time check of the generated gfx950 ISA.
+"""Build-time checks of the generated gfx950 ISA.
 
-Fails the build if a vector-memory store of more than 8 bytes is followed, within two wait
+scan: fails the build if a vector-memory store of more than 8 bytes is followed, within two wait
 states, by a VALU instruction that overwrites one of the store's data registers. The hardware
 reads such store data after issue, so the store would write the new value; the compiler
 covers this case for FLAT/global stores but not for buffer stores that use an SGPR offset.
+
+loop_scratch: fails the build if a named kernel touches scratch memory inside a loop. In the
+one-wave-per-SIMD dK/dV kernel a spill reload in the step loop waits for every direct load in
+flight (vmcnt(0)) and costs most of its speed; its register assignment is tuned to avoid spills,
+and a change elsewhere in the kernel can undo that without any other sign.
 """
 from __future__ import annotations
 
@@ -86,3 +91,29 @@ def scan(asm_text: str) -> list[str]:
         if hit:
             problems.append(f"line {n + 1}: '{s}' then {hit}")
     return problems
+
+
+# kernels whose loops must not touch scratch memory
+LOOP_SCRATCH_FREE = ("replay_bwd_dkdv_w64",)
+
+
+def loop_scratch(asm_text: str, kernels=LOOP_SCRATCH_FREE) -> list[str]:
+    """Scratch accesses between a loop label and a later branch back to it, in the named kernels."""
+    problems = []
+    lines = asm_text.splitlines()
+    starts = [(n, l.split(":")[0]) for n, l in enumerate(lines) if re.match(r"^_Z\S+:", l)]
+    for i, (n0, name) in enumerate(starts):
+        if not any(k in name for k in kernels):
+            continue
+        n1 = starts[i + 1][0] if i + 1 < len(starts) else len(lines)
+        insts, labels = _parse(lines[n0:n1])
+        for b, (_, s) in enumerate(insts):
+            op = s.split()[0]
+            if not (op.startswith("s_branch") or op.startswith("s_cbranch")):
+                continue
+            target = s.split()[1]
+            if target in labels and labels[target] <= b:
+                for k in range(labels[target], b + 1):
+                    if insts[k][1].startswith("scratch_"):
+                        problems.append(f"{name}: line {n0 + insts[k][0] + 1}: '{insts[k][1]}' inside a loop")
+    return sorted(set(problems))
