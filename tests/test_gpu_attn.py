@@ -131,6 +131,15 @@ def test_prompt_dkdv_tile_edges(P):
     _check_all(_serial(case), case.oracle(), literal_abs=False)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(16, 1), (16, 2)])
+def test_wide_gqa_groups(Hq, Hkv):
+    """Head dim 128 with 16 and 8 query heads per kv head: many packed rows per token, so a short
+    response already spans several 32-row steps of the prompt dK/dV sweep and several dQ row tiles."""
+    cfg = inputs.replace(inputs.CONFIGS["tiny"], Hq=Hq, Hkv=Hkv, Dqk=128, Dv=128, P=700, seed=40)
+    case = Case(cfg, [3, 41])
+    _check_all(_serial(case), case.oracle(), literal_abs=False)
+
+
 def test_no_prompt_is_plain_causal():
     cfg = inputs.replace(inputs.CONFIGS["tiny"], P=0, seed=32)
     case = Case(cfg, [70, 5])
